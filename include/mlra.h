@@ -1,0 +1,179 @@
+/*
+ * mlra.h -- C ABI of libmlra.so: decode-stage Multi-Head Low-Rank Attention
+ * (MLRA) over a paged latent KV cache, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (wispaper.ai blog "MLRA: Breaking the Sharding Bottleneck
+ * in Latent Attention", section "The Core Insight: Sum of Branches, Not Sum
+ * of Keys", and section "Mathematical Calibration: Scaling the Latents"):
+ * the latent is split into n_branch branches; each branch b runs its own
+ * softmax attention and the branch outputs are summed *after* attention and
+ * multiplied by a fixed output factor. Keys are scored in absorbed form, so
+ * the kernel only ever reads the cached latents c_b[t] and one decoupled RoPE
+ * key k_r[t] per token that every branch shares (the blog's 1.5*dh per-rank
+ * load: one dh-wide branch latent plus a 0.5*dh position key). For sequence s,
+ * new query token j (0 <= j < Q), head h and branch b:
+ *
+ *   V      = L_s - (Q - 1 - j)   if causal, else L_s   (L_s = seq_lens[s])
+ *   z[t]   = scale * (q_latent[s,j,h,b,:] . c_b[t] + q_rope[s,j,h,:] . k_r[t]),  t < V
+ *   lse_b  = ln sum_{t<V} exp(z[t])
+ *   o_b    = sum_{t<V} exp(z[t] - lse_b) * c_b[t]                 (latent space, DC wide)
+ *   SUM    : out[s,j,h,:]   = out_rescale * sum_b o_b
+ *   CONCAT : out[s,j,h,b,:] = out_rescale * o_b
+ *   V <= 0 : o_b = 0 and lse_b = -inf.
+ *
+ * Token t of sequence s lives in physical block block_table[s][t / 64], slot
+ * t % 64 of both caches. seq_lens counts the Q new tokens, which must already
+ * be in the cache.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state besides cached device properties.
+ *  - Calls are asynchronous: they enqueue work on `stream` (a hipStream_t;
+ *    NULL = the default stream) and return. Buffers must stay alive until the
+ *    stream reaches that point.
+ *  - Host-side validation is synchronous, reads no device memory, and on
+ *    failure returns a status without enqueuing anything. MLRA_ERR_HIP means a
+ *    launch failed (hipGetLastError); the stream may hold partial work.
+ *  - No exceptions cross the ABI and the library prints nothing.
+ *  - Two calls that share a workspace must not run concurrently.
+ */
+#ifndef MLRA_H_
+#define MLRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mlra_status {
+  MLRA_OK = 0,
+  MLRA_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
+  MLRA_ERR_BAD_DIMS = 2,     /* a size is out of range or inconsistent */
+  MLRA_ERR_UNSUPPORTED = 3,  /* valid, but no kernel is built for this shape */
+  MLRA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required */
+  MLRA_ERR_ALIGNMENT = 5,    /* pointer or stride breaks the 16-byte rule */
+  MLRA_ERR_HIP = 6           /* a HIP runtime call or launch failed */
+} mlra_status;
+
+typedef enum mlra_dtype {
+  MLRA_BF16 = 0,  /* q, caches and out in bfloat16; MFMA path */
+  MLRA_FP32 = 1   /* q, caches and out in float32; vector-ALU path */
+} mlra_dtype;
+
+typedef enum mlra_branch_reduce {
+  MLRA_BRANCH_SUM = 0,    /* out[S][Q][H][DC] = out_rescale * sum_b o_b */
+  MLRA_BRANCH_CONCAT = 1  /* out[S][Q][H][n_branch][DC] = out_rescale * o_b */
+} mlra_branch_reduce;
+
+/* Shapes and layout of one decode call. Strides are in ELEMENTS; 0 selects the
+ * dense default. The innermost (feature) dimension is always contiguous. */
+typedef struct mlra_decode_dims {
+  int32_t num_seqs;            /* S  >= 1 */
+  int32_t q_len;               /* Q  in {1, 2}: new query tokens per sequence */
+  int32_t num_heads;           /* H  >= 1, H * Q <= 64 */
+  int32_t d_latent;            /* DC per branch: bf16 {64, 128, 512}, fp32 {64, 128, 256, 512} */
+  int32_t d_rope;              /* DR in {32, 64} */
+  int32_t block_size;          /* tokens per cache block; must be 64 */
+  int32_t max_blocks_per_seq;  /* columns of block_table */
+  int32_t num_blocks;          /* physical blocks in each cache */
+  int32_t max_seq_len;         /* host-side upper bound of seq_lens (no device read needed) */
+  int32_t causal;              /* nonzero: query j sees t < L - (Q - 1 - j) */
+  int32_t num_splits;          /* 0: library plans split-K; >0: at most this many splits per sequence */
+  int32_t dtype;               /* mlra_dtype */
+  int32_t reduce;              /* mlra_branch_reduce */
+  int32_t reserved;            /* must be 0 */
+  /* latent_cache element strides: block, token, branch. Defaults (0):
+   * token-major [num_blocks][64][n_branch][DC] -> 64*n_branch*DC, n_branch*DC, DC */
+  int64_t latent_stride_block, latent_stride_token, latent_stride_branch;
+  /* rope_cache element strides: block, token. Defaults: [num_blocks][64][DR] */
+  int64_t rope_stride_block, rope_stride_token;
+  /* Optional host-side sum of seq_lens (0 = unknown: plan as if every
+   * sequence had max_seq_len). Only steers how tokens are split across
+   * workgroups; results do not depend on it. */
+  int64_t sum_seq_lens;
+} mlra_decode_dims;
+
+/* Split-K plan, computed on the host from dims alone (no device read). On
+ * the device each sequence uses ceil(ceil(L/64) / tiles_per_split) of its
+ * splits_per_seq workgroups; the rest exit at once. */
+typedef struct mlra_decode_plan {
+  int32_t num_cus;             /* compute units the plan targets */
+  int32_t target_groups;       /* split-kernel workgroups the planner aims for */
+  int32_t waves_per_group;     /* waves in one split-kernel workgroup */
+  int32_t tiles_per_split;     /* 64-token tiles one workgroup (one split) covers */
+  int32_t splits_per_seq;      /* splits of the longest sequence; grid = S x this */
+  int32_t kernel_variant;      /* internal kernel id (for logs and tests) */
+  int32_t lds_bytes;           /* LDS one split workgroup allocates */
+  int32_t reserved;
+  size_t workspace_bytes;      /* bytes of device workspace the call needs */
+} mlra_decode_plan;
+
+/* Plan a call without touching the GPU: split sequences into chunks of
+ * tiles_per_split 64-token tiles so that about target_groups workgroups run.
+ * num_cus <= 0 queries the current device (needs HIP); pass e.g. 256 to plan
+ * for an MI355X on a host without a GPU. Returns the same validation errors
+ * as mlra_decode_attention, minus the pointer checks. */
+mlra_status mlra_decode_make_plan(const mlra_decode_dims* dims, int32_t n_branch,
+                                  int32_t num_cus, mlra_decode_plan* plan);
+
+/* Workspace bytes for a call on the current device (queries its CU count). */
+mlra_status mlra_decode_workspace_size(const mlra_decode_dims* dims, int32_t n_branch,
+                                       size_t* bytes);
+
+/*
+ * MLRA decode attention (formula above).
+ *
+ *  q_latent     [S][Q][H][n_branch][DC]   dtype, dense
+ *  q_rope       [S][Q][H][DR]             dtype, dense; shared by all branches
+ *  latent_cache paged, see latent_stride_*; dtype
+ *  rope_cache   paged, see rope_stride_*;   dtype
+ *  block_table  [S][max_blocks_per_seq]   int32, physical block ids in [0, num_blocks)
+ *  seq_lens     [S]                       int32, device; 0 <= L <= max_seq_len
+ *  n_branch     branches in the cache and in q_latent: {1, 2, 4}
+ *  scale        softmax scale on the raw dot products (finite)
+ *  out_rescale  output factor (finite); 1/sqrt(4) for MLRA-4
+ *  out          SUM: [S][Q][H][DC]; CONCAT: [S][Q][H][n_branch][DC]; dtype
+ *  lse          [S][Q][H][n_branch] float32, natural log; -inf where V <= 0
+ *  workspace    device scratch of at least mlra_decode_workspace_size bytes,
+ *               16-byte aligned; contents need no initialisation
+ *
+ * Alignment: every tensor pointer 16-byte aligned; cache strides multiples
+ * of 16 bytes. Table entries past ceil(L/64) are never read, nor are cache
+ * rows past L (they may hold NaN). Memory safety on bad input: a seq_lens
+ * entry above max_seq_len is treated as max_seq_len, and a table entry
+ * outside [0, num_blocks) reads block 0 instead; both give wrong results
+ * for that sequence but never an out-of-bounds access.
+ */
+mlra_status mlra_decode_attention(const void* q_latent, const void* q_rope,
+                                  const void* latent_cache, const void* rope_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t n_branch, float scale, float out_rescale,
+                                  void* out, float* lse, const mlra_decode_dims* dims,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MLA-shaped comparison call: a single latent head (n_branch = 1, typically
+ * DC = 512 plus DR = 64, the 4.5*dh per-token load the blog attributes to MLA),
+ * one softmax, out_rescale = 1. Same argument rules as mlra_decode_attention;
+ * out is [S][Q][H][DC] and lse [S][Q][H].
+ */
+mlra_status mla_decode_attention(const void* q_latent, const void* q_rope,
+                                 const void* latent_cache, const void* rope_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 float scale, void* out, float* lse,
+                                 const mlra_decode_dims* dims, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Static, never-NULL description of a status code. */
+const char* mlra_status_string(mlra_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t mlra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLRA_H_ */

@@ -1,0 +1,172 @@
+// Host-side validation and split-K planning for MLRA decode attention.
+//
+// Pure C++ (no HIP calls): argument checks, default strides, the choice of
+// kernel shape and the split plan. The plan splits each sequence's 64-token
+// tiles into chunks so that roughly a fixed number of workgroups fill the GPU
+// (flash-decoding); each chunk yields a partial (output, log-sum-exp) per
+// query row and branch that the combine kernel merges.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <initializer_list>
+
+#include "mlra_internal.h"
+
+namespace mlra {
+
+static bool pow2_in(int v, std::initializer_list<int> allowed) {
+  for (int a : allowed)
+    if (v == a) return true;
+  return false;
+}
+
+mlra_status resolve_dims(const mlra_decode_dims* d, int32_t n_branch, Resolved* r) {
+  if (!d || !r) return MLRA_ERR_NULL_PTR;
+  if (d->dtype != MLRA_BF16 && d->dtype != MLRA_FP32) return MLRA_ERR_BAD_DIMS;
+  if (d->reduce != MLRA_BRANCH_SUM && d->reduce != MLRA_BRANCH_CONCAT) return MLRA_ERR_BAD_DIMS;
+  if (d->reserved != 0) return MLRA_ERR_BAD_DIMS;
+  if (d->num_seqs < 1 || d->num_heads < 1 || d->q_len < 1) return MLRA_ERR_BAD_DIMS;
+  if (d->num_seqs > 65535) return MLRA_ERR_UNSUPPORTED;  // grid y dimension
+  if (d->q_len > 2) return MLRA_ERR_UNSUPPORTED;
+  if (d->num_heads * d->q_len > 64) return MLRA_ERR_UNSUPPORTED;
+  if (n_branch < 1) return MLRA_ERR_BAD_DIMS;
+  if (!pow2_in(n_branch, {1, 2, 4})) return MLRA_ERR_UNSUPPORTED;
+  if (d->d_latent < 1 || d->d_rope < 1) return MLRA_ERR_BAD_DIMS;
+  if (!pow2_in(d->d_rope, {32, 64})) return MLRA_ERR_UNSUPPORTED;
+  if (d->dtype == MLRA_BF16) {
+    if (!pow2_in(d->d_latent, {64, 128, 512})) return MLRA_ERR_UNSUPPORTED;
+    if (d->d_latent == 512 && (n_branch != 1 || d->d_rope != 64)) return MLRA_ERR_UNSUPPORTED;
+  } else {
+    if (!pow2_in(d->d_latent, {64, 128, 256, 512})) return MLRA_ERR_UNSUPPORTED;
+  }
+  if (d->block_size != kBlock) return d->block_size < 1 ? MLRA_ERR_BAD_DIMS : MLRA_ERR_UNSUPPORTED;
+  if (d->max_blocks_per_seq < 1 || d->num_blocks < 1) return MLRA_ERR_BAD_DIMS;
+  if (d->max_seq_len < 0) return MLRA_ERR_BAD_DIMS;
+  if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * kBlock) return MLRA_ERR_BAD_DIMS;
+  if (d->num_splits < 0 || d->sum_seq_lens < 0) return MLRA_ERR_BAD_DIMS;
+  if (d->sum_seq_lens > (int64_t)d->num_seqs * d->max_seq_len) return MLRA_ERR_BAD_DIMS;
+
+  Resolved o;
+  o.S = d->num_seqs;
+  o.Q = d->q_len;
+  o.H = d->num_heads;
+  o.rows = d->num_heads * d->q_len;
+  o.NB = n_branch;
+  o.DC = d->d_latent;
+  o.DR = d->d_rope;
+  o.max_blocks = d->max_blocks_per_seq;
+  o.num_blocks = d->num_blocks;
+  o.max_seq_len = d->max_seq_len;
+  o.lcap = d->max_seq_len;
+  o.causal = d->causal ? 1 : 0;
+  o.dtype = d->dtype;
+  o.reduce = d->reduce;
+  o.lsbr = d->latent_stride_branch ? d->latent_stride_branch : o.DC;
+  o.lst = d->latent_stride_token ? d->latent_stride_token : (int64_t)o.NB * o.DC;
+  o.lsb = d->latent_stride_block ? d->latent_stride_block : (int64_t)kBlock * o.lst;
+  o.rst = d->rope_stride_token ? d->rope_stride_token : o.DR;
+  o.rsb = d->rope_stride_block ? d->rope_stride_block : (int64_t)kBlock * o.rst;
+  if (o.lsbr < 0 || o.lst < 0 || o.lsb < 0 || o.rst < 0 || o.rsb < 0) return MLRA_ERR_BAD_DIMS;
+  // Rows of one token / one block must not overlap each other.
+  if (o.NB > 1 && o.lsbr < o.DC) return MLRA_ERR_BAD_DIMS;
+  if (o.lst < (int64_t)(o.NB - 1) * o.lsbr + o.DC) return MLRA_ERR_BAD_DIMS;
+  if (o.lsb < (int64_t)(kBlock - 1) * o.lst + (int64_t)(o.NB - 1) * o.lsbr + o.DC)
+    return MLRA_ERR_BAD_DIMS;
+  if (o.rst < o.DR || o.rsb < (int64_t)(kBlock - 1) * o.rst + o.DR) return MLRA_ERR_BAD_DIMS;
+  // 16-byte rule for every stride.
+  const int64_t vec = (o.dtype == MLRA_BF16) ? 8 : 4;
+  if (o.lsbr % vec || o.lst % vec || o.lsb % vec || o.rst % vec || o.rsb % vec)
+    return MLRA_ERR_ALIGNMENT;
+  *r = o;
+  return MLRA_OK;
+}
+
+KernelShape choose_shape(const Resolved& r) {
+  KernelShape k{};
+  if (r.dtype == MLRA_FP32) {
+    k.variant = kVariantValuFp32;
+    k.NT = 1;
+    k.WD = 1;
+    k.WT = 1;
+    k.NPF = 1;
+    k.waves = 4;  // four (row, branch) pairs per workgroup
+    k.groups_per_cu = 2;
+    return k;
+  }
+  k.variant = kVariantMfmaBf16;
+  k.NT = r.rows > 32 ? 2 : 1;
+  k.WD = r.DC == 512 ? 4 : 1;
+  // Token-split waves so that a workgroup keeps four waves busy: one branch
+  // alone gets four waves over its tokens, two branches two waves each.
+  k.WT = (r.NB == 1 && k.WD == 1) ? 4 : (r.NB == 2 ? 2 : 1);
+  k.NPF = 2;
+  k.waves = r.NB * k.WD * k.WT;
+  k.groups_per_cu = 2;
+  return k;
+}
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
+                      int32_t num_splits, int64_t sum_seq_lens, mlra_decode_plan* plan) {
+  if (!plan) return MLRA_ERR_NULL_PTR;
+  if (num_cus < 1) return MLRA_ERR_BAD_DIMS;
+  mlra_decode_plan p;
+  std::memset(&p, 0, sizeof(p));
+  p.num_cus = num_cus;
+  p.waves_per_group = k.waves;
+  p.kernel_variant = k.variant;
+
+  const int64_t max_tiles = cdiv(r.lcap, kBlock);
+  int64_t tps;
+  if (k.variant == kVariantValuFp32) {
+    // One workgroup covers 4 (row, branch) pairs; groups along the pairs
+    // multiply the split count.
+    const int64_t pair_groups = cdiv((int64_t)r.rows * r.NB, k.waves);
+    p.target_groups = (int32_t)std::max<int64_t>(1, (int64_t)num_cus * k.groups_per_cu / pair_groups);
+  } else {
+    p.target_groups = num_cus * k.groups_per_cu;
+  }
+  if (num_splits > 0) {
+    tps = cdiv(std::max<int64_t>(max_tiles, 1), num_splits);
+  } else {
+    // Expected tiles in the batch: exact for full blocks when the caller gave
+    // sum(seq_lens); otherwise as if every sequence had max_seq_len.
+    const int64_t total =
+        sum_seq_lens > 0 ? cdiv(sum_seq_lens, kBlock) : (int64_t)r.S * max_tiles;
+    tps = cdiv(std::max<int64_t>(total, 1), p.target_groups);
+  }
+  tps = std::max<int64_t>(tps, k.WT);
+  tps = cdiv(tps, k.WT) * k.WT;  // every token-split wave gets the same tile count
+  const int64_t spl = std::max<int64_t>(1, cdiv(max_tiles, tps));
+  if (spl > 65535 || tps > (1 << 24)) return MLRA_ERR_UNSUPPORTED;
+  p.tiles_per_split = (int32_t)tps;
+  p.splits_per_seq = (int32_t)spl;
+  p.lds_bytes = k.variant == kVariantMfmaBf16
+                    ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, k.NT, k.WT)
+                    : 0;
+  // Partials: output [S][spl][NB][rows][DC] and lse [S][spl][NB][rows], fp32.
+  const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;
+  const int64_t o_bytes = cdiv(slots * r.DC * 4, 256) * 256;
+  const int64_t l_bytes = cdiv(slots * 4, 256) * 256;
+  p.workspace_bytes = (size_t)(o_bytes + l_bytes);
+  *plan = p;
+  return MLRA_OK;
+}
+
+}  // namespace mlra
+
+extern "C" const char* mlra_status_string(mlra_status s) {
+  switch (s) {
+    case MLRA_OK: return "ok";
+    case MLRA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MLRA_ERR_BAD_DIMS: return "a size is out of range or inconsistent";
+    case MLRA_ERR_UNSUPPORTED: return "valid, but no kernel is built for this shape";
+    case MLRA_ERR_WORKSPACE: return "workspace is NULL or smaller than required";
+    case MLRA_ERR_ALIGNMENT: return "a pointer or stride breaks the 16-byte rule";
+    case MLRA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+  }
+  return "unknown status";
+}
+
+extern "C" int32_t mlra_version(void) { return 100; }  // 0.1.0

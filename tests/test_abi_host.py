@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, validates arguments and plans split-K on the host."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from latent_kv_cache_amd import _lib, configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlra.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _dims(cfg, **kw):
+    d = _lib.DecodeDims()
+    d.num_seqs, d.q_len, d.num_heads = cfg.num_seqs, cfg.q_len, cfg.num_heads
+    d.d_latent, d.d_rope, d.block_size = cfg.d_latent, cfg.d_rope, 64
+    L = cfg.context if cfg.context is not None else cfg.context_range[1]
+    d.max_blocks_per_seq = -(-L // 64)
+    d.num_blocks = d.max_blocks_per_seq * cfg.num_seqs + 1
+    d.max_seq_len = L
+    d.causal = 1
+    d.dtype = _lib.MLRA_BF16 if cfg.dtype == "bf16" else _lib.MLRA_FP32
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _plan(lib, d, nb, cus=256):
+    p = _lib.DecodePlan()
+    st = lib.mlra_decode_make_plan(ctypes.byref(d), nb, cus, ctypes.byref(p))
+    return st, p
+
+
+def test_header_declarations_are_exported(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:mlra_status|const char\*|int32_t)\s+(\w+)\s*\(", text,
+                              re.M))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layouts_match_header():
+    # int32 x 14 then int64 x 6; the plan ends with a size_t.
+    assert ctypes.sizeof(_lib.DecodeDims) == 14 * 4 + 6 * 8
+    assert _lib.DecodeDims.latent_stride_block.offset == 56
+    assert ctypes.sizeof(_lib.DecodePlan) == 8 * 4 + 8
+
+
+def test_status_strings_and_version(lib):
+    for code in range(7):
+        assert lib.mlra_status_string(code)
+    assert lib.mlra_status_string(99) == b"unknown status"
+    assert lib.mlra_version() >= 100
+
+
+@pytest.mark.parametrize("cfg", configs.ALL + [configs.MLA_COMPARE], ids=lambda c: c.name)
+def test_plan_covers_every_tile(lib, cfg):
+    d = _dims(cfg)
+    st, p = _plan(lib, d, cfg.n_branch)
+    assert st == 0
+    max_tiles = -(-d.max_seq_len // 64)
+    assert p.splits_per_seq * p.tiles_per_split >= max_tiles
+    assert (p.splits_per_seq - 1) * p.tiles_per_split < max(max_tiles, 1)
+    assert p.tiles_per_split % (p.waves_per_group // (cfg.n_branch * (4 if cfg.d_latent == 512 and cfg.dtype == "bf16" else 1)) if cfg.dtype == "bf16" else 1) == 0
+    rows = cfg.num_heads * cfg.q_len
+    slots = cfg.num_seqs * p.splits_per_seq * cfg.n_branch * rows
+    assert p.workspace_bytes >= slots * (cfg.d_latent + 1) * 4
+    assert p.kernel_variant == (2 if cfg.dtype == "bf16" else 1)
+    assert p.lds_bytes <= 160 * 1024
+
+
+def test_plan_fills_the_gpu_for_the_single_branch_share(lib):
+    d = _dims(configs.MLRA4_TP_SHARE)
+    st, p = _plan(lib, d, 1)
+    groups = d.num_seqs * p.splits_per_seq
+    assert st == 0 and groups >= 256
+
+
+def test_ragged_hint_balances_splits(lib):
+    cfg = configs.RAGGED_Q2
+    d = _dims(cfg)
+    _, p_worst = _plan(lib, d, 4)
+    d.sum_seq_lens = cfg.num_seqs * 16896
+    _, p_hint = _plan(lib, d, 4)
+    assert p_hint.tiles_per_split < p_worst.tiles_per_split
+    d.num_splits = 3
+    _, p_forced = _plan(lib, d, 4)
+    assert p_forced.splits_per_seq <= 3
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_seqs", 0, 2), ("q_len", 3, 3), ("num_heads", 33, 3), ("d_latent", 96, 3),
+    ("d_rope", 48, 3), ("block_size", 32, 3), ("block_size", 0, 2), ("max_blocks_per_seq", 0, 2),
+    ("max_seq_len", 10 ** 6, 2), ("max_seq_len", -1, 2), ("num_splits", -2, 2), ("dtype", 7, 2),
+    ("reduce", 2, 2), ("reserved", 1, 2), ("latent_stride_token", 100, 2),
+    ("latent_stride_token", 516, 5), ("rope_stride_token", 60, 2), ("sum_seq_lens", -1, 2),
+    ("num_seqs", 70000, 3),
+])
+def test_validation_errors(lib, field, value, status):
+    d = _dims(configs.MLRA4_FUSED)
+    if field == "num_heads":
+        d.q_len = 2
+    setattr(d, field, value)
+    st, _ = _plan(lib, d, 4)
+    assert st == status, (field, value, st)
+
+
+def test_branch_and_width_rules(lib):
+    d = _dims(configs.MLA_COMPARE)
+    assert _plan(lib, d, 1)[0] == 0
+    assert _plan(lib, d, 2)[0] == 3        # bf16 512-wide latent only as a single head
+    assert _plan(lib, d, 3)[0] == 3
+    assert _plan(lib, d, 0)[0] == 2
+    d.dtype = _lib.MLRA_FP32
+    assert _plan(lib, d, 2)[0] == 0
+
+
+def test_pointer_and_alignment_errors_before_any_device_call(lib):
+    cfg = configs.MLRA4_TP_SHARE
+    d = _dims(cfg)
+    ok = ctypes.c_void_p(4096)
+    args = [ok] * 6 + [1, 0.1, 0.5, ok, ok, ctypes.byref(d), ok, 1 << 30, None]
+    a = list(args)
+    a[0] = None
+    assert lib.mlra_decode_attention(*a) == 1
+    a = list(args)
+    a[10] = None
+    assert lib.mlra_decode_attention(*a) == 1
+    a = list(args)
+    a[2] = ctypes.c_void_p(4096 + 8)
+    assert lib.mlra_decode_attention(*a) == 5
+    a = list(args)
+    a[7] = math.inf
+    assert lib.mlra_decode_attention(*a) == 2
+    a = list(args)
+    a[6] = 3
+    assert lib.mlra_decode_attention(*a) == 3
+    assert lib.mla_decode_attention(None, ok, ok, ok, ok, ok, 0.1, ok, ok, ctypes.byref(d), ok,
+                                    1 << 30, None) == 1

@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
+
+Bar (per output tensor): max |out - ref| <= 2e-2 and ||out - ref||_2 / ||ref||_2
+<= 1e-2; lse within 1e-3 absolute where finite, and -inf exactly where the
+oracle has -inf. float32 workloads must also be within 1e-4 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+from latent_kv_cache_amd import api, configs
+from latent_kv_cache_amd.inputs import make_inputs, to_device
+from oracle import mlra_decode
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL_L2, LSE_ATOL = 2e-2, 1e-2, 1e-3
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def run_gpu(inp, reduce="sum", num_splits=0, dev=None, hint=True, entry="mlra"):
+    cfg = inp.cfg
+    d = dev if dev is not None else to_device(inp)
+    kw = dict(max_seq_len=inp.max_seq_len, causal=cfg.causal, num_splits=num_splits,
+              sum_seq_lens=int(inp.seq_lens.sum()) if hint else 0)
+    if entry == "mla":
+        out, lse = api.mla_decode_attention(d["q_latent"], d["q_rope"], d["latent_cache"],
+                                            d["rope_cache"], d["block_table"], d["seq_lens"],
+                                            cfg.scale, **kw)
+        lse = lse[..., None]
+    else:
+        out, lse = api.mlra_decode_attention(d["q_latent"], d["q_rope"], d["latent_cache"],
+                                             d["rope_cache"], d["block_table"], d["seq_lens"],
+                                             cfg.n_branch, cfg.scale, cfg.out_rescale,
+                                             reduce=reduce, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle(inp, reduce="sum"):
+    c = inp.cfg
+    return mlra_decode(inp.q_latent, inp.q_rope, inp.latent_cache, inp.rope_cache,
+                       inp.block_table, inp.seq_lens, c.scale, c.out_rescale, reduce, c.causal,
+                       c.block_size)
+
+
+def assert_parity(out, lse, ref_out, ref_lse, fp32=False):
+    assert out.shape == ref_out.shape and lse.shape == ref_lse.shape
+    assert not np.isnan(out).any(), "NaN in GPU output"
+    err = np.abs(out - ref_out)
+    rel = np.linalg.norm(out - ref_out) / max(np.linalg.norm(ref_out), 1e-30)
+    assert err.max() <= ATOL, f"max-abs {err.max():.3e}"
+    assert rel <= RTOL_L2, f"L2-rel {rel:.3e}"
+    if fp32:
+        assert err.max() <= 1e-4, f"fp32 max-abs {err.max():.3e}"
+    ninf = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), ninf), "-inf pattern of lse differs"
+    if (~ninf).any():
+        lerr = np.abs(lse[~ninf] - ref_lse[~ninf]).max()
+        assert lerr <= LSE_ATOL, f"lse max-abs {lerr:.3e}"
+
+
+def _cfg(**kw):
+    base = dict(name="t", num_seqs=3, q_len=1, num_heads=32, n_branch=4, d_latent=128,
+                d_rope=64, dtype="bf16", context=None, context_range=(1, 700), seed=21,
+                scale=1 / np.sqrt(192), out_rescale=0.5)
+    base.update(kw)
+    return configs.DecodeConfig(**base)
+
+
+# Every kernel instance: branches x latent width x RoPE width x row tiles.
+SHAPES = []
+for nb in (1, 2, 4):
+    for dc in (64, 128):
+        for dr in (32, 64):
+            for h, q in ((16, 1), (24, 2)):
+                SHAPES.append((nb, dc, dr, h, q))
+SHAPES += [(1, 512, 64, 32, 1), (1, 512, 64, 32, 2)]
+
+
+@pytest.mark.parametrize("nb,dc,dr,h,q", SHAPES)
+def test_small_shapes_every_instance(nb, dc, dr, h, q):
+    cfg = _cfg(n_branch=nb, d_latent=dc, d_rope=dr, num_heads=h, q_len=q,
+               seed=100 + nb * 7 + dc + dr + h + q, scale=1 / np.sqrt(dc + dr))
+    inp = make_inputs(cfg)
+    for reduce in ("sum", "concat"):
+        _say(f"small nb={nb} dc={dc} dr={dr} h={h} q={q} {reduce} lens={inp.seq_lens.tolist()}")
+        out, lse = run_gpu(inp, reduce)
+        ro, rl = oracle(inp, reduce)
+        assert_parity(out, lse, ro, rl)
+
+
+@pytest.mark.parametrize("cfg", configs.ALL, ids=lambda c: c.name)
+def test_full_size_workloads(cfg):
+    _say(f"full {cfg.name}")
+    inp = make_inputs(cfg)
+    out, lse = run_gpu(inp)
+    ro, rl = oracle(inp)
+    assert_parity(out, lse, ro, rl, fp32=cfg.dtype == "fp32")
+
+
+def test_full_size_mla_comparison_call():
+    cfg = configs.MLA_COMPARE
+    _say(f"full {cfg.name} via mla_decode_attention")
+    inp = make_inputs(cfg)
+    out, lse = run_gpu(inp, entry="mla")
+    ro, rl = oracle(inp)
+    assert_parity(out, lse, ro, rl)
+
+
+def test_fp32_path_small_shapes():
+    for nb, dc, dr, q in ((1, 256, 64, 2), (2, 512, 32, 1), (4, 64, 32, 2)):
+        cfg = _cfg(dtype="fp32", n_branch=nb, d_latent=dc, d_rope=dr, q_len=q, num_heads=5,
+                   context_range=(1, 300), seed=dc + nb)
+        inp = make_inputs(cfg)
+        _say(f"fp32 nb={nb} dc={dc} dr={dr} q={q}")
+        for reduce in ("sum", "concat"):
+            out, lse = run_gpu(inp, reduce)
+            assert_parity(out, lse, *oracle(inp, reduce), fp32=True)
+
+
+@pytest.mark.parametrize("nb,dc", [(1, 128), (4, 128), (1, 512)])
+def test_split_count_invariance(nb, dc):
+    cfg = _cfg(n_branch=nb, d_latent=dc, num_seqs=2, context=None, context_range=(3000, 5000),
+               seed=5 + nb)
+    inp = make_inputs(cfg)
+    ro, rl = oracle(inp)
+    dev = to_device(inp)
+    for ns in (1, 2, 7, 0, 79):
+        _say(f"splits nb={nb} dc={dc} num_splits={ns}")
+        out, lse = run_gpu(inp, num_splits=ns, dev=dev)
+        assert_parity(out, lse, ro, rl)
+
+
+def test_block_relabelling_and_determinism_are_bitwise():
+    cfg = _cfg(num_seqs=4, context_range=(100, 2000), seed=77)
+    inp = make_inputs(cfg)
+    _say("determinism")
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    perm = np.random.default_rng(1).permutation(inp.num_blocks)
+    inp2 = make_inputs(cfg)
+    inp2.latent_cache[perm] = inp.latent_cache
+    inp2.rope_cache[perm] = inp.rope_cache
+    inp2.block_table = perm[inp.block_table].astype(np.int32)
+    _say("relabelled blocks")
+    c = run_gpu(inp2)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+def test_fused_equals_sum_of_single_branch_shares():
+    cfg = _cfg(num_seqs=2, context_range=(500, 1500), seed=9)
+    inp = make_inputs(cfg)
+    _say("fused vs single-branch shares")
+    fused, lse_f = run_gpu(inp)
+    d = to_device(inp)
+    acc = 0
+    for b in range(4):
+        share = dict(d)
+        share["q_latent"] = d["q_latent"][:, :, :, b:b + 1].contiguous()
+        share["latent_cache"] = d["latent_cache"][:, :, b:b + 1]
+        one = inp.cfg.with_(n_branch=1)
+        inp_b = make_inputs(cfg)
+        inp_b.cfg = one
+        o, l = run_gpu(inp_b, dev=share)
+        acc = acc + o
+        np.testing.assert_allclose(l[..., 0], lse_f[..., b], atol=2e-5)
+    assert np.abs(acc - fused).max() <= 2e-2
+    assert np.linalg.norm(acc - fused) / np.linalg.norm(fused) <= 1e-2
+
+
+def test_branch_major_cache_strides():
+    cfg = _cfg(num_seqs=2, context_range=(64, 900), seed=13)
+    inp = make_inputs(cfg)
+    d = to_device(inp)
+    # same values stored branch-major [blocks][NB][64][DC], viewed as [blocks][64][NB][DC]
+    bm = d["latent_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert bm.stride(2) == 64 * cfg.d_latent
+    d["latent_cache"] = bm
+    _say("branch-major strides")
+    out, lse = run_gpu(inp, dev=d)
+    assert_parity(out, lse, *oracle(inp))
+
+
+def test_empty_and_degenerate_sequences():
+    cfg = _cfg(q_len=2, num_seqs=5, context=130, seed=4)
+    inp = make_inputs(cfg)
+    inp.seq_lens[:] = [0, 1, 2, 64, 130]
+    _say("degenerate lengths")
+    out, lse = run_gpu(inp)
+    ro, rl = oracle(inp)
+    assert_parity(out, lse, ro, rl)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.all(out[1, 0] == 0) and np.all(np.isneginf(lse[1, 0]))
+    inp.seq_lens[:] = 0
+    out, lse = run_gpu(inp, hint=False)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_seq_len_above_max_is_clamped_not_read_out_of_bounds():
+    cfg = _cfg(num_seqs=2, context=256, seed=3)
+    inp = make_inputs(cfg)
+    d = to_device(inp)
+    d["seq_lens"] = torch.tensor([10_000, 256], dtype=torch.int32, device="cuda")
+    _say("over-long seq_lens clamp")
+    out, lse = api.mlra_decode_attention(d["q_latent"], d["q_rope"], d["latent_cache"],
+                                         d["rope_cache"], d["block_table"], d["seq_lens"], 4,
+                                         cfg.scale, cfg.out_rescale, max_seq_len=256)
+    torch.cuda.synchronize()
+    ro, rl = oracle(inp)
+    assert_parity(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy(), ro, rl)
