@@ -1,0 +1,210 @@
+"""Benchmark: MLRA decode attention over a paged latent KV cache on one MI355X.
+
+Headline workload: one 4-way tensor-parallel rank's share of MLRA-4 decode
+(one latent branch of 128 plus the shared 64-wide RoPE key, 1.5*dh per token),
+batch 16, context 8192, 32 query heads, bf16, 64-token blocks placed by a
+shuffled block table. A step is one full decode-attention call (split-K
+kernel + log-sum-exp combine) over the batch.
+
+Timing: the caches are replicated into enough copies (each with its own
+block table) that consecutive steps never find their data in the 256 MB
+Infinity Cache; HIP events on the launch stream bracket the K timed steps.
+value = algorithmic HBM bytes per step / time per step (GB/s); algorithmic
+bytes = cache rows read + queries + block-table entries + seq_lens + outputs.
+
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+                       [--workload NAME] [--no-cpu-baseline] [--graph]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 << 20      # Infinity Cache
+
+
+def algorithmic_bytes(inp) -> dict:
+    c = inp.cfg
+    el = 2 if c.dtype == "bf16" else 4
+    L = inp.seq_lens.astype(np.int64)
+    cache = int(L.sum()) * (c.n_branch * c.d_latent + c.d_rope) * el
+    q = c.num_seqs * c.q_len * c.num_heads * (c.n_branch * c.d_latent + c.d_rope) * el
+    table = int(((L + c.block_size - 1) // c.block_size).sum()) * 4
+    lens = c.num_seqs * 4
+    out = c.num_seqs * c.q_len * c.num_heads * c.d_latent * el
+    lse = c.num_seqs * c.q_len * c.num_heads * c.n_branch * 4
+    total = cache + q + table + lens + out + lse
+    return dict(total=total, cache=cache, kv_tokens=int(L.sum()))
+
+
+def flops(inp) -> int:
+    c = inp.cfg
+    L = inp.seq_lens.astype(np.int64)
+    per = 2 * (c.n_branch * c.d_latent + c.d_rope) + 2 * c.n_branch * c.d_latent
+    return int(L.sum()) * c.q_len * c.num_heads * per
+
+
+def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
+    """Time the float64 oracle on the host over repeated passes of the batch."""
+    from oracle import mlra_decode
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    c = inp.cfg
+    nbytes = algorithmic_bytes(inp)["total"]
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 1000:
+        t0 = time.perf_counter()
+        mlra_decode(inp.q_latent, inp.q_rope, inp.latent_cache, inp.rope_cache,
+                    inp.block_table, inp.seq_lens, c.scale, c.out_rescale, "sum", c.causal,
+                    c.block_size)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per = t_total / reps
+    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} full passes of the {c.name} batch through the float64 NumPy "
+                      f"oracle ({per * 1e3:.1f} ms per pass, {c.num_seqs * c.q_len / per:.1f} "
+                      f"decode tokens/s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mlra4_tp_share_b16_t8192")
+    ap.add_argument("--copies", type=int, default=0, help="cache copies (0: enough to exceed 2x MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this decode path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    from latent_kv_cache_amd import api, configs
+    from latent_kv_cache_amd.inputs import make_inputs, to_device
+
+    cfg = configs.BY_NAME[args.workload]
+    inp = make_inputs(cfg)
+    ab = algorithmic_bytes(inp)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = to_device(inp, dev)
+
+    # Replicate the caches so that consecutive steps touch disjoint memory.
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / ab["cache"]))
+    nb = inp.num_blocks
+    lat_all = d["latent_cache"].repeat(copies, 1, 1, 1)
+    rope_all = d["rope_cache"].repeat(copies, 1, 1)
+    tables = [(d["block_table"] + k * nb).contiguous() for k in range(copies)]
+    del d["latent_cache"], d["rope_cache"]
+    reduce = "sum"
+    S, Q, H, NB, DC = inp.q_latent.shape
+    out = torch.empty((S, Q, H, DC), dtype=d["q_latent"].dtype, device=dev)
+    lse = torch.empty((S, Q, H, NB), dtype=torch.float32, device=dev)
+    kw = dict(max_seq_len=inp.max_seq_len, reduce=reduce, causal=cfg.causal,
+              sum_seq_lens=int(inp.seq_lens.sum()))
+    dims = api.make_dims(d["q_latent"], d["q_rope"], lat_all, rope_all, tables[0], **kw)
+    plan = api.make_plan(dims, NB)
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        api.mlra_decode_attention(d["q_latent"], d["q_rope"], lat_all, rope_all,
+                                  tables[i % copies], d["seq_lens"], NB, cfg.scale,
+                                  cfg.out_rescale, out=out, lse=lse, workspace=ws, **kw)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(copies):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+
+    # timed region: K steps between two events on the launch stream
+    per_step = []
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    if graph is not None:
+        reps = max(1, args.steps // copies)
+        for _ in range(reps):
+            graph.replay()
+        steps = reps * copies
+    else:
+        for i in range(args.steps):
+            step(i)
+        steps = args.steps
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / steps
+
+    # per-step events (separate pass) for the median
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(args.steps, 200))]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) for a, b in evs)
+    med_ms = per_step[len(per_step) // 2]
+
+    gbs = ab["total"] / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode attention latent-cache HBM GB/s (% of peak) + tokens/s at B=16, T=8k",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) latents and queries, shuffled paged blocks)",
+        "config": {"workload": cfg.name, "batch": cfg.num_seqs, "context": inp.max_seq_len,
+                   "q_len": cfg.q_len, "heads": cfg.num_heads, "n_branch": cfg.n_branch,
+                   "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "block_size": cfg.block_size,
+                   "cache_copies": copies, "tiles_per_split": plan.tiles_per_split,
+                   "splits_per_seq": plan.splits_per_seq, "graph": bool(graph)},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(cfg.num_seqs * cfg.q_len / (ms * 1e-3), 1),
+        "kv_tokens_per_s": round(ab["kv_tokens"] / (ms * 1e-3), 1),
+        "median_step_ms": round(med_ms, 5),
+        "algorithmic_bytes_per_step": ab["total"],
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -132,7 +132,7 @@ mlra_status mlra_decode_workspace_size(const mlra_decode_dims* dims, int32_t n_b
  *  block_table  [S][max_blocks_per_seq]   int32, physical block ids in [0, num_blocks)
  *  seq_lens     [S]                       int32, device; 0 <= L <= max_seq_len
  *  n_branch     branches in the cache and in q_latent: {1, 2, 4}
- *  scale        softmax scale on the raw dot products (finite)
+ *  scale        softmax scale on the raw dot products (finite, > 0)
  *  out_rescale  output factor (finite); 1/sqrt(4) for MLRA-4
  *  out          SUM: [S][Q][H][DC]; CONCAT: [S][Q][H][n_branch][DC]; dtype
  *  lse          [S][Q][H][n_branch] float32, natural log; -inf where V <= 0
@@ -140,8 +140,10 @@ mlra_status mlra_decode_workspace_size(const mlra_decode_dims* dims, int32_t n_b
  *               16-byte aligned; contents need no initialisation
  *
  * Alignment: every tensor pointer 16-byte aligned; cache strides multiples
- * of 16 bytes. Table entries past ceil(L/64) are never read, nor are cache
- * rows past L (they may hold NaN). Memory safety on bad input: a seq_lens
+ * of 16 bytes. Table entries past ceil(L/64) are never used (they may hold
+ * anything; the kernel may load but never dereferences them). Cache rows
+ * past L inside a sequence's last block may be loaded but never enter the
+ * arithmetic (they may hold NaN). Memory safety on bad input: a seq_lens
  * entry above max_seq_len is treated as max_seq_len, and a table entry
  * outside [0, num_blocks) reads block 0 instead; both give wrong results
  * for that sequence but never an out-of-bounds access.

@@ -32,7 +32,8 @@ def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     key = (device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        # zero-filled once: the library keeps its counter words at zero
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

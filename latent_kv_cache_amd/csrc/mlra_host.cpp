@@ -26,7 +26,7 @@ mlra_status resolve_dims(const mlra_decode_dims* d, int32_t n_branch, Resolved* 
   if (d->reduce != MLRA_BRANCH_SUM && d->reduce != MLRA_BRANCH_CONCAT) return MLRA_ERR_BAD_DIMS;
   if (d->reserved != 0) return MLRA_ERR_BAD_DIMS;
   if (d->num_seqs < 1 || d->num_heads < 1 || d->q_len < 1) return MLRA_ERR_BAD_DIMS;
-  if (d->num_seqs > 65535) return MLRA_ERR_UNSUPPORTED;  // grid y dimension
+  if (d->num_seqs > kMaxSeqs) return MLRA_ERR_UNSUPPORTED;  // grid y dimension
   if (d->q_len > 2) return MLRA_ERR_UNSUPPORTED;
   if (d->num_heads * d->q_len > 64) return MLRA_ERR_UNSUPPORTED;
   if (n_branch < 1) return MLRA_ERR_BAD_DIMS;
@@ -67,12 +67,17 @@ mlra_status resolve_dims(const mlra_decode_dims* d, int32_t n_branch, Resolved* 
   o.rst = d->rope_stride_token ? d->rope_stride_token : o.DR;
   o.rsb = d->rope_stride_block ? d->rope_stride_block : (int64_t)kBlock * o.rst;
   if (o.lsbr < 0 || o.lst < 0 || o.lsb < 0 || o.rst < 0 || o.rsb < 0) return MLRA_ERR_BAD_DIMS;
-  // Rows of one token / one block must not overlap each other.
-  if (o.NB > 1 && o.lsbr < o.DC) return MLRA_ERR_BAD_DIMS;
-  if (o.lst < (int64_t)(o.NB - 1) * o.lsbr + o.DC) return MLRA_ERR_BAD_DIMS;
+  // Token-major ([blk][64][NB][DC]) and branch-major ([blk][NB][64][DC]) are
+  // both accepted: strides must be positive and one block's rows must fit
+  // inside the block stride, so distinct blocks never overlap.
+  if ((o.NB > 1 && o.lsbr < 1) || o.lst < 1 || o.rst < 1) return MLRA_ERR_BAD_DIMS;
   if (o.lsb < (int64_t)(kBlock - 1) * o.lst + (int64_t)(o.NB - 1) * o.lsbr + o.DC)
     return MLRA_ERR_BAD_DIMS;
-  if (o.rst < o.DR || o.rsb < (int64_t)(kBlock - 1) * o.rst + o.DR) return MLRA_ERR_BAD_DIMS;
+  if (o.rsb < (int64_t)(kBlock - 1) * o.rst + o.DR) return MLRA_ERR_BAD_DIMS;
+  // Byte offsets inside one block are 32-bit on the device.
+  if ((o.lsb - 0) * (o.dtype == MLRA_BF16 ? 2 : 4) >= (int64_t(1) << 31) ||
+      o.rsb * (o.dtype == MLRA_BF16 ? 2 : 4) >= (int64_t(1) << 31))
+    return MLRA_ERR_UNSUPPORTED;
   // 16-byte rule for every stride.
   const int64_t vec = (o.dtype == MLRA_BF16) ? 8 : 4;
   if (o.lsbr % vec || o.lst % vec || o.lsb % vec || o.rst % vec || o.rsb % vec)
@@ -95,13 +100,11 @@ KernelShape choose_shape(const Resolved& r) {
   }
   k.variant = kVariantMfmaBf16;
   k.NT = r.rows > 32 ? 2 : 1;
-  k.WD = r.DC == 512 ? 4 : 1;
-  // Token-split waves so that a workgroup keeps four waves busy: one branch
-  // alone gets four waves over its tokens, two branches two waves each.
-  k.WT = (r.NB == 1 && k.WD == 1) ? 4 : (r.NB == 2 ? 2 : 1);
-  k.NPF = 2;
+  k.WD = mfma_wd(r.DC);
+  k.WT = mfma_wt(r.NB, r.DC, k.NT);
+  k.NPF = 2;  // sub-tiles in flight per wave (register prefetch)
   k.waves = r.NB * k.WD * k.WT;
-  k.groups_per_cu = 2;
+  k.groups_per_cu = 1;  // one workgroup fills a CU
   return k;
 }
 
@@ -143,7 +146,7 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
   p.tiles_per_split = (int32_t)tps;
   p.splits_per_seq = (int32_t)spl;
   p.lds_bytes = k.variant == kVariantMfmaBf16
-                    ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, k.NT, k.WT)
+                    ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, r.DR, k.NT, k.WT)
                     : 0;
   // Partials: output [S][spl][NB][rows][DC] and lse [S][spl][NB][rows], fp32.
   const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;

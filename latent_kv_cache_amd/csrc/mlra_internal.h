@@ -9,8 +9,25 @@
 namespace mlra {
 
 constexpr int kBlock = 64;      // tokens per cache block (= one split-K tile)
+constexpr int kMaxSeqs = 65535;  // grid y limit
 constexpr int kSub = 32;        // tokens per MFMA sub-tile (M of the 32x32 MFMA)
-constexpr int kLdsPad = 8;      // bf16 elements of padding per LDS latent row
+
+// Workgroup shape of the bf16 MFMA split kernel, shared by planner and
+// launcher. One workgroup fills one CU: 2 waves per SIMD when a wave holds 32
+// query rows (4 SIMDs -> 8 waves), 1 per SIMD with 64 rows or the 512-wide
+// latent. Its waves split the branches (NB), the latent width (WD) and the
+// workgroup's tiles (WT).
+constexpr int mfma_wd(int DC) { return DC == 512 ? 4 : 1; }
+constexpr int mfma_waves_per_simd(int NT, int DC) { return (NT == 1 && DC != 512) ? 2 : 1; }
+constexpr int mfma_wt(int NB, int DC, int NT) {
+  return 4 * mfma_waves_per_simd(NT, DC) / (NB * mfma_wd(DC)) > 0
+             ? 4 * mfma_waves_per_simd(NT, DC) / (NB * mfma_wd(DC))
+             : 1;
+}
+// Staged row pitches in 16-byte chunks: latent rows get 2 spare chunks, RoPE
+// rows 1 (see the kernel for the bank analysis).
+constexpr int mfma_lpitch(int DCW) { return DCW / 8 + 2; }
+constexpr int mfma_rpitch(int DR) { return DR / 8 + 1; }
 
 enum Variant : int32_t {
   kVariantValuFp32 = 1,  // float32 inputs: one wave per (row, branch), vector ALU
@@ -36,16 +53,23 @@ struct KernelShape {
   int32_t groups_per_cu;  // resident workgroups per CU the planner aims for
 };
 
-// LDS bytes of one MFMA split workgroup: the per-wave latent sub-tile used for
-// the LDS transpose, the score exchange when WD > 1, and (aliased over both,
-// after the token loop) the cross-wave merge buffer when WT > 1.
-inline int32_t mfma_lds_bytes(int NB, int DCW, int WD, int NT, int WT) {
+// LDS bytes of one MFMA split workgroup:
+//   latent sub-tile stage   one per wave           [32][lpitch] chunks
+//   RoPE sub-tile stage     one per (wt, branch)   [32][rpitch]
+//   latent query rows       one per (branch, wd)   [NT*32][lpitch]
+//   RoPE query rows         one                    [NT*32][rpitch]
+//   score exchange (WD > 1) [NB*WT][WD][NT][64 lanes][16 floats]
+// and, aliased over all of it after the token loop, the cross-wave merge
+// records when WT > 1: [WT][NB*WD][NT*NDT*4 + 1][64 lanes] float4.
+inline int32_t mfma_lds_bytes(int NB, int DCW, int WD, int DR, int NT, int WT) {
   const int waves = NB * WD * WT;
-  const int tile = waves * kSub * (DCW + kLdsPad) * 2;
-  const int xchg = (WD > 1) ? 2 * NB * WT * WD * NT * 64 * 16 * 4 : 0;
+  const int lp = mfma_lpitch(DCW), rp = mfma_rpitch(DR);
+  const int stage = waves * 32 * lp * 16 + NB * WT * 32 * rp * 16;
+  const int qry = (NB * WD * lp + rp) * NT * 32 * 16;
+  const int xchg = (WD > 1) ? NB * WT * WD * NT * 64 * 16 * 4 : 0;
   const int ndt = DCW / 32;
-  const int merge = (WT > 1) ? (WT - 1) * NB * WD * 64 * (NT * ndt * 16 + 4) * 4 : 0;
-  const int loop = tile + xchg;
+  const int merge = (WT > 1) ? WT * NB * WD * 64 * (NT * ndt * 16 + 4) * 4 : 0;
+  const int loop = stage + qry + xchg;
   return loop > merge ? loop : merge;
 }
 

@@ -87,6 +87,15 @@ __device__ __forceinline__ float wave_sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup barrier that orders LDS only: it does not wait for this wave's
+// outstanding global loads (a plain __syncthreads() would, which would stall
+// the software pipeline on its prefetches).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -94,65 +103,134 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 // ---------------------------------------------------------------------------
 // bf16 split kernel (MFMA)
 // ---------------------------------------------------------------------------
-template <int NL, int NR>
-struct SubTile {
-  u32x4 l[NL];  // latent: NL chunks of 8 bf16 (k-steps of S^T)
-  u32x4 r[NR];  // RoPE key: NR chunks of 8 bf16
-};
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-template <int NB, int DCW, int WD, int DR, int NT, int WT, int NPF>
+// LDS transpose read (gfx950 ds_read_b64_tr_b16): within each 16-lane group,
+// lane j supplies the address of 4 bf16 at row j/4, column 4*(j%4) of a 4x16
+// block; lane i receives column i, rows 0..3 of that block.
+__device__ __forceinline__ i16x4 lds_read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<unsigned char*>(p)));
+}
+
+// Staged rows are padded so that every LDS address is a per-lane base plus a
+// compile-time offset. Latent rows get 2 spare 16-byte chunks (pitch = 2 mod 16
+// chunks for 256-byte rows, 10 mod 16 for 128-byte rows): 8 lanes reading one
+// chunk of 8 consecutive rows, and a 16-lane transpose read of 4 consecutive
+// rows x 32 bytes, both land on distinct banks. RoPE rows (read row-wise
+// only) get 1 spare chunk, an odd pitch.
+
+template <int NB, int DCW, int WD, int DR, int NT, int WT, int WPS>
 __global__ void __launch_bounds__(64 * NB * WD * WT)
+__attribute__((amdgpu_waves_per_eu(WPS)))
 mlra_split_mfma(SplitParams p) {
   constexpr int DC = DCW * WD;
-  constexpr int DRW = DR / WD;
-  constexpr int NL = DCW / 16;
-  constexpr int NR = DRW / 16;
-  constexpr int NDT = DCW / 32;
-  constexpr int LDW = DCW + kLdsPad;
-  static_assert(NR >= 1 && NL >= 1 && NDT >= 1, "bad shape");
+  constexpr int NL = DCW / 16;   // S^T k-steps over this wave's latent slice
+  constexpr int NR = DR / 16;    // S^T k-steps over the RoPE key (wave wd == 0)
+  constexpr int NDT = DCW / 32;  // 32-wide d tiles of O^T
+  constexpr int LCH = DCW / 8;   // 16-byte chunks per staged latent row
+  constexpr int RCH = DR / 8;    // 16-byte chunks per staged RoPE row
+  constexpr int LQ = kSub * LCH / 64;  // coalesced 16-byte loads per lane per sub-tile
+  constexpr int RQ = kSub * RCH / 64;
+  constexpr int PD = 1;          // sub-tiles in flight per wave
+  constexpr int WAVES = NB * WD * WT;
+  constexpr int LP = mfma_lpitch(DCW);  // staged row pitch, 16-byte chunks
+  constexpr int RP = mfma_rpitch(DR);
+  static_assert(LQ >= 1 && RQ >= 1 && NDT >= 1, "bad shape");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int wd = wave % WD;
   const int b = (wave / WD) % NB;
   const int wt = wave / (WD * NB);
   const int n = lane & 31;
   const int g = lane >> 5;
+  const bool has_rope = WD == 1 || wd == 0;  // uniform per wave
 
   const int k = blockIdx.x;
   const int s = blockIdx.y;
-  const int L = seq_len_of(p.seq_lens, s, p.lcap);
-  const int ntiles = (L + kBlock - 1) / kBlock;
   const int t0 = k * p.tps;
-  if (t0 >= ntiles) return;  // uniform over the workgroup: no barrier skipped
-  const int t1 = min(t0 + p.tps, ntiles);
-
   const __bf16* __restrict__ qlat = static_cast<const __bf16*>(p.q_lat);
   const __bf16* __restrict__ qrop = static_cast<const __bf16*>(p.q_rope);
   const __bf16* __restrict__ lat = static_cast<const __bf16*>(p.lat);
   const __bf16* __restrict__ rope = static_cast<const __bf16*>(p.rope);
 
-  // Query rows as the B operand of S^T = C . Q^T (zero for padding rows).
-  bf16x8 qL[NT][NL], qR[NT][NR];
-  int vis[NT];
+  // Independent loads first: sequence length, this wave's first 64 block ids
+  // (any id below max_blocks lies inside the table) and the queries.
+  const int L_raw = p.seq_lens[s];
+  const int64_t tab_base = (int64_t)s * p.max_blocks;
+  // Loads in this prologue are unconditional (clamped, in-bounds addresses,
+  // results selected afterwards) so that the compiler can count outstanding
+  // loads exactly and never waits on more than it needs.
+  int tab = p.table[tab_base + min(t0 + wt + WT * lane, p.max_blocks - 1)];
+  int tab_chunk = 0;
+
+  // Query rows (the B operand of S^T = C . Q^T) are staged once per workgroup
+  // in LDS, padded like the cache tiles: latent rows per (branch, width
+  // slice), RoPE rows once (shared by all branches). Every wave loads a share
+  // first, before its cache loads, so that writing it to LDS waits only on
+  // these loads. K-slot (g, e) of step st is latent feature g*DCW/2 + 8*st + e
+  // of the slice, or RoPE feature g*DR/2 + 8*st + e. Padding rows are zero.
+  constexpr int QL_CH = NB * WD * NT * kSub * LCH;  // latent query chunks
+  constexpr int Q_CH = QL_CH + NT * kSub * RCH;     // + RoPE query chunks
+  constexpr int QK = (Q_CH + WAVES * 64 - 1) / (WAVES * 64);
+  u32x4 qv[QK];
+  int qdst[QK];  // LDS byte offset in the query region, -1 = none
+#pragma unroll
+  for (int kq = 0; kq < QK; ++kq) {
+    const int x = (kq * WAVES + wave) * 64 + lane;
+    const bool is_lat = x < QL_CH;
+    const bool is_rope = !is_lat && x < Q_CH;
+    // latent chunk coordinates
+    const int gq = x / (NT * kSub * LCH), rem = x % (NT * kSub * LCH);
+    const int rl = rem / LCH, cl = rem % LCH;
+    // RoPE chunk coordinates
+    const int xr = is_rope ? x - QL_CH : 0;
+    const int rr = xr / RCH, cr = xr % RCH;
+    const int r = is_lat ? rl : rr;
+    const bool live = (is_lat || is_rope) && r < p.rows;
+    const int rs = live ? r : 0;
+    const int j = rs / p.H, h = rs % p.H;
+    const int64_t head = ((int64_t)s * p.Q + j) * p.H + h;
+    const __bf16* src = is_lat ? qlat + (head * NB + (is_lat ? gq / WD : 0)) * DC +
+                                     (is_lat ? gq % WD : 0) * DCW + cl * 8
+                               : qrop + head * DR + cr * 8;
+    const u32x4 v = ld16(src);
+    qv[kq] = live ? v : u32x4{};
+    qdst[kq] = is_lat ? ((gq * NT * kSub + rl) * LP + cl) * 16
+                      : (is_rope ? NB * WD * NT * kSub * LP * 16 + (rr * RP + cr) * 16 : -1);
+  }
+
+  int jrow[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = nt * 32 + n;
-    const bool ok = row < p.rows;
-    const int j = ok ? row / p.H : 0;
-    const int h = ok ? row % p.H : 0;
-    vis[nt] = p.causal ? L - (p.Q - 1 - j) : L;
-    const int64_t qb = ((((int64_t)s * p.Q + j) * p.H + h) * NB + b) * DC + wd * DCW + g * (DCW / 2);
-    const int64_t rb = (((int64_t)s * p.Q + j) * p.H + h) * DR + wd * DRW + g * (DRW / 2);
-#pragma unroll
-    for (int st = 0; st < NL; ++st)
-      qL[nt][st] = ok ? __builtin_bit_cast(bf16x8, ld16(qlat + qb + 8 * st)) : bf16x8{};
-#pragma unroll
-    for (int st = 0; st < NR; ++st)
-      qR[nt][st] = ok ? __builtin_bit_cast(bf16x8, ld16(qrop + rb + 8 * st)) : bf16x8{};
+    jrow[nt] = row < p.rows ? row / p.H : 0;
   }
 
+  const int L = L_raw < 0 ? 0 : (L_raw > p.lcap ? p.lcap : L_raw);
+  const int ntiles = (L + kBlock - 1) / kBlock;
+  if (t0 >= ntiles) return;  // uniform over the workgroup: no barrier skipped
+  const int t1 = min(t0 + p.tps, ntiles);
+  int vis[NT];
+  const int min_vis = p.causal ? L - (p.Q - 1) : L;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) vis[nt] = p.causal ? L - (p.Q - 1 - jrow[nt]) : L;
+
+  // Query rows, the B operand of S^T = C . Q^T, staged once per (branch,
+  // width slice) in LDS with the same padded row layout as the cache tiles.
+  // K-slot (g, e) of step st is latent feature g*DCW/2 + 8*st + e of this
+  // wave's slice, or RoPE feature g*DR/2 + 8*st + e. Padding rows are zero.
+  // LDS layout (see mfma_lds_bytes). The RoPE query rows are shared by all
+  // branches and staged once; RoPE tiles only by the waves that use them.
+  unsigned char* stage_l = smem + wave * kSub * LP * 16;
+  unsigned char* const rope_base = smem + WAVES * kSub * LP * 16;
+  unsigned char* stage_r = rope_base + (wt * NB + b) * kSub * RP * 16;
+  unsigned char* const q_base = rope_base + NB * WT * kSub * RP * 16;
+  unsigned char* q_l = q_base + (b * WD + wd) * NT * kSub * LP * 16;
+  unsigned char* q_r = q_base + NB * WD * NT * kSub * LP * 16;
+  float* xchg = reinterpret_cast<float*>(q_r + NT * kSub * RP * 16);
   f32x16 acc[NT][NDT];
   float m_run[NT], l_run[NT];
 #pragma unroll
@@ -163,79 +241,133 @@ mlra_split_mfma(SplitParams p) {
     for (int dt = 0; dt < NDT; ++dt) acc[nt][dt] = f32x16{};
   }
 
-  // This wave's tiles: t0 + wt + WT*i for i < my_tiles (uniform across the
-  // workgroup up to masking), two 32-token sub-tiles each.
+  // This wave's tiles are t0 + wt + WT*i; each is two 32-token sub-tiles.
   const int nu = 2 * ((t1 - t0 + WT - 1) / WT);
-  const int nup = (nu + NPF - 1) / NPF * NPF;
-  const int64_t tab_base = (int64_t)s * p.max_blocks;
-  int tab = 0, tab_chunk = -1;
 
-  __bf16* tile_lds = reinterpret_cast<__bf16*>(smem) + wave * (kSub * LDW);
-  float* xchg = reinterpret_cast<float*>(smem + NB * WD * WT * kSub * LDW * 2);
-
-  auto load = [&](int u, SubTile<NL, NR>& bf) {
+  // Coalesced loads of one sub-tile: instruction q, lane -> 16-byte chunk
+  // x = 64*q + lane, i.e. row x / CH, chunk x % CH. Every address is valid: a
+  // missing tile reads block 0 and rows past L stay inside their block; such
+  // rows are zeroed (zero_tail) before any arithmetic.
+  u32x4 bl[PD][LQ], br[PD][RQ];
+  // lane -> (row, chunk) of the first load instruction; instruction q adds
+  // 64/CH rows. Offsets are bytes within one cache block (< 2^31, checked on
+  // the host).
+  const uint32_t l_lane = (uint32_t)((lane / LCH) * p.lst * 2 + (lane % LCH) * 16);
+  const uint32_t l_step = (uint32_t)((64 / LCH) * p.lst * 2);
+  const uint32_t r_lane = (uint32_t)((lane / RCH) * p.rst * 2 + (lane % RCH) * 16);
+  const uint32_t r_step = (uint32_t)((64 / RCH) * p.rst * 2);
+  auto load_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
     const int i = u >> 1;
     const int ti = t0 + wt + WT * i;
     const bool valid = (u < nu) && ti < t1;
-    const int c = i >> 6;
-    if (c != tab_chunk) {  // uniform: refresh 64 block ids at once
-      const int tj = t0 + wt + WT * (c * 64 + lane);
-      tab = tj < t1 ? p.table[tab_base + tj] : 0;
-      tab_chunk = c;
+    if ((i >> 6) != tab_chunk) {  // uniform: next 64 block ids of this wave
+      tab_chunk = i >> 6;
+      tab = p.table[tab_base + min(t0 + wt + WT * (tab_chunk * 64 + lane), p.max_blocks - 1)];
     }
-    const int phys = clamp_block(__builtin_amdgcn_readlane(tab, i & 63), p.num_blocks);
-    const int slot = (u & 1) * kSub + n;
-    const bool pred = valid && (ti * kBlock + slot) < L;
-    const __bf16* lp = lat + (int64_t)phys * p.lsb + (int64_t)slot * p.lst +
-                       (int64_t)b * p.lsbr + wd * DCW + g * (DCW / 2);
-    const __bf16* rp = rope + (int64_t)phys * p.rsb + (int64_t)slot * p.rst + wd * DRW +
-                       g * (DRW / 2);
-    if (pred) {
+    const int phys = valid ? clamp_block(__builtin_amdgcn_readlane(tab, i & 63), p.num_blocks) : 0;
+    const int sub = (u & 1) * kSub;
+    // uniform base of this sub-tile (scalar registers) + 32-bit lane offset
+    const char* lb = reinterpret_cast<const char*>(lat) +
+                     ((int64_t)phys * p.lsb + (int64_t)sub * p.lst + (int64_t)b * p.lsbr + wd * DCW) * 2;
 #pragma unroll
-      for (int st = 0; st < NL; ++st) bf.l[st] = ld16(lp + 8 * st);
+    for (int q = 0; q < LQ; ++q) dl[q] = ld16(lb + (size_t)q * l_step + l_lane);
+    if (has_rope) {
+      const char* rbp = reinterpret_cast<const char*>(rope) +
+                        ((int64_t)phys * p.rsb + (int64_t)sub * p.rst) * 2;
 #pragma unroll
-      for (int st = 0; st < NR; ++st) bf.r[st] = ld16(rp + 8 * st);
-    } else {
+      for (int q = 0; q < RQ; ++q) dr[q] = ld16(rbp + (size_t)q * r_step + r_lane);
+    }
+  };
+  auto zero_tail = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
+    const int ti = t0 + wt + WT * (u >> 1);
+    const bool valid = (u < nu) && ti < t1;
+    const int tok0 = ti * kBlock + (u & 1) * kSub;
+    if (!(valid && tok0 + kSub <= L)) {  // uniform
 #pragma unroll
-      for (int st = 0; st < NL; ++st) bf.l[st] = u32x4{};
+      for (int q = 0; q < LQ; ++q) {
+        const bool keep = valid && tok0 + (q * 64 + lane) / LCH < L;
+        dl[q] = keep ? dl[q] : u32x4{};
+      }
 #pragma unroll
-      for (int st = 0; st < NR; ++st) bf.r[st] = u32x4{};
+      for (int q = 0; q < RQ; ++q) {
+        const bool keep = valid && tok0 + (q * 64 + lane) / RCH < L;
+        dr[q] = keep ? dr[q] : u32x4{};
+      }
+    }
+  };
+  unsigned char* const wl_base = stage_l + ((lane / LCH) * LP + lane % LCH) * 16;
+  unsigned char* const wr_base = stage_r + ((lane / RCH) * RP + lane % RCH) * 16;
+  auto stage_unit = [&](const u32x4 (&dl)[LQ], const u32x4 (&dr)[RQ]) {
+#pragma unroll
+    for (int q = 0; q < LQ; ++q)
+      *reinterpret_cast<u32x4*>(wl_base + q * (64 / LCH) * LP * 16) = dl[q];
+    if (has_rope) {
+#pragma unroll
+      for (int q = 0; q < RQ; ++q)
+        *reinterpret_cast<u32x4*>(wr_base + q * (64 / RCH) * RP * 16) = dr[q];
     }
   };
 
-  auto compute = [&](int u, const SubTile<NL, NR>& bf) {
-    const int i = u >> 1;
-    const int ti = t0 + wt + WT * i;
+  // lane bases of the operand reads: row n, chunk g*CH/2 (A of S^T); the
+  // transpose reads of C^T start at row 4*(lane/32) + (lane%16)/4, column
+  // 16*((lane/16)%2) + 4*(lane%4).
+  const unsigned char* const al_base = stage_l + (n * LP + g * (LCH / 2)) * 16;
+  const unsigned char* const ar_base = stage_r + (n * RP + g * (RCH / 2)) * 16;
+  const unsigned char* const ql_base = q_l + (n * LP + g * (LCH / 2)) * 16;
+  const unsigned char* const qr_base = q_r + (n * RP + g * (RCH / 2)) * 16;
+  const unsigned char* const tr_base =
+      stage_l + (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
+      (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
+  // One sub-tile: scores, masking, online softmax, P.C.
+  auto compute_unit = [&](int u) {
+    const int ti = t0 + wt + WT * (u >> 1);
     const bool valid = (u < nu) && ti < t1;
     const int tb = ti * kBlock + (u & 1) * kSub;
 
-    // scores S^T[token][row], fp32 accumulate
+    // S^T[token][row] = C . Q^T with A read row-wise from the staged tile
     f32x16 sc[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      sc[nt] = f32x16{};
+    for (int nt = 0; nt < NT; ++nt) sc[nt] = f32x16{};
+    if (has_rope) {
 #pragma unroll
-      for (int st = 0; st < NL; ++st)
-        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bf.l[st]),
-                                                         qL[nt][st], sc[nt], 0, 0, 0);
+      for (int st = 0; st < NR; ++st) {
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ar_base + st * 16));
 #pragma unroll
-      for (int st = 0; st < NR; ++st)
-        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bf.r[st]),
-                                                         qR[nt][st], sc[nt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8 qv = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(qr_base + (nt * kSub * RP + st) * 16));
+          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv, sc[nt], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < NL; ++st) {
+      const bf16x8 a =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(al_base + st * 16));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 qv = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(ql_base + (nt * kSub * LP + st) * 16));
+        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv, sc[nt], 0, 0, 0);
+      }
     }
 
     if constexpr (WD > 1) {
-      // Sum the WD partial score tiles (each wave holds a slice of the
-      // latent width) in a fixed order so every wave gets identical scores.
+      // Sum the WD partial score tiles (each wave holds a slice of the latent
+      // width; wave 0 also the RoPE part) in a fixed order so every wave gets
+      // identical scores.
       const int grp = wt * NB + b;
-      f32x4* X = reinterpret_cast<f32x4*>(xchg) + (u & 1) * (NB * WT * WD * NT * 4 * 64);
+      f32x4* X = reinterpret_cast<f32x4*>(xchg);
+      lds_barrier();  // the previous sub-tile's reads of X are done
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           X[(((grp * WD + wd) * NT + nt) * 4 + q) * 64 + lane] =
               f32x4{sc[nt][4 * q], sc[nt][4 * q + 1], sc[nt][4 * q + 2], sc[nt][4 * q + 3]};
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -243,91 +375,125 @@ mlra_split_mfma(SplitParams p) {
           f32x4 t = X[(((grp * WD + 0) * NT + nt) * 4 + q) * 64 + lane];
 #pragma unroll
           for (int w = 1; w < WD; ++w) t += X[(((grp * WD + w) * NT + nt) * 4 + q) * 64 + lane];
-          sc[nt][4 * q] = t[0];
-          sc[nt][4 * q + 1] = t[1];
-          sc[nt][4 * q + 2] = t[2];
-          sc[nt][4 * q + 3] = t[3];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[nt][4 * q + e] = t[e];
         }
     }
 
-    // wave-private LDS copy of the latent sub-tile, row-major [32][LDW]
+    // Mask tokens past a row's visible length (only when the sub-tile reaches
+    // past the shortest row, or holds no tile).
+    if (!(valid && tb + kSub <= min_vis)) {
 #pragma unroll
-    for (int st = 0; st < NL; ++st)
-      *reinterpret_cast<u32x4*>(tile_lds + n * LDW + g * (DCW / 2) + 8 * st) = bf.l[st];
+      for (int nt = 0; nt < NT; ++nt) {
+        const int lim = valid ? vis[nt] : 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = tb + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (tok >= lim) sc[nt][r] = -INFINITY;
+        }
+      }
+    }
 
-    // online softmax per query row (row = lane column of the MFMA tile)
+    // Online softmax per query row (row = lane column of the MFMA tile); the
+    // accumulator is rescaled only when some row's maximum grew.
     bf16x8 pB[NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int lim = valid ? vis[nt] : 0;
-      float x[16];
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = tb + 8 * (r >> 2) + 4 * g + (r & 3);
-        x[r] = tok < lim ? sc[nt][r] * p.score_scale : -INFINITY;
-        mx = fmaxf(mx, x[r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nt][r]);
+      mx = wave_max_halves(mx) * p.score_scale;
+      const bool grow = mx > m_run[nt];
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[nt] - mx) : 1.f;
+        m_run[nt] = grow ? mx : m_run[nt];
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[nt][dt] *= alpha;
       }
-      mx = wave_max_halves(mx);
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+      const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
       float sum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x[r] = __builtin_amdgcn_exp2f(x[r] - m_use);
-        sum += x[r];
-      }
-      l_run[nt] = l_run[nt] * alpha + sum;
-      m_run[nt] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[nt][dt] *= alpha;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pB[nt][h2][e] = (__bf16)x[8 * h2 + e];
+        for (int e = 0; e < 8; ++e) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sc[nt][8 * h2 + e], p.score_scale, -m_use));
+          sum += pe;
+          pB[nt][h2][e] = (__bf16)pe;
+        }
+      l_run[nt] += sum;
     }
 
-    // O^T[d][row] += C^T[d][t] . P^T[t][row]; K-slot e of lane group g in
-    // half h2 is token 16*h2 + 8*(e/4) + 4*g + e%4, matching P's registers.
+    // O^T[d][row] += C^T[d][t] . P^T[t][row]. K-slot e of lane group g in half
+    // h2 is token 16*h2 + 8*(e/4) + 4*g + e%4, where P already sits; C^T comes
+    // from two LDS transpose reads of 4 tokens each.
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        bf16x8 a;
-        const __bf16* col = tile_lds + dt * 32 + n;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          a[e] = col[(16 * h2 + 8 * (e >> 2) + 4 * g + (e & 3)) * LDW];
+        const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
+        const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[nt][h2], acc[nt][dt], 0, 0, 0);
       }
-    }
   };
 
-  SubTile<NL, NR> buf[NPF];
+  // Software pipeline: PD sub-tiles in flight in registers; the wave stages
+  // one into LDS, refills its registers with the sub-tile PD ahead, computes.
+  const int nsteps = (nu + PD - 1) / PD * PD;
 #pragma unroll
-  for (int i = 0; i < NPF; ++i) load(i, buf[i]);
-  for (int u0 = 0; u0 < nup; u0 += NPF) {
+  for (int i = 0; i < PD; ++i) load_unit(i, bl[i], br[i]);
 #pragma unroll
-    for (int i = 0; i < NPF; ++i) {
-      compute(u0 + i, buf[i]);
-      if (u0 + i + NPF < nup) load(u0 + i + NPF, buf[i]);
+  for (int kq = 0; kq < QK; ++kq)
+    if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(q_base + qdst[kq]) = qv[kq];
+  lds_barrier();  // queries staged
+  for (int u0 = 0; u0 < nsteps; u0 += PD) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) {
+      const int u = u0 + i;
+      zero_tail(u, bl[i], br[i]);
+      stage_unit(bl[i], br[i]);
+      if (u + PD < nsteps) load_unit(u + PD, bl[i], br[i]);
+      compute_unit(u);
     }
   }
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) l_run[nt] = wave_sum_halves(l_run[nt]);
 
-  if constexpr (WT > 1) {
-    // Merge the WT token-split waves of each (branch, width slice) in LDS.
+  const int64_t slot = (int64_t)s * p.spl + k;
+  if constexpr (WT == 1) {
+    // Partial (output / l, lse) of this split for each (branch, row).
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int row = nt * 32 + n;
+      if (row >= p.rows) continue;
+      const float l = l_run[nt];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int64_t ri = (slot * NB + b) * p.rows + row;
+      float* o = p.part_o + ri * DC + wd * DCW;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
+              f32x4{acc[nt][dt][4 * q], acc[nt][dt][4 * q + 1], acc[nt][dt][4 * q + 2],
+                    acc[nt][dt][4 * q + 3]} * inv;
+      if (g == 0 && wd == 0)
+        p.part_lse[ri] = l > 0.f ? (m_run[nt] + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  } else {
+    // Merge the WT token-split waves of each (branch, width slice): every wave
+    // publishes its record, then wave wt merges the d-tiles dt = wt, wt+WT, ...
     constexpr int REC = NT * NDT * 4 + 1;  // float4 records per lane
-    __syncthreads();
+    __syncthreads();  // all waves are done with the staged tiles
     f32x4* M = reinterpret_cast<f32x4*>(smem);
     const int gi = b * WD + wd;
-    if (wt > 0) {
-      f32x4* my = M + ((wt - 1) * NB * WD + gi) * REC * 64;
+    {
+      f32x4* my = M + (wt * NB * WD + gi) * REC * 64;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -341,54 +507,53 @@ mlra_split_mfma(SplitParams p) {
                                         NT > 1 ? l_run[NT - 1] : 0.f};
     }
     __syncthreads();
-    if (wt > 0) return;
-#pragma unroll 1
-    for (int w = 1; w < WT; ++w) {
-      const f32x4* ot = M + ((w - 1) * NB * WD + gi) * REC * 64;
-      const f32x4 ml = ot[(REC - 1) * 64 + lane];
+    float ms[WT][NT], ls[WT][NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float mw = nt == 0 ? ml[0] : ml[2];
-        const float lw = nt == 0 ? ml[1] : ml[3];
-        const float m_new = fmaxf(m_run[nt], mw);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float a0 = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
-        const float a1 = __builtin_amdgcn_exp2f(mw - m_use);
-        l_run[nt] = l_run[nt] * a0 + lw * a1;
-        m_run[nt] = m_new;
+    for (int w = 0; w < WT; ++w) {
+      const f32x4 ml = M[((w * NB * WD + gi) * REC + REC - 1) * 64 + lane];
+      ms[w][0] = ml[0];
+      ls[w][0] = ml[1];
+      if constexpr (NT > 1) {
+        ms[w][NT - 1] = ml[2];
+        ls[w][NT - 1] = ml[3];
+      }
+    }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+    for (int nt = 0; nt < NT; ++nt) {
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WT; ++w) mm = fmaxf(mm, ms[w][nt]);
+      const float m_use = mm == -INFINITY ? 0.f : mm;
+      float wsc[WT];
+      float l = 0.f;
+#pragma unroll
+      for (int w = 0; w < WT; ++w) {
+        wsc[w] = __builtin_amdgcn_exp2f(ms[w][nt] - m_use);
+        l += ls[w][nt] * wsc[w];
+      }
+      const int row = nt * 32 + n;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int64_t ri = (slot * NB + b) * p.rows + row;
+      if (row < p.rows) {
+        float* o = p.part_o + ri * DC + wd * DCW;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          if (dt % WT != wt) continue;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x4 v = ot[((nt * NDT + dt) * 4 + q) * 64 + lane];
+            f32x4 v = f32x4{};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[nt][dt][4 * q + e] = acc[nt][dt][4 * q + e] * a0 + v[e] * a1;
+            for (int w = 0; w < WT; ++w)
+              v += M[((w * NB * WD + gi) * REC + (nt * NDT + dt) * 4 + q) * 64 + lane] * wsc[w];
+            *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
           }
+        }
+        if (g == 0 && wd == 0 && wt == 0)
+          p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
       }
     }
   }
 
-  // Partial (output / l, lse) of this split for each (branch, row).
-  const int64_t slot = (int64_t)s * p.spl + k;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = nt * 32 + n;
-    if (row >= p.rows) continue;
-    const float l = l_run[nt];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t ri = (slot * NB + b) * p.rows + row;
-    float* o = p.part_o + ri * DC + wd * DCW;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
-            f32x4{acc[nt][dt][4 * q], acc[nt][dt][4 * q + 1], acc[nt][dt][4 * q + 2],
-                  acc[nt][dt][4 * q + 3]} * inv;
-    if (g == 0 && wd == 0)
-      p.part_lse[ri] = l > 0.f ? (m_run[nt] + __log2f(l)) * kLn2 : -INFINITY;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -458,59 +623,159 @@ __global__ void __launch_bounds__(256) mlra_split_valu(SplitParams p) {
 // ---------------------------------------------------------------------------
 // combine: log-sum-exp merge of the splits, branch sum / concat, rescale
 // ---------------------------------------------------------------------------
-template <typename OutT>
-__device__ __forceinline__ void store4(OutT* dst, f32x4 v);
-
-template <>
-__device__ __forceinline__ void store4<float>(float* dst, f32x4 v) {
-  *reinterpret_cast<f32x4*>(dst) = v;
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
 }
 
-template <>
-__device__ __forceinline__ void store4<__bf16>(__bf16* dst, f32x4 v) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-  *reinterpret_cast<bf16x4*>(dst) = o;
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
 }
 
-template <typename OutT>
-__global__ void __launch_bounds__(256) mlra_combine(CombineParams c) {
-  const int tpr = c.DC / 4;
-  const int row = blockIdx.x * (256 / tpr) + threadIdx.x / tpr;
-  const int d4 = threadIdx.x % tpr;
-  const int s = blockIdx.y;
-  if (row >= c.rows) return;
-  const int L = seq_len_of(c.seq_lens, s, c.lcap);
-  const int ntiles = (L + kBlock - 1) / kBlock;
-  const int nsplit = min((ntiles + c.tps - 1) / c.tps, c.spl);
+template <typename OutT, int VPL>
+__device__ __forceinline__ void store_vpl(OutT* dst, const float* v);
+
+template <>
+__device__ __forceinline__ void store_vpl<float, 1>(float* d, const float* v) { d[0] = v[0]; }
+template <>
+__device__ __forceinline__ void store_vpl<float, 2>(float* d, const float* v) {
+  *reinterpret_cast<float2*>(d) = make_float2(v[0], v[1]);
+}
+template <>
+__device__ __forceinline__ void store_vpl<float, 4>(float* d, const float* v) {
+  *reinterpret_cast<f32x4*>(d) = f32x4{v[0], v[1], v[2], v[3]};
+}
+template <>
+__device__ __forceinline__ void store_vpl<float, 8>(float* d, const float* v) {
+  *reinterpret_cast<f32x4*>(d) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(d + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+template <int VPL>
+__device__ __forceinline__ void store_bf16(__bf16* d, const float* v) {
+  typedef __bf16 vec __attribute__((ext_vector_type(VPL)));
+  vec o;
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) o[e] = (__bf16)v[e];
+  *reinterpret_cast<vec*>(d) = o;
+}
+template <>
+__device__ __forceinline__ void store_vpl<__bf16, 1>(__bf16* d, const float* v) { d[0] = (__bf16)v[0]; }
+template <>
+__device__ __forceinline__ void store_vpl<__bf16, 2>(__bf16* d, const float* v) { store_bf16<2>(d, v); }
+template <>
+__device__ __forceinline__ void store_vpl<__bf16, 4>(__bf16* d, const float* v) { store_bf16<4>(d, v); }
+template <>
+__device__ __forceinline__ void store_vpl<__bf16, 8>(__bf16* d, const float* v) { store_bf16<8>(d, v); }
+
+// One wave (one workgroup) per (sequence, query row). Lane k holds split k's
+// lse; the weights exp(lse_k - max) are broadcast with readlane while lanes
+// sum the split outputs over the feature range (VPL = DC/64 values per lane).
+// The first split batch's loads are issued before seq_lens has arrived
+// (splits past the sequence's count are masked with selects, so stale
+// workspace contents can never reach the result).
+template <int VPL>
+__device__ __forceinline__ void load_vpl(float (&v)[VPL], const float* src) {
+  if constexpr (VPL >= 4) {
+#pragma unroll
+    for (int e4 = 0; e4 < VPL; e4 += 4) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(src + e4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e4 + e] = t[e];
+    }
+  } else if constexpr (VPL == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(src);
+    v[0] = t.x;
+    v[1] = t.y;
+  } else {
+    v[0] = src[0];
+  }
+}
+
+template <typename OutT, int VPL>
+__global__ void __launch_bounds__(64) mlra_combine(CombineParams c) {
+  constexpr int KB = VPL >= 4 ? 8 : 16;  // splits whose loads are in flight together
+  const int lane = threadIdx.x;
+  const int pair = blockIdx.x;
+  const int s = pair / c.rows, row = pair % c.rows;
+  const int L_raw = c.seq_lens[s];
   const int j = row / c.H, h = row % c.H;
   const int64_t orow = ((int64_t)s * c.Q + j) * c.H + h;
+  const int64_t kstride = (int64_t)c.NB * c.rows;  // between splits, in rows
+  const int last = c.spl - 1;
   OutT* out = static_cast<OutT*>(c.out);
-  f32x4 tot = {};
+  float tot[VPL];
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) tot[e] = 0.f;
   for (int b = 0; b < c.NB; ++b) {
-    float M = -INFINITY;
-    for (int k = 0; k < nsplit; ++k)
-      M = fmaxf(M, c.part_lse[(((int64_t)s * c.spl + k) * c.NB + b) * c.rows + row]);
-    f32x4 o = {};
+    const int64_t base = ((int64_t)s * c.spl * c.NB + b) * c.rows + row;
+    const float* lse_p = c.part_lse + base;
+    const float* o_p = c.part_o + base * c.DC + lane * VPL;
+    // Unconditional loads (indices clamped into the plan's splits) so the
+    // compiler keeps them all in flight; results past the sequence's split
+    // count are discarded with selects.
+    float v[KB][VPL];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) load_vpl<VPL>(v[u], o_p + (int64_t)min(u, last) * kstride * c.DC);
+    const float l0 = lse_p[(int64_t)min(lane, last) * kstride];
+    const int L = L_raw < 0 ? 0 : (L_raw > c.lcap ? c.lcap : L_raw);
+    const int nsplit = min((L + kBlock * c.tps - 1) / (kBlock * c.tps), c.spl);
+    float M = lane < nsplit ? l0 : -INFINITY;
+    for (int k0 = 64; k0 < nsplit; k0 += 64) {
+      const float lk = lse_p[(int64_t)min(k0 + lane, last) * kstride];
+      M = fmaxf(M, k0 + lane < nsplit ? lk : -INFINITY);
+    }
+    M = wave_max(M);
+    float o[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) o[e] = 0.f;
     float lse_b = -INFINITY;
     if (M != -INFINITY) {
       float den = 0.f;
-      for (int k = 0; k < nsplit; ++k) {
-        const int64_t ri = (((int64_t)s * c.spl + k) * c.NB + b) * c.rows + row;
-        const float w = expf(c.part_lse[ri] - M);
+      for (int k0 = 0; k0 < nsplit; k0 += 64) {
+        const float lk = k0 == 0 ? l0 : lse_p[(int64_t)min(k0 + lane, last) * kstride];
+        const float w = k0 + lane < nsplit ? expf(lk - M) : 0.f;
         den += w;
-        o += w * *reinterpret_cast<const f32x4*>(c.part_o + ri * c.DC + 4 * d4);
+        const int kn = min(64, nsplit - k0);
+        for (int q0 = 0; q0 < kn; q0 += KB) {
+          if (k0 + q0 > 0) {
+#pragma unroll
+            for (int u = 0; u < KB; ++u)
+              load_vpl<VPL>(v[u], o_p + (int64_t)min(k0 + q0 + u, last) * kstride * c.DC);
+          }
+#pragma unroll
+          for (int u = 0; u < KB; ++u) {
+            const bool use = q0 + u < kn;
+            const float wq =
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(q0 + u, 63)));
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) o[e] = use ? fmaf(wq, v[u][e], o[e]) : o[e];
+          }
+        }
       }
-      o *= 1.f / den;
+      den = wave_sum(den);
+      const float inv = 1.f / den;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) o[e] *= inv;
       lse_b = M + logf(den);
     }
-    if (c.concat)
-      store4<OutT>(out + (orow * c.NB + b) * c.DC + 4 * d4, o * c.out_rescale);
-    else
-      tot += o;
-    if (d4 == 0) c.lse[orow * c.NB + b] = lse_b;
+    if (c.concat) {
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) o[e] *= c.out_rescale;
+      store_vpl<OutT, VPL>(out + (orow * c.NB + b) * c.DC + lane * VPL, o);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) tot[e] += o[e];
+    }
+    if (lane == 0) c.lse[orow * c.NB + b] = lse_b;
   }
-  if (!c.concat) store4<OutT>(out + orow * c.DC + 4 * d4, tot * c.out_rescale);
+  if (!c.concat) {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) tot[e] *= c.out_rescale;
+    store_vpl<OutT, VPL>(out + orow * c.DC + lane * VPL, tot);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -519,14 +784,14 @@ __global__ void __launch_bounds__(256) mlra_combine(CombineParams c) {
 template <int NB, int DC, int DR, int NT>
 static hipError_t launch_mfma(const SplitParams& sp, const mlra_decode_plan& plan,
                               hipStream_t stream) {
-  constexpr int WD = DC == 512 ? 4 : 1;
+  constexpr int WD = mfma_wd(DC);
   constexpr int DCW = DC / WD;
-  constexpr int WT = (NB == 1 && WD == 1) ? 4 : (NB == 2 ? 2 : 1);
-  constexpr int NPF = 2;
-  auto kern = mlra_split_mfma<NB, DCW, WD, DR, NT, WT, NPF>;
-  const int lds = mfma_lds_bytes(NB, DCW, WD, NT, WT);
+  constexpr int WT = mfma_wt(NB, DC, NT);
+  constexpr int WPS = mfma_waves_per_simd(NT, DC);
+  auto kern = mlra_split_mfma<NB, DCW, WD, DR, NT, WT, WPS>;
+  const int lds = mfma_lds_bytes(NB, DCW, WD, DR, NT, WT);
   if (lds > 64 * 1024) {
-    static bool attr_set = false;  // per instance; benign race (idempotent call)
+    static bool attr_set = false;  // per instance; the call is idempotent
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -586,6 +851,14 @@ static hipError_t launch_split(const SplitParams& sp, const KernelShape& ks,
   return hipGetLastError();
 }
 
+template <int VPL>
+static void launch_combine(bool bf16, dim3 grid, const CombineParams& cp, hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL((mlra_combine<__bf16, VPL>), grid, dim3(64), 0, st, cp);
+  else
+    hipLaunchKernelGGL((mlra_combine<float, VPL>), grid, dim3(64), 0, st, cp);
+}
+
 static int device_cus(int* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -616,7 +889,8 @@ static mlra_status decode(const void* q_latent, const void* q_rope, const void* 
   if (!q_latent || !q_rope || !latent_cache || !rope_cache || !block_table || !seq_lens ||
       !out || !lse)
     return MLRA_ERR_NULL_PTR;
-  if (!std::isfinite(scale) || !std::isfinite(out_rescale)) return MLRA_ERR_BAD_DIMS;
+  if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(out_rescale))
+    return MLRA_ERR_BAD_DIMS;
   if (!aligned16(q_latent) || !aligned16(q_rope) || !aligned16(latent_cache) ||
       !aligned16(rope_cache) || !aligned16(out) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(block_table) & 3) ||
@@ -682,12 +956,15 @@ static mlra_status decode(const void* q_latent, const void* q_rope, const void* 
   cp.lcap = r.lcap;
   cp.concat = r.reduce == MLRA_BRANCH_CONCAT;
   cp.out_rescale = out_rescale;
-  const int rpb = 256 / (r.DC / 4);
-  dim3 cgrid((r.rows + rpb - 1) / rpb, r.S);
-  if (r.dtype == MLRA_BF16)
-    hipLaunchKernelGGL(mlra_combine<__bf16>, cgrid, dim3(256), 0, hs, cp);
-  else
-    hipLaunchKernelGGL(mlra_combine<float>, cgrid, dim3(256), 0, hs, cp);
+  dim3 cgrid(r.S * r.rows);
+  const bool bf = r.dtype == MLRA_BF16;
+  switch (r.DC / 64) {
+    case 1: launch_combine<1>(bf, cgrid, cp, hs); break;
+    case 2: launch_combine<2>(bf, cgrid, cp, hs); break;
+    case 4: launch_combine<4>(bf, cgrid, cp, hs); break;
+    case 8: launch_combine<8>(bf, cgrid, cp, hs); break;
+    default: return MLRA_ERR_UNSUPPORTED;
+  }
   if (hipGetLastError() != hipSuccess) return MLRA_ERR_HIP;
   return MLRA_OK;
 }

@@ -101,8 +101,8 @@ def test_ragged_hint_balances_splits(lib):
     ("num_seqs", 0, 2), ("q_len", 3, 3), ("num_heads", 33, 3), ("d_latent", 96, 3),
     ("d_rope", 48, 3), ("block_size", 32, 3), ("block_size", 0, 2), ("max_blocks_per_seq", 0, 2),
     ("max_seq_len", 10 ** 6, 2), ("max_seq_len", -1, 2), ("num_splits", -2, 2), ("dtype", 7, 2),
-    ("reduce", 2, 2), ("reserved", 1, 2), ("latent_stride_token", 100, 2),
-    ("latent_stride_token", 516, 5), ("rope_stride_token", 60, 2), ("sum_seq_lens", -1, 2),
+    ("reduce", 2, 2), ("reserved", 1, 2), ("latent_stride_block", 1000, 2),
+    ("latent_stride_token", 516, 5), ("rope_stride_block", 60, 2), ("sum_seq_lens", -1, 2),
     ("num_seqs", 70000, 3),
 ])
 def test_validation_errors(lib, field, value, status):

@@ -187,7 +187,7 @@ def test_branch_major_cache_strides():
 
 
 def test_empty_and_degenerate_sequences():
-    cfg = _cfg(q_len=2, num_seqs=5, context=130, seed=4)
+    cfg = _cfg(q_len=2, num_seqs=5, context=130, context_range=None, seed=4)
     inp = make_inputs(cfg)
     inp.seq_lens[:] = [0, 1, 2, 64, 130]
     _say("degenerate lengths")
@@ -202,7 +202,7 @@ def test_empty_and_degenerate_sequences():
 
 
 def test_seq_len_above_max_is_clamped_not_read_out_of_bounds():
-    cfg = _cfg(num_seqs=2, context=256, seed=3)
+    cfg = _cfg(num_seqs=2, context=256, context_range=None, seed=3)
     inp = make_inputs(cfg)
     d = to_device(inp)
     d["seq_lens"] = torch.tensor([10_000, 256], dtype=torch.int32, device="cuda")
