@@ -11,6 +11,10 @@ block table) that consecutive steps never find their data in the 256 MB
 Infinity Cache; HIP events on the launch stream bracket the K timed steps.
 value = algorithmic HBM bytes per step / time per step (GB/s); algorithmic
 bytes = cache rows read + queries + block-table entries + seq_lens + outputs.
+A second pass issues the same K steps as their two halves (split kernel, then
+combine kernel) with events between them: roofline.achieved is the split
+kernel's algorithmic bytes (everything above but the outputs) over its
+average event-timed duration.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
                        [--workload NAME] [--no-cpu-baseline] [--graph]
@@ -18,6 +22,7 @@ Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -44,7 +49,38 @@ def algorithmic_bytes(inp) -> dict:
     out = c.num_seqs * c.q_len * c.num_heads * c.d_latent * el
     lse = c.num_seqs * c.q_len * c.num_heads * c.n_branch * 4
     total = cache + q + table + lens + out + lse
-    return dict(total=total, cache=cache, kv_tokens=int(L.sum()))
+    return dict(total=total, cache=cache, out=out, lse=lse, kv_tokens=int(L.sum()))
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the kernel sources, to tell whether a stored counter
+    measurement still describes the kernel that runs."""
+    h = hashlib.sha256()
+    for name in ("mlra_kernels.hip", "mlra_internal.h"):
+        with open(os.path.join(ROOT, "latent_kv_cache_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per split-kernel launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when there is none for this workload or the kernel source has changed."""
+    path = os.path.join(ROOT, "profiles", f"mlra_split_mfma_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def flops(inp) -> int:
@@ -121,14 +157,13 @@ def main() -> int:
     lse = torch.empty((S, Q, H, NB), dtype=torch.float32, device=dev)
     kw = dict(max_seq_len=inp.max_seq_len, reduce=reduce, causal=cfg.causal,
               sum_seq_lens=int(inp.seq_lens.sum()))
-    dims = api.make_dims(d["q_latent"], d["q_rope"], lat_all, rope_all, tables[0], **kw)
-    plan = api.make_plan(dims, NB)
-    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    prep = api.PreparedDecode(d["q_latent"], d["q_rope"], lat_all, rope_all, tables[0],
+                              d["seq_lens"], NB, cfg.scale, cfg.out_rescale, out=out, lse=lse,
+                              **kw)
+    plan = prep.plan
 
     def step(i):
-        api.mlra_decode_attention(d["q_latent"], d["q_rope"], lat_all, rope_all,
-                                  tables[i % copies], d["seq_lens"], NB, cfg.scale,
-                                  cfg.out_rescale, out=out, lse=lse, workspace=ws, **kw)
+        prep.run(tables[i % copies])
 
     for i in range(args.warmup):
         step(i)
@@ -138,13 +173,14 @@ def main() -> int:
     if args.graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
+            cs = torch.cuda.current_stream().cuda_stream
             for i in range(copies):
-                step(i)
+                prep.run(tables[i], stream=cs)
         graph.replay()
         torch.cuda.synchronize()
 
-    # timed region: K steps between two events on the launch stream
-    per_step = []
+    # Timed region: K steps between two events on the launch stream (torch's
+    # current stream, which the prepared call enqueues on).
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -159,19 +195,28 @@ def main() -> int:
         steps = args.steps
     stop.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms = total_ms / steps
+    ms = start.elapsed_time(stop) / steps
 
-    # per-step events (separate pass) for the median
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(min(args.steps, 200))]
-    for i, (a, b) in enumerate(evs):
+    # Kernel pass: the same K steps, issued as the two halves of the call with
+    # an event before, between and after them, to time each kernel alone.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i, (a, b, c) in enumerate(ev):
         a.record()
-        step(i)
+        prep.partials(tables[i % copies])
         b.record()
+        prep.combine()
+        c.record()
     torch.cuda.synchronize()
-    per_step = sorted(a.elapsed_time(b) for a, b in evs)
+    split_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    comb_ms = [b.elapsed_time(c) for _, b, c in ev]
+    kpass_ms = ev[0][0].elapsed_time(ev[-1][2]) / len(ev)
+    split_avg = sum(split_ms) / len(split_ms)
+    comb_avg = sum(comb_ms) / len(comb_ms)
+    split_bytes = ab["total"] - ab["out"] - ab["lse"]
+    split_gbs = split_bytes / (split_avg * 1e-3) / 1e9
+    per_step = sorted(a.elapsed_time(c) for a, _, c in ev)
     med_ms = per_step[len(per_step) // 2]
+    traffic = measured_traffic(cfg.name)
 
     gbs = ab["total"] / (ms * 1e-3) / 1e9
     res = {
@@ -197,8 +242,13 @@ def main() -> int:
         "kv_tokens_per_s": round(ab["kv_tokens"] / (ms * 1e-3), 1),
         "median_step_ms": round(med_ms, 5),
         "algorithmic_bytes_per_step": ab["total"],
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "kernels": {"split_avg_us": round(split_avg * 1e3, 3),
+                    "combine_avg_us": round(comb_avg * 1e3, 3),
+                    "split_algorithmic_bytes": split_bytes,
+                    "ms_per_step_two_phase": round(kpass_ms, 5)},
+        "roofline": {"bound": "hbm", "kernel": "mlra_split_mfma", "achieved": round(split_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp)

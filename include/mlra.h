@@ -168,6 +168,45 @@ mlra_status mla_decode_attention(const void* q_latent, const void* q_rope,
                                  const mlra_decode_dims* dims, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * The two halves of mlra_decode_attention, for callers that schedule or time
+ * them separately, or that merge partial results of one sequence computed
+ * elsewhere (e.g. a context range held by another device) before combining.
+ * Split-K with a log-sum-exp merge is exact: every split's softmax is
+ * normalised on its own and re-weighted by exp(lse_split - lse_total).
+ *
+ * mlra_decode_partials runs the split kernel only. It takes the arguments of
+ * mlra_decode_attention that the scores need and leaves, in the workspace,
+ * with P = plan.splits_per_seq, T = plan.tiles_per_split, R = Q*H and
+ * row r = j*H + h (plan from mlra_decode_make_plan with the same dims on the
+ * same device):
+ *   part_o   float32 [S][P][n_branch][R][DC] at byte offset 0:
+ *            split k's softmax-weighted latent output over its tokens
+ *            (already divided by its own sum of weights; 0 if it saw none);
+ *   part_lse float32 [S][P][n_branch][R] at byte offset
+ *            round_up(S*P*n_branch*R*DC*4, 256): natural log of the split's
+ *            sum of exp(scaled score), -inf if it saw no visible token.
+ * Split k of sequence s covers tokens [64*T*k, min(64*T*(k+1), L)); only the
+ * splits k < ceil(ceil(L/64) / T) are written, the rest of the slots keep
+ * whatever they held.
+ *
+ * mlra_decode_combine runs the combine kernel only: it merges the splits of
+ * each (sequence, row, branch), applies the branch reduction and out_rescale,
+ * and writes out and lse exactly as mlra_decode_attention does. It must get
+ * the dims, n_branch and seq_lens of the partials call it follows, on the
+ * same device and the same stream (or after it). Errors as for
+ * mlra_decode_attention, checking only the pointers each half uses.
+ */
+mlra_status mlra_decode_partials(const void* q_latent, const void* q_rope,
+                                 const void* latent_cache, const void* rope_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 int32_t n_branch, float scale, const mlra_decode_dims* dims,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+mlra_status mlra_decode_combine(const int32_t* seq_lens, int32_t n_branch, float out_rescale,
+                                void* out, float* lse, const mlra_decode_dims* dims,
+                                const void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* mlra_status_string(mlra_status status);
 

@@ -12,6 +12,10 @@ include/mlra.h:
   seq_lens      [S]                    int32, on the device
 Returns (out, lse): out [S][Q][H][DC] for reduce="sum", [S][Q][H][NB][DC] for
 "concat"; lse [S][Q][H][NB] float32.
+
+Calls that do not pass a workspace share one per device; such calls must not
+run concurrently on different streams. PreparedDecode validates and marshals
+once, for loops that repeat the same call.
 """
 from __future__ import annotations
 
@@ -32,8 +36,8 @@ def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     key = (device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        # zero-filled once: the library keeps its counter words at zero
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        # the library needs no initialised contents
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -98,32 +102,48 @@ def _call(entry: str, q_latent, q_rope, latent_cache, rope_cache, block_table, s
                      num_splits=num_splits, sum_seq_lens=sum_seq_lens)
     S, Q, H, NB, DC = q_latent.shape
     oshape = (S, Q, H, DC) if reduce == "sum" else (S, Q, H, NB, DC)
-    if out is None:
+    if entry == "partials":
+        pass
+    elif out is None:
         out = torch.empty(oshape, dtype=q_latent.dtype, device=dev)
-    if lse is None:
-        lse = torch.empty((S, Q, H, NB), dtype=torch.float32, device=dev)
-    if tuple(out.shape) != oshape or out.dtype != q_latent.dtype or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous {q_latent.dtype} tensor of shape {oshape}")
-    if tuple(lse.shape) != (S, Q, H, NB) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [S][Q][H][NB]")
-    need = make_plan(dims, NB).workspace_bytes
+    if entry != "partials":
+        if lse is None:
+            lse = torch.empty((S, Q, H, NB), dtype=torch.float32, device=dev)
+        if tuple(out.shape) != oshape or out.dtype != q_latent.dtype or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous {q_latent.dtype} tensor of shape {oshape}")
+        if (tuple(lse.shape) != (S, Q, H, NB) or lse.dtype != torch.float32
+                or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 tensor [S][Q][H][NB]")
     if workspace is None:
-        workspace = _workspace(dev, need)
+        if entry == "combine":
+            raise ValueError("mlra_decode_combine needs the workspace of its partials call")
+        workspace = _workspace(dev, make_plan(dims, NB).workspace_bytes)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    if entry == "mla":
+    wsb = workspace.numel() * workspace.element_size()
+    if entry == "partials":
+        status = lib.mlra_decode_partials(
+            q_latent.data_ptr(), q_rope.data_ptr(), latent_cache.data_ptr(),
+            rope_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), int(n_branch),
+            float(scale), dims, workspace.data_ptr(), wsb, stream)
+        _lib.check(status, "mlra_decode_partials")
+        return workspace
+    if entry == "combine":
+        status = lib.mlra_decode_combine(
+            seq_lens.data_ptr(), int(n_branch), float(out_rescale), out.data_ptr(),
+            lse.data_ptr(), dims, workspace.data_ptr(), wsb, stream)
+    elif entry == "mla":
         status = lib.mla_decode_attention(
             q_latent.data_ptr(), q_rope.data_ptr(), latent_cache.data_ptr(),
             rope_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), float(scale),
-            out.data_ptr(), lse.data_ptr(), dims, workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), stream)
+            out.data_ptr(), lse.data_ptr(), dims, workspace.data_ptr(), wsb, stream)
     else:
         status = lib.mlra_decode_attention(
             q_latent.data_ptr(), q_rope.data_ptr(), latent_cache.data_ptr(),
             rope_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), int(n_branch),
             float(scale), float(out_rescale), out.data_ptr(), lse.data_ptr(), dims,
-            workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
-    _lib.check(status, f"{entry}_decode_attention")
+            workspace.data_ptr(), wsb, stream)
+    _lib.check(status, "mlra_decode_combine" if entry == "combine" else f"{entry}_decode_attention")
     return out, lse
 
 
@@ -167,3 +187,116 @@ def mla_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
                      1, scale, 1.0, max_seq_len, "sum", causal, num_splits, sum_seq_lens, out,
                      lse, workspace, stream)
     return out, lse[..., 0]
+
+
+def mlra_decode_partials(q_latent: torch.Tensor, q_rope: torch.Tensor,
+                         latent_cache: torch.Tensor, rope_cache: torch.Tensor,
+                         block_table: torch.Tensor, seq_lens: torch.Tensor, n_branch: int,
+                         scale: float, *, max_seq_len: int, reduce: str = "sum",
+                         causal: bool = True, num_splits: int = 0, sum_seq_lens: int = 0,
+                         workspace: Optional[torch.Tensor] = None,
+                         stream: Optional[int] = None) -> torch.Tensor:
+    """First half of mlra_decode_attention: per-split partial results into the
+    workspace (layout in include/mlra.h). Returns the workspace tensor."""
+    if q_latent.dim() != 5 or q_latent.shape[3] != n_branch:
+        raise ValueError("q_latent must be [S][Q][H][n_branch][DC]")
+    return _call("partials", q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
+                 n_branch, scale, 1.0, max_seq_len, reduce, causal, num_splits, sum_seq_lens,
+                 None, None, workspace, stream)
+
+
+def mlra_decode_combine(q_latent: torch.Tensor, q_rope: torch.Tensor,
+                        latent_cache: torch.Tensor, rope_cache: torch.Tensor,
+                        block_table: torch.Tensor, seq_lens: torch.Tensor, n_branch: int,
+                        out_rescale: float, *, workspace: torch.Tensor, max_seq_len: int,
+                        reduce: str = "sum", causal: bool = True, num_splits: int = 0,
+                        sum_seq_lens: int = 0, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None,
+                        stream: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Second half of mlra_decode_attention. The tensors other than seq_lens
+    only give the shapes (the same as the partials call); their data is not
+    read."""
+    if q_latent.dim() != 5 or q_latent.shape[3] != n_branch:
+        raise ValueError("q_latent must be [S][Q][H][n_branch][DC]")
+    return _call("combine", q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
+                 n_branch, 1.0, out_rescale, max_seq_len, reduce, causal, num_splits,
+                 sum_seq_lens, out, lse, workspace, stream)
+
+
+class PreparedDecode:
+    """One decode call with its arguments validated and marshalled once.
+
+    run() / partials() / combine() enqueue the same call again on the stream
+    captured at construction (the current stream by default; run() also takes
+    another stream handle, e.g. a capturing one); a different
+    block table of the same shape (e.g. another copy of the cache) may be
+    passed per call. Tensors must stay alive and keep their storage.
+    """
+
+    def __init__(self, q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
+                 n_branch: int, scale: float, out_rescale: float, *, max_seq_len: int,
+                 reduce: str = "sum", causal: bool = True, num_splits: int = 0,
+                 sum_seq_lens: int = 0, out=None, lse=None, workspace=None, stream=None):
+        if q_latent.dim() != 5 or q_latent.shape[3] != n_branch:
+            raise ValueError("q_latent must be [S][Q][H][n_branch][DC]")
+        # one validated functional-path setup; its checks and shapes are reused
+        self.dims = make_dims(q_latent, q_rope, latent_cache, rope_cache, block_table,
+                              max_seq_len=max_seq_len, reduce=reduce, causal=causal,
+                              num_splits=num_splits, sum_seq_lens=sum_seq_lens)
+        self.plan = make_plan(self.dims, n_branch)
+        dev = q_latent.device
+        S, Q, H, NB, DC = q_latent.shape
+        oshape = (S, Q, H, DC) if reduce == "sum" else (S, Q, H, NB, DC)
+        self.out = out if out is not None else torch.empty(oshape, dtype=q_latent.dtype,
+                                                           device=dev)
+        self.lse = lse if lse is not None else torch.empty((S, Q, H, NB), dtype=torch.float32,
+                                                           device=dev)
+        self.workspace = workspace if workspace is not None else torch.empty(
+            max(self.plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        # run the functional path once: validates every tensor and pointer rule
+        _call("mlra", q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
+              n_branch, scale, out_rescale, max_seq_len, reduce, causal, num_splits,
+              sum_seq_lens, self.out, self.lse, self.workspace, self.stream)
+        self._table_shape = tuple(block_table.shape)
+        self._table_dev = block_table.device
+        self._lib = _lib.load()
+        self._ptrs = (q_latent.data_ptr(), q_rope.data_ptr(), latent_cache.data_ptr(),
+                      rope_cache.data_ptr())
+        self._table = block_table.data_ptr()
+        self._lens = seq_lens.data_ptr()
+        self._nb, self._scale, self._rescale = int(n_branch), float(scale), float(out_rescale)
+        self._wsb = self.workspace.numel() * self.workspace.element_size()
+
+    def _table_ptr(self, block_table):
+        if block_table is None:
+            return self._table
+        if (tuple(block_table.shape) != self._table_shape or block_table.dtype != torch.int32
+                or block_table.device != self._table_dev or not block_table.is_contiguous()):
+            raise ValueError("block_table must match the prepared table's shape and device")
+        return block_table.data_ptr()
+
+    def run(self, block_table=None, stream=None):
+        """Both kernels (mlra_decode_attention); returns (out, lse)."""
+        q, qr, lc, rc = self._ptrs
+        _lib.check(self._lib.mlra_decode_attention(
+            q, qr, lc, rc, self._table_ptr(block_table), self._lens, self._nb, self._scale,
+            self._rescale, self.out.data_ptr(), self.lse.data_ptr(), self.dims,
+            self.workspace.data_ptr(), self._wsb, self.stream if stream is None else stream),
+            "mlra_decode_attention")
+        return self.out, self.lse
+
+    def partials(self, block_table=None):
+        """The split kernel only (mlra_decode_partials)."""
+        q, qr, lc, rc = self._ptrs
+        _lib.check(self._lib.mlra_decode_partials(
+            q, qr, lc, rc, self._table_ptr(block_table), self._lens, self._nb, self._scale,
+            self.dims, self.workspace.data_ptr(), self._wsb, self.stream),
+            "mlra_decode_partials")
+
+    def combine(self):
+        """The combine kernel only (mlra_decode_combine); returns (out, lse)."""
+        _lib.check(self._lib.mlra_decode_combine(
+            self._lens, self._nb, self._rescale, self.out.data_ptr(), self.lse.data_ptr(),
+            self.dims, self.workspace.data_ptr(), self._wsb, self.stream), "mlra_decode_combine")
+        return self.out, self.lse

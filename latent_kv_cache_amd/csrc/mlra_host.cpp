@@ -146,7 +146,7 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
   p.tiles_per_split = (int32_t)tps;
   p.splits_per_seq = (int32_t)spl;
   p.lds_bytes = k.variant == kVariantMfmaBf16
-                    ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, r.DR, k.NT, k.WT)
+                    ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, r.DR, k.NT, k.WT, mfma_qreg(k.NT, r.DC))
                     : 0;
   // Partials: output [S][spl][NB][rows][DC] and lse [S][spl][NB][rows], fp32.
   const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;

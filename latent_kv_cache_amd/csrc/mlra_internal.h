@@ -19,6 +19,11 @@ constexpr int kSub = 32;        // tokens per MFMA sub-tile (M of the 32x32 MFMA
 // workgroup's tiles (WT).
 constexpr int mfma_wd(int DC) { return DC == 512 ? 4 : 1; }
 constexpr int mfma_waves_per_simd(int NT, int DC) { return (NT == 1 && DC != 512) ? 2 : 1; }
+// 32-token sub-tiles each wave keeps in flight in registers (48 VGPRs each at
+// DC = 128, DR = 64); a wave requests PD sub-tiles ahead of the one it computes.
+constexpr int mfma_pd(int /*NT*/, int /*DC*/) { return 1; }
+// Query rows in each wave's registers (true) or staged once per workgroup in LDS.
+constexpr bool mfma_qreg(int NT, int /*DC*/) { return NT == 1; }
 constexpr int mfma_wt(int NB, int DC, int NT) {
   return 4 * mfma_waves_per_simd(NT, DC) / (NB * mfma_wd(DC)) > 0
              ? 4 * mfma_waves_per_simd(NT, DC) / (NB * mfma_wd(DC))
@@ -56,16 +61,16 @@ struct KernelShape {
 // LDS bytes of one MFMA split workgroup:
 //   latent sub-tile stage   one per wave           [32][lpitch] chunks
 //   RoPE sub-tile stage     one per (wt, branch)   [32][rpitch]
-//   latent query rows       one per (branch, wd)   [NT*32][lpitch]
-//   RoPE query rows         one                    [NT*32][rpitch]
+//   latent query rows       one per (branch, wd)   [NT*32][lpitch]  (unless in registers)
+//   RoPE query rows         one                    [NT*32][rpitch]  (unless in registers)
 //   score exchange (WD > 1) [NB*WT][WD][NT][64 lanes][16 floats]
 // and, aliased over all of it after the token loop, the cross-wave merge
 // records when WT > 1: [WT][NB*WD][NT*NDT*4 + 1][64 lanes] float4.
-inline int32_t mfma_lds_bytes(int NB, int DCW, int WD, int DR, int NT, int WT) {
+inline int32_t mfma_lds_bytes(int NB, int DCW, int WD, int DR, int NT, int WT, bool qreg) {
   const int waves = NB * WD * WT;
   const int lp = mfma_lpitch(DCW), rp = mfma_rpitch(DR);
   const int stage = waves * 32 * lp * 16 + NB * WT * 32 * rp * 16;
-  const int qry = (NB * WD * lp + rp) * NT * 32 * 16;
+  const int qry = qreg ? 0 : (NB * WD * lp + rp) * NT * 32 * 16;
   const int xchg = (WD > 1) ? NB * WT * WD * NT * 64 * 16 * 4 : 0;
   const int ndt = DCW / 32;
   const int merge = (WT > 1) ? WT * NB * WD * 64 * (NT * ndt * 16 + 4) * 4 : 0;

@@ -120,7 +120,7 @@ __device__ __forceinline__ i16x4 lds_read_tr(const unsigned char* p) {
 // rows x 32 bytes, both land on distinct banks. RoPE rows (read row-wise
 // only) get 1 spare chunk, an odd pitch.
 
-template <int NB, int DCW, int WD, int DR, int NT, int WT, int WPS>
+template <int NB, int DCW, int WD, int DR, int NT, int WT, int WPS, int PD, bool QREG>
 __global__ void __launch_bounds__(64 * NB * WD * WT)
 __attribute__((amdgpu_waves_per_eu(WPS)))
 mlra_split_mfma(SplitParams p) {
@@ -132,7 +132,10 @@ mlra_split_mfma(SplitParams p) {
   constexpr int RCH = DR / 8;    // 16-byte chunks per staged RoPE row
   constexpr int LQ = kSub * LCH / 64;  // coalesced 16-byte loads per lane per sub-tile
   constexpr int RQ = kSub * RCH / 64;
-  constexpr int PD = 1;          // sub-tiles in flight per wave
+  // QREG: query rows (the B operand of S^T) live in each wave's registers
+  // (no workgroup barrier before the first MFMA); otherwise they are staged
+  // once per workgroup in LDS.
+  static_assert(!QREG || NT == 1, "register queries hold one row tile");
   constexpr int WAVES = NB * WD * WT;
   constexpr int LP = mfma_lpitch(DCW);  // staged row pitch, 16-byte chunks
   constexpr int RP = mfma_rpitch(DR);
@@ -174,9 +177,9 @@ mlra_split_mfma(SplitParams p) {
   // of the slice, or RoPE feature g*DR/2 + 8*st + e. Padding rows are zero.
   constexpr int QL_CH = NB * WD * NT * kSub * LCH;  // latent query chunks
   constexpr int Q_CH = QL_CH + NT * kSub * RCH;     // + RoPE query chunks
-  constexpr int QK = (Q_CH + WAVES * 64 - 1) / (WAVES * 64);
-  u32x4 qv[QK];
-  int qdst[QK];  // LDS byte offset in the query region, -1 = none
+  constexpr int QK = QREG ? 0 : (Q_CH + WAVES * 64 - 1) / (WAVES * 64);
+  u32x4 qv[QK > 0 ? QK : 1];
+  int qdst[QK > 0 ? QK : 1];  // LDS byte offset in the query region, -1 = none
 #pragma unroll
   for (int kq = 0; kq < QK; ++kq) {
     const int x = (kq * WAVES + wave) * 64 + lane;
@@ -208,6 +211,30 @@ mlra_split_mfma(SplitParams p) {
     const int row = nt * 32 + n;
     jrow[nt] = row < p.rows ? row / p.H : 0;
   }
+  // Register-resident queries: lane (n, g) holds row n's features of K-slot
+  // group g (same K-slot order as the staged layout). Loaded unconditionally
+  // from a clamped row, zeroed for padding rows.
+  constexpr int NLq = QREG ? NL : 1, NRq = QREG ? NR : 1;
+  bf16x8 qLr[NLq], qRr[NRq];
+  if constexpr (QREG) {
+    const int row = n;
+    const bool ok = row < p.rows;
+    const int rs = ok ? row : 0;
+    const int j = rs / p.H, h = rs % p.H;
+    const int64_t head = ((int64_t)s * p.Q + j) * p.H + h;
+    const __bf16* ql = qlat + (head * NB + b) * DC + wd * DCW + g * (DCW / 2);
+    const __bf16* qr = qrop + head * DR + g * (DR / 2);
+#pragma unroll
+    for (int st = 0; st < NL; ++st) {
+      const u32x4 v = ld16(ql + 8 * st);
+      qLr[st] = __builtin_bit_cast(bf16x8, ok ? v : u32x4{});
+    }
+#pragma unroll
+    for (int st = 0; st < NR; ++st) {
+      const u32x4 v = ld16(qr + 8 * st);
+      qRr[st] = __builtin_bit_cast(bf16x8, (ok && has_rope) ? v : u32x4{});
+    }
+  }
 
   const int L = L_raw < 0 ? 0 : (L_raw > p.lcap ? p.lcap : L_raw);
   const int ntiles = (L + kBlock - 1) / kBlock;
@@ -230,7 +257,7 @@ mlra_split_mfma(SplitParams p) {
   unsigned char* const q_base = rope_base + NB * WT * kSub * RP * 16;
   unsigned char* q_l = q_base + (b * WD + wd) * NT * kSub * LP * 16;
   unsigned char* q_r = q_base + NB * WD * NT * kSub * LP * 16;
-  float* xchg = reinterpret_cast<float*>(q_r + NT * kSub * RP * 16);
+  float* xchg = reinterpret_cast<float*>(QREG ? q_base : q_r + NT * kSub * RP * 16);
   f32x16 acc[NT][NDT];
   float m_run[NT], l_run[NT];
 #pragma unroll
@@ -325,32 +352,55 @@ mlra_split_mfma(SplitParams p) {
     const bool valid = (u < nu) && ti < t1;
     const int tb = ti * kBlock + (u & 1) * kSub;
 
-    // S^T[token][row] = C . Q^T with A read row-wise from the staged tile
+    // Operands of this sub-tile, all read from LDS before the first MFMA so
+    // that their latency overlaps: A of S^T (row-wise), and the C^T operands
+    // of P.C (transpose reads; K-slot e of lane group g in half h2 is token
+    // 16*h2 + 8*(e/4) + 4*g + e%4).
+    bf16x8 aR[NR], aL[NL], aT[2][NDT];
+    if (has_rope) {
+#pragma unroll
+      for (int st = 0; st < NR; ++st)
+        aR[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ar_base + st * 16));
+    }
+#pragma unroll
+    for (int st = 0; st < NL; ++st)
+      aL[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(al_base + st * 16));
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
+        const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
+        aT[h2][dt] =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+
+    // S^T[token][row] = C . Q^T
     f32x16 sc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sc[nt] = f32x16{};
     if (has_rope) {
 #pragma unroll
       for (int st = 0; st < NR; ++st) {
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ar_base + st * 16));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const bf16x8 qv = __builtin_bit_cast(
+          bf16x8 qv;
+          if constexpr (QREG) qv = qRr[st];
+          else qv = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(qr_base + (nt * kSub * RP + st) * 16));
-          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv, sc[nt], 0, 0, 0);
+          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qv, sc[nt], 0, 0, 0);
         }
       }
     }
 #pragma unroll
     for (int st = 0; st < NL; ++st) {
-      const bf16x8 a =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(al_base + st * 16));
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const bf16x8 qv = __builtin_bit_cast(
+        bf16x8 qv;
+        if constexpr (QREG) qv = qLr[st];
+        else qv = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(ql_base + (nt * kSub * LP + st) * 16));
-        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv, sc[nt], 0, 0, 0);
+        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qv, sc[nt], 0, 0, 0);
       }
     }
 
@@ -424,32 +474,29 @@ mlra_split_mfma(SplitParams p) {
       l_run[nt] += sum;
     }
 
-    // O^T[d][row] += C^T[d][t] . P^T[t][row]. K-slot e of lane group g in half
-    // h2 is token 16*h2 + 8*(e/4) + 4*g + e%4, where P already sits; C^T comes
-    // from two LDS transpose reads of 4 tokens each.
+    // O^T[d][row] += C^T[d][t] . P^T[t][row]
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
-        const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[nt][h2], acc[nt][dt], 0, 0, 0);
-      }
+          acc[nt][dt] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(aT[h2][dt], pB[nt][h2], acc[nt][dt], 0, 0, 0);
   };
 
-  // Software pipeline: PD sub-tiles in flight in registers; the wave stages
-  // one into LDS, refills its registers with the sub-tile PD ahead, computes.
+  // Software pipeline: PD sub-tiles in flight in registers. The wave stages
+  // the oldest into LDS, refills those registers with the sub-tile PD ahead,
+  // then computes it. The first sub-tile is staged before the wave waits for
+  // the other waves' query rows (when those are staged in LDS).
   const int nsteps = (nu + PD - 1) / PD * PD;
 #pragma unroll
   for (int i = 0; i < PD; ++i) load_unit(i, bl[i], br[i]);
+  if constexpr (!QREG) {
 #pragma unroll
-  for (int kq = 0; kq < QK; ++kq)
-    if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(q_base + qdst[kq]) = qv[kq];
-  lds_barrier();  // queries staged
+    for (int kq = 0; kq < QK; ++kq)
+      if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(q_base + qdst[kq]) = qv[kq];
+  }
   for (int u0 = 0; u0 < nsteps; u0 += PD) {
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
@@ -457,6 +504,9 @@ mlra_split_mfma(SplitParams p) {
       zero_tail(u, bl[i], br[i]);
       stage_unit(bl[i], br[i]);
       if (u + PD < nsteps) load_unit(u + PD, bl[i], br[i]);
+      if constexpr (!QREG) {
+        if (u == 0) lds_barrier();  // queries staged
+      }
       compute_unit(u);
     }
   }
@@ -536,17 +586,16 @@ mlra_split_mfma(SplitParams p) {
       const int64_t ri = (slot * NB + b) * p.rows + row;
       if (row < p.rows) {
         float* o = p.part_o + ri * DC + wd * DCW;
+        // float4 items (dt, q) of this row tile, spread over the WT waves
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          if (dt % WT != wt) continue;
+        for (int it = 0; it < NDT * 4; ++it) {
+          if (it % WT != wt) continue;
+          const int dt = it / 4, q = it % 4;
+          f32x4 v = f32x4{};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f32x4 v = f32x4{};
-#pragma unroll
-            for (int w = 0; w < WT; ++w)
-              v += M[((w * NB * WD + gi) * REC + (nt * NDT + dt) * 4 + q) * 64 + lane] * wsc[w];
-            *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
-          }
+          for (int w = 0; w < WT; ++w)
+            v += M[((w * NB * WD + gi) * REC + (nt * NDT + dt) * 4 + q) * 64 + lane] * wsc[w];
+          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
         }
         if (g == 0 && wd == 0 && wt == 0)
           p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
@@ -788,8 +837,10 @@ static hipError_t launch_mfma(const SplitParams& sp, const mlra_decode_plan& pla
   constexpr int DCW = DC / WD;
   constexpr int WT = mfma_wt(NB, DC, NT);
   constexpr int WPS = mfma_waves_per_simd(NT, DC);
-  auto kern = mlra_split_mfma<NB, DCW, WD, DR, NT, WT, WPS>;
-  const int lds = mfma_lds_bytes(NB, DCW, WD, DR, NT, WT);
+  constexpr int PD = mfma_pd(NT, DC);
+  constexpr bool QREG = mfma_qreg(NT, DC);
+  auto kern = mlra_split_mfma<NB, DCW, WD, DR, NT, WT, WPS, PD, QREG>;
+  const int lds = mfma_lds_bytes(NB, DCW, WD, DR, NT, WT, QREG);
   if (lds > 64 * 1024) {
     static bool attr_set = false;  // per instance; the call is idempotent
     if (!attr_set) {
@@ -878,23 +929,34 @@ static int device_cus(int* out) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-static mlra_status decode(const void* q_latent, const void* q_rope, const void* latent_cache,
-                          const void* rope_cache, const int32_t* block_table,
-                          const int32_t* seq_lens, int32_t n_branch, float scale,
-                          float out_rescale, void* out, float* lse, const mlra_decode_dims* dims,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+// Which kernels one call enqueues: the split kernel (partial results of
+// every split into the workspace), the combine kernel, or both.
+enum Phase { kPartials = 1, kCombine = 2, kBoth = 3 };
+
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+static mlra_status decode(int phases, const void* q_latent, const void* q_rope,
+                          const void* latent_cache, const void* rope_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, int32_t n_branch,
+                          float scale, float out_rescale, void* out, float* lse,
+                          const mlra_decode_dims* dims, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   Resolved r;
   mlra_status st = resolve_dims(dims, n_branch, &r);
   if (st != MLRA_OK) return st;
-  if (!q_latent || !q_rope || !latent_cache || !rope_cache || !block_table || !seq_lens ||
-      !out || !lse)
+  const bool do_split = phases & kPartials, do_combine = phases & kCombine;
+  if (!seq_lens || (do_split && (!q_latent || !q_rope || !latent_cache || !rope_cache ||
+                                 !block_table)) ||
+      (do_combine && (!out || !lse)))
     return MLRA_ERR_NULL_PTR;
-  if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(out_rescale))
+  if (!workspace) return MLRA_ERR_WORKSPACE;
+  if ((do_split && (!std::isfinite(scale) || !(scale > 0.f))) ||
+      (do_combine && !std::isfinite(out_rescale)))
     return MLRA_ERR_BAD_DIMS;
-  if (!aligned16(q_latent) || !aligned16(q_rope) || !aligned16(latent_cache) ||
-      !aligned16(rope_cache) || !aligned16(out) || !aligned16(workspace) ||
-      (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(block_table) & 3) ||
-      (reinterpret_cast<uintptr_t>(seq_lens) & 3))
+  if (!aligned4(seq_lens) || !aligned16(workspace) ||
+      (do_split && (!aligned16(q_latent) || !aligned16(q_rope) || !aligned16(latent_cache) ||
+                    !aligned16(rope_cache) || !aligned4(block_table))) ||
+      (do_combine && (!aligned16(out) || !aligned4(lse))))
     return MLRA_ERR_ALIGNMENT;
   const KernelShape ks = choose_shape(r);
   int cus = 0;
@@ -937,7 +999,8 @@ static mlra_status decode(const void* q_latent, const void* q_rope, const void* 
   sp.causal = r.causal;
   sp.score_scale = scale * kLog2e;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (launch_split(sp, ks, plan, hs) != hipSuccess) return MLRA_ERR_HIP;
+  if (do_split && launch_split(sp, ks, plan, hs) != hipSuccess) return MLRA_ERR_HIP;
+  if (!do_combine) return MLRA_OK;
 
   CombineParams cp;
   cp.part_o = part_o;
@@ -999,9 +1062,9 @@ extern "C" mlra_status mlra_decode_attention(const void* q_latent, const void* q
                                              void* out, float* lse, const mlra_decode_dims* dims,
                                              void* workspace, size_t workspace_bytes,
                                              void* stream) {
-  return mlra::decode(q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
-                      n_branch, scale, out_rescale, out, lse, dims, workspace, workspace_bytes,
-                      stream);
+  return mlra::decode(mlra::kBoth, q_latent, q_rope, latent_cache, rope_cache, block_table,
+                      seq_lens, n_branch, scale, out_rescale, out, lse, dims, workspace,
+                      workspace_bytes, stream);
 }
 
 extern "C" mlra_status mla_decode_attention(const void* q_latent, const void* q_rope,
@@ -1010,6 +1073,27 @@ extern "C" mlra_status mla_decode_attention(const void* q_latent, const void* q_
                                             float scale, void* out, float* lse,
                                             const mlra_decode_dims* dims, void* workspace,
                                             size_t workspace_bytes, void* stream) {
-  return mlra::decode(q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens, 1,
-                      scale, 1.0f, out, lse, dims, workspace, workspace_bytes, stream);
+  return mlra::decode(mlra::kBoth, q_latent, q_rope, latent_cache, rope_cache, block_table,
+                      seq_lens, 1, scale, 1.0f, out, lse, dims, workspace, workspace_bytes,
+                      stream);
+}
+
+extern "C" mlra_status mlra_decode_partials(const void* q_latent, const void* q_rope,
+                                            const void* latent_cache, const void* rope_cache,
+                                            const int32_t* block_table, const int32_t* seq_lens,
+                                            int32_t n_branch, float scale,
+                                            const mlra_decode_dims* dims, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  return mlra::decode(mlra::kPartials, q_latent, q_rope, latent_cache, rope_cache, block_table,
+                      seq_lens, n_branch, scale, 1.0f, nullptr, nullptr, dims, workspace,
+                      workspace_bytes, stream);
+}
+
+extern "C" mlra_status mlra_decode_combine(const int32_t* seq_lens, int32_t n_branch,
+                                           float out_rescale, void* out, float* lse,
+                                           const mlra_decode_dims* dims, const void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  return mlra::decode(mlra::kCombine, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens,
+                      n_branch, 1.0f, out_rescale, out, lse, dims, const_cast<void*>(workspace),
+                      workspace_bytes, stream);
 }

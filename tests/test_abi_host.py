@@ -146,3 +146,33 @@ def test_pointer_and_alignment_errors_before_any_device_call(lib):
     assert lib.mlra_decode_attention(*a) == 3
     assert lib.mla_decode_attention(None, ok, ok, ok, ok, ok, 0.1, ok, ok, ctypes.byref(d), ok,
                                     1 << 30, None) == 1
+
+
+def test_two_phase_entry_points_check_only_their_own_pointers(lib):
+    d = _dims(configs.MLRA4_TP_SHARE)
+    ok = ctypes.c_void_p(4096)
+    part = [ok] * 6 + [1, 0.1, ctypes.byref(d), ok, 1 << 30, None]
+    for i in range(6):
+        a = list(part)
+        a[i] = None
+        assert lib.mlra_decode_partials(*a) == 1, i
+    a = list(part)
+    a[7] = -1.0
+    assert lib.mlra_decode_partials(*a) == 2
+    a = list(part)
+    a[4] = ctypes.c_void_p(4098)          # block table must be 4-byte aligned
+    assert lib.mlra_decode_partials(*a) == 5
+    a = list(part)
+    a[9] = None                           # workspace
+    assert lib.mlra_decode_partials(*a) == 4
+    comb = [ok, 1, 0.5, ok, ok, ctypes.byref(d), ok, 1 << 30, None]
+    for i in (0, 3, 4):
+        a = list(comb)
+        a[i] = None
+        assert lib.mlra_decode_combine(*a) == 1, i
+    a = list(comb)
+    a[2] = math.nan
+    assert lib.mlra_decode_combine(*a) == 2
+    a = list(comb)
+    a[3] = ctypes.c_void_p(4096 + 4)      # out must be 16-byte aligned
+    assert lib.mlra_decode_combine(*a) == 5

@@ -213,3 +213,28 @@ def test_seq_len_above_max_is_clamped_not_read_out_of_bounds():
     torch.cuda.synchronize()
     ro, rl = oracle(inp)
     assert_parity(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy(), ro, rl)
+
+
+def test_two_phase_and_prepared_calls_match_the_single_call_bitwise():
+    cfg = _cfg(num_seqs=3, context_range=(100, 3000), seed=31)
+    inp = make_inputs(cfg)
+    d = to_device(inp)
+    args = (d["q_latent"], d["q_rope"], d["latent_cache"], d["rope_cache"], d["block_table"],
+            d["seq_lens"], cfg.n_branch)
+    kw = dict(max_seq_len=inp.max_seq_len, sum_seq_lens=int(inp.seq_lens.sum()))
+    _say("single call vs partials+combine vs prepared")
+    o1, l1 = api.mlra_decode_attention(*args, cfg.scale, cfg.out_rescale, **kw)
+    o1, l1 = o1.clone(), l1.clone()
+    ws = api.mlra_decode_partials(*args, cfg.scale, **kw)
+    o2, l2 = api.mlra_decode_combine(*args, cfg.out_rescale, workspace=ws, **kw)
+    prep = api.PreparedDecode(*args, cfg.scale, cfg.out_rescale, **kw)
+    prep.out.zero_()
+    prep.partials()
+    o3, l3 = (t.clone() for t in prep.combine())
+    prep.out.zero_()
+    o4, l4 = prep.run(d["block_table"].clone())
+    torch.cuda.synchronize()
+    for o, l in ((o2, l2), (o3, l3), (o4, l4)):
+        assert torch.equal(o, o1) and torch.equal(l, l1)
+    assert_parity(o1.float().cpu().numpy().astype(np.float64),
+                  l1.cpu().numpy().astype(np.float64), *oracle(inp))
