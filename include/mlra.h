@@ -97,7 +97,7 @@ typedef struct mlra_decode_dims {
 
 /* Split-K plan, computed on the host from dims alone (no device read). On
  * the device each sequence uses ceil(ceil(L/64) / tiles_per_split) of its
- * splits_per_seq workgroups; the rest exit at once. */
+ * splits_per_seq splits (row_groups workgroups each); the rest exit at once. */
 typedef struct mlra_decode_plan {
   int32_t num_cus;             /* compute units the plan targets */
   int32_t target_groups;       /* split-kernel workgroups the planner aims for */
@@ -106,7 +106,7 @@ typedef struct mlra_decode_plan {
   int32_t splits_per_seq;      /* splits of the longest sequence; grid = S x this */
   int32_t kernel_variant;      /* internal kernel id (for logs and tests) */
   int32_t lds_bytes;           /* LDS one split workgroup allocates */
-  int32_t reserved;
+  int32_t row_groups;          /* split-kernel workgroups per split (one per 32 query rows) */
   size_t workspace_bytes;      /* bytes of device workspace the call needs */
 } mlra_decode_plan;
 

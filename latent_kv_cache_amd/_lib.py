@@ -45,7 +45,7 @@ class DecodePlan(ctypes.Structure):
         ("num_cus", ctypes.c_int32), ("target_groups", ctypes.c_int32),
         ("waves_per_group", ctypes.c_int32), ("tiles_per_split", ctypes.c_int32),
         ("splits_per_seq", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
-        ("lds_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_int32), ("row_groups", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

@@ -86,11 +86,14 @@ mlra_status resolve_dims(const mlra_decode_dims* d, int32_t n_branch, Resolved* 
   return MLRA_OK;
 }
 
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 KernelShape choose_shape(const Resolved& r) {
   KernelShape k{};
   if (r.dtype == MLRA_FP32) {
     k.variant = kVariantValuFp32;
     k.NT = 1;
+    k.NRT = 1;
     k.WD = 1;
     k.WT = 1;
     k.NPF = 1;
@@ -99,7 +102,11 @@ KernelShape choose_shape(const Resolved& r) {
     return k;
   }
   k.variant = kVariantMfmaBf16;
-  k.NT = r.rows > 32 ? 2 : 1;
+  // A wave holds 32 query rows; 64 rows run as two workgroups per split
+  // (register pressure of two row tiles in one wave costs more than reading
+  // each cache tile twice from L2).
+  k.NT = 1;
+  k.NRT = r.rows > 32 ? 2 : 1;
   k.WD = mfma_wd(r.DC);
   k.WT = mfma_wt(r.NB, r.DC, k.NT);
   k.NPF = 2;  // sub-tiles in flight per wave (register prefetch)
@@ -108,7 +115,40 @@ KernelShape choose_shape(const Resolved& r) {
   return k;
 }
 
-static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// Tiles per split that minimise the estimated makespan of the split kernel:
+// rounds * (tiles per split + a fixed per-workgroup cost), where a round is
+// one workgroup on each of the target_groups slots. The fixed cost counts
+// the prologue and merge (about two tiles of streaming) plus writing and
+// re-reading the workgroup's fp32 partial results, in tile-sized units. Sequence lengths live on
+// the device, so the number of non-empty workgroups is estimated from the
+// host-side hints: exact when every sequence has max_seq_len (sum_seq_lens =
+// S * max_seq_len, or no hint), otherwise the batch's tiles / tps plus half a
+// workgroup of rounding per sequence. Ties go to the larger split (fewer
+// partial results to combine).
+static int64_t choose_tiles_per_split(const Resolved& r, const KernelShape& k,
+                                      int64_t slots, int64_t max_tiles, int64_t sum_seq_lens) {
+  const int64_t elem = r.dtype == MLRA_BF16 ? 2 : 4;
+  const double tile_bytes = (double)kBlock * (r.NB * r.DC + r.DR) * elem;
+  const double partial_bytes = (double)r.NB * (r.rows / k.NRT) * (r.DC + 1) * 4;
+  const double fixed = 2.0 + 2.0 * partial_bytes / tile_bytes;
+  const bool uniform = sum_seq_lens <= 0 || sum_seq_lens >= (int64_t)r.S * r.lcap;
+  const int64_t total = uniform ? (int64_t)r.S * max_tiles : cdiv(sum_seq_lens, kBlock);
+  const int64_t top = std::max<int64_t>(cdiv(std::max<int64_t>(max_tiles, 1), k.WT) * k.WT, k.WT);
+  int64_t best = top;
+  double best_cost = -1.0;
+  for (int64_t tps = top; tps >= k.WT; tps -= k.WT) {
+    const int64_t groups = k.NRT * (uniform ? (int64_t)r.S * cdiv(max_tiles, tps)
+                                            : cdiv(total, tps) + cdiv(r.S, 2));
+    const double cost =
+        (double)cdiv(std::max<int64_t>(groups, 1), slots) * ((double)tps + fixed);
+    if (best_cost < 0 || cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = tps;
+    }
+    if (groups > 64 * slots) break;  // finer splits only add rounds
+  }
+  return best;
+}
 
 mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
                       int32_t num_splits, int64_t sum_seq_lens, mlra_decode_plan* plan) {
@@ -132,19 +172,17 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
   }
   if (num_splits > 0) {
     tps = cdiv(std::max<int64_t>(max_tiles, 1), num_splits);
+    tps = std::max<int64_t>(tps, k.WT);
+    tps = cdiv(tps, k.WT) * k.WT;  // every token-split wave gets the same tile count
   } else {
-    // Expected tiles in the batch: exact for full blocks when the caller gave
-    // sum(seq_lens); otherwise as if every sequence had max_seq_len.
-    const int64_t total =
-        sum_seq_lens > 0 ? cdiv(sum_seq_lens, kBlock) : (int64_t)r.S * max_tiles;
-    tps = cdiv(std::max<int64_t>(total, 1), p.target_groups);
+    tps = choose_tiles_per_split(r, k, p.target_groups, max_tiles, sum_seq_lens);
   }
-  tps = std::max<int64_t>(tps, k.WT);
-  tps = cdiv(tps, k.WT) * k.WT;  // every token-split wave gets the same tile count
   const int64_t spl = std::max<int64_t>(1, cdiv(max_tiles, tps));
-  if (spl > 65535 || tps > (1 << 24)) return MLRA_ERR_UNSUPPORTED;
+  if (spl > 65535 || tps > (1 << 24) || (int64_t)r.S * spl * k.NRT > (1 << 28))
+    return MLRA_ERR_UNSUPPORTED;
   p.tiles_per_split = (int32_t)tps;
   p.splits_per_seq = (int32_t)spl;
+  p.row_groups = k.NRT;
   p.lds_bytes = k.variant == kVariantMfmaBf16
                     ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, r.DR, k.NT, k.WT, mfma_qreg(k.NT, r.DC))
                     : 0;

@@ -21,7 +21,8 @@ constexpr int mfma_wd(int DC) { return DC == 512 ? 4 : 1; }
 constexpr int mfma_waves_per_simd(int NT, int DC) { return (NT == 1 && DC != 512) ? 2 : 1; }
 // 32-token sub-tiles each wave keeps in flight in registers (48 VGPRs each at
 // DC = 128, DR = 64); a wave requests PD sub-tiles ahead of the one it computes.
-constexpr int mfma_pd(int /*NT*/, int /*DC*/) { return 1; }
+// With two row tiles a CU runs only 4 waves, so each requests two ahead.
+constexpr int mfma_pd(int NT, int DC) { return (NT == 2 && DC != 512) ? 2 : 1; }
 // Query rows in each wave's registers (true) or staged once per workgroup in LDS.
 constexpr bool mfma_qreg(int NT, int /*DC*/) { return NT == 1; }
 constexpr int mfma_wt(int NB, int DC, int NT) {
@@ -50,7 +51,8 @@ struct Resolved {
 // Shape of the split-kernel workgroup.
 struct KernelShape {
   int32_t variant;
-  int32_t NT;       // 32-row tiles of query rows (H*Q): 1 or 2
+  int32_t NT;       // 32-row tiles of query rows one wave holds (bf16: 1)
+  int32_t NRT;      // workgroups per split, one per 32 query rows (H*Q <= 64: 1 or 2)
   int32_t WD;       // waves that split the latent width of one branch (DC = 512 -> 4)
   int32_t WT;       // waves that split the workgroup's tokens (merged in LDS)
   int32_t NPF;      // sub-tiles in flight per wave (register prefetch depth)

@@ -54,6 +54,7 @@ struct SplitParams {
   float* part_lse;  // [S][spl][NB][rows]
   int64_t lsb, lst, lsbr, rsb, rst;
   int32_t S, Q, H, rows, NB, DC, DR, spl, tps, max_blocks, num_blocks, lcap, causal;
+  int32_t nrt;        // workgroups per split (one per 32 query rows)
   float score_scale;  // scale * log2(e): scores kept in base-2 units
 };
 
@@ -151,8 +152,24 @@ mlra_split_mfma(SplitParams p) {
   const int g = lane >> 5;
   const bool has_rope = WD == 1 || wd == 0;  // uniform per wave
 
-  const int k = blockIdx.x;
-  const int s = blockIdx.y;
+  // Workgroup -> (split k, sequence s, 32-row tile rt). With two row tiles,
+  // ids 16c + i and 16c + 8 + i (i < 8) are the two row tiles of split pair
+  // 8c + i: workgroups are dealt round-robin over the 8 XCDs, so both land on
+  // one XCD at about the same time and the second reads the tiles from L2.
+  int k, s, rt;
+  if (p.nrt == 1) {
+    k = blockIdx.x;
+    s = blockIdx.y;
+    rt = 0;
+  } else {
+    const int id = blockIdx.x;
+    const int pr = (id >> 4) * 8 + (id & 7);
+    if (pr >= p.S * p.spl) return;  // grid rounded up to 16
+    rt = (id >> 3) & 1;
+    s = pr / p.spl;
+    k = pr % p.spl;
+  }
+  const int row0 = rt * 32;  // first query row of this workgroup
   const int t0 = k * p.tps;
   const __bf16* __restrict__ qlat = static_cast<const __bf16*>(p.q_lat);
   const __bf16* __restrict__ qrop = static_cast<const __bf16*>(p.q_rope);
@@ -191,7 +208,7 @@ mlra_split_mfma(SplitParams p) {
     // RoPE chunk coordinates
     const int xr = is_rope ? x - QL_CH : 0;
     const int rr = xr / RCH, cr = xr % RCH;
-    const int r = is_lat ? rl : rr;
+    const int r = row0 + (is_lat ? rl : rr);
     const bool live = (is_lat || is_rope) && r < p.rows;
     const int rs = live ? r : 0;
     const int j = rs / p.H, h = rs % p.H;
@@ -208,7 +225,7 @@ mlra_split_mfma(SplitParams p) {
   int jrow[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int row = nt * 32 + n;
+    const int row = row0 + nt * 32 + n;
     jrow[nt] = row < p.rows ? row / p.H : 0;
   }
   // Register-resident queries: lane (n, g) holds row n's features of K-slot
@@ -217,7 +234,7 @@ mlra_split_mfma(SplitParams p) {
   constexpr int NLq = QREG ? NL : 1, NRq = QREG ? NR : 1;
   bf16x8 qLr[NLq], qRr[NRq];
   if constexpr (QREG) {
-    const int row = n;
+    const int row = row0 + n;
     const bool ok = row < p.rows;
     const int rs = ok ? row : 0;
     const int j = rs / p.H, h = rs % p.H;
@@ -352,10 +369,17 @@ mlra_split_mfma(SplitParams p) {
     const bool valid = (u < nu) && ti < t1;
     const int tb = ti * kBlock + (u & 1) * kSub;
 
-    // Operands of this sub-tile, all read from LDS before the first MFMA so
-    // that their latency overlaps: A of S^T (row-wise), and the C^T operands
-    // of P.C (transpose reads; K-slot e of lane group g in half h2 is token
-    // 16*h2 + 8*(e/4) + 4*g + e%4).
+    // Operands of this sub-tile, read from LDS before the first MFMA so that
+    // their latency overlaps: A of S^T (row-wise), and the C^T operands of
+    // P.C (transpose reads; K-slot e of lane group g in half h2 is token
+    // 16*h2 + 8*(e/4) + 4*g + e%4). With two row tiles the registers are
+    // short, and the C^T operands are read next to their MFMAs instead.
+    constexpr bool kEagerT = NT == 1;
+    auto read_t = [&](int h2, int dt) {
+      const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
+      const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     bf16x8 aR[NR], aL[NL], aT[2][NDT];
     if (has_rope) {
 #pragma unroll
@@ -365,15 +389,12 @@ mlra_split_mfma(SplitParams p) {
 #pragma unroll
     for (int st = 0; st < NL; ++st)
       aL[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(al_base + st * 16));
+    if constexpr (kEagerT) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
-        const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
-        aT[h2][dt] =
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+        for (int dt = 0; dt < NDT; ++dt) aT[h2][dt] = read_t(h2, dt);
+    }
 
     // S^T[token][row] = C . Q^T
     f32x16 sc[NT];
@@ -478,11 +499,12 @@ mlra_split_mfma(SplitParams p) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 at = kEagerT ? aT[h2][dt] : read_t(h2, dt);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[nt][dt] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(aT[h2][dt], pB[nt][h2], acc[nt][dt], 0, 0, 0);
+          acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pB[nt][h2], acc[nt][dt], 0, 0, 0);
+      }
   };
 
   // Software pipeline: PD sub-tiles in flight in registers. The wave stages
@@ -519,7 +541,7 @@ mlra_split_mfma(SplitParams p) {
     // Partial (output / l, lse) of this split for each (branch, row).
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int row = nt * 32 + n;
+      const int row = row0 + nt * 32 + n;
       if (row >= p.rows) continue;
       const float l = l_run[nt];
       const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -581,7 +603,7 @@ mlra_split_mfma(SplitParams p) {
         wsc[w] = __builtin_amdgcn_exp2f(ms[w][nt] - m_use);
         l += ls[w][nt] * wsc[w];
       }
-      const int row = nt * 32 + n;
+      const int row = row0 + nt * 32 + n;
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const int64_t ri = (slot * NB + b) * p.rows + row;
       if (row < p.rows) {
@@ -743,10 +765,16 @@ __device__ __forceinline__ void load_vpl(float (&v)[VPL], const float* src) {
   }
 }
 
+// One workgroup per (sequence, query row), one wave per branch: wave b merges
+// the splits of branch b (weights exp(lse_k - lse_b)), writes lse_b and, for
+// CONCAT, its output slice; for SUM the branch outputs meet in LDS and wave 0
+// adds them in branch order and applies out_rescale.
 template <typename OutT, int VPL>
-__global__ void __launch_bounds__(64) mlra_combine(CombineParams c) {
-  constexpr int KB = VPL >= 4 ? 8 : 16;  // splits whose loads are in flight together
-  const int lane = threadIdx.x;
+__global__ void __launch_bounds__(256) mlra_combine(CombineParams c) {
+  constexpr int KB = VPL >= 8 ? 8 : (VPL >= 4 ? 16 : 32);  // splits in flight together
+  __shared__ float red[4 * 512];
+  const int lane = threadIdx.x & 63;
+  const int b = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pair = blockIdx.x;
   const int s = pair / c.rows, row = pair % c.rows;
   const int L_raw = c.seq_lens[s];
@@ -755,76 +783,82 @@ __global__ void __launch_bounds__(64) mlra_combine(CombineParams c) {
   const int64_t kstride = (int64_t)c.NB * c.rows;  // between splits, in rows
   const int last = c.spl - 1;
   OutT* out = static_cast<OutT*>(c.out);
-  float tot[VPL];
+
+  const int64_t base = ((int64_t)s * c.spl * c.NB + b) * c.rows + row;
+  const float* lse_p = c.part_lse + base;
+  const float* o_p = c.part_o + base * c.DC + lane * VPL;
+  // Unconditional loads (indices clamped into the plan's splits) so the
+  // compiler keeps them all in flight; results past the sequence's split
+  // count are discarded with selects.
+  float v[KB][VPL];
 #pragma unroll
-  for (int e = 0; e < VPL; ++e) tot[e] = 0.f;
-  for (int b = 0; b < c.NB; ++b) {
-    const int64_t base = ((int64_t)s * c.spl * c.NB + b) * c.rows + row;
-    const float* lse_p = c.part_lse + base;
-    const float* o_p = c.part_o + base * c.DC + lane * VPL;
-    // Unconditional loads (indices clamped into the plan's splits) so the
-    // compiler keeps them all in flight; results past the sequence's split
-    // count are discarded with selects.
-    float v[KB][VPL];
+  for (int u = 0; u < KB; ++u) load_vpl<VPL>(v[u], o_p + (int64_t)min(u, last) * kstride * c.DC);
+  const float l0 = lse_p[(int64_t)min(lane, last) * kstride];
+  const int L = L_raw < 0 ? 0 : (L_raw > c.lcap ? c.lcap : L_raw);
+  const int nsplit = min((L + kBlock * c.tps - 1) / (kBlock * c.tps), c.spl);
+  float M = lane < nsplit ? l0 : -INFINITY;
+  for (int k0 = 64; k0 < nsplit; k0 += 64) {
+    const float lk = lse_p[(int64_t)min(k0 + lane, last) * kstride];
+    M = fmaxf(M, k0 + lane < nsplit ? lk : -INFINITY);
+  }
+  M = wave_max(M);
+  float o[VPL];
 #pragma unroll
-    for (int u = 0; u < KB; ++u) load_vpl<VPL>(v[u], o_p + (int64_t)min(u, last) * kstride * c.DC);
-    const float l0 = lse_p[(int64_t)min(lane, last) * kstride];
-    const int L = L_raw < 0 ? 0 : (L_raw > c.lcap ? c.lcap : L_raw);
-    const int nsplit = min((L + kBlock * c.tps - 1) / (kBlock * c.tps), c.spl);
-    float M = lane < nsplit ? l0 : -INFINITY;
-    for (int k0 = 64; k0 < nsplit; k0 += 64) {
-      const float lk = lse_p[(int64_t)min(k0 + lane, last) * kstride];
-      M = fmaxf(M, k0 + lane < nsplit ? lk : -INFINITY);
-    }
-    M = wave_max(M);
-    float o[VPL];
+  for (int e = 0; e < VPL; ++e) o[e] = 0.f;
+  float lse_b = -INFINITY;
+  if (M != -INFINITY) {
+    float den = 0.f;
+    for (int k0 = 0; k0 < nsplit; k0 += 64) {
+      const float lk = k0 == 0 ? l0 : lse_p[(int64_t)min(k0 + lane, last) * kstride];
+      const float w = k0 + lane < nsplit ? expf(lk - M) : 0.f;
+      den += w;
+      const int kn = min(64, nsplit - k0);
+      for (int q0 = 0; q0 < kn; q0 += KB) {
+        if (k0 + q0 > 0) {
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) o[e] = 0.f;
-    float lse_b = -INFINITY;
-    if (M != -INFINITY) {
-      float den = 0.f;
-      for (int k0 = 0; k0 < nsplit; k0 += 64) {
-        const float lk = k0 == 0 ? l0 : lse_p[(int64_t)min(k0 + lane, last) * kstride];
-        const float w = k0 + lane < nsplit ? expf(lk - M) : 0.f;
-        den += w;
-        const int kn = min(64, nsplit - k0);
-        for (int q0 = 0; q0 < kn; q0 += KB) {
-          if (k0 + q0 > 0) {
+          for (int u = 0; u < KB; ++u)
+            load_vpl<VPL>(v[u], o_p + (int64_t)min(k0 + q0 + u, last) * kstride * c.DC);
+        }
 #pragma unroll
-            for (int u = 0; u < KB; ++u)
-              load_vpl<VPL>(v[u], o_p + (int64_t)min(k0 + q0 + u, last) * kstride * c.DC);
-          }
+        for (int u = 0; u < KB; ++u) {
+          const bool use = q0 + u < kn;
+          const float wq =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(q0 + u, 63)));
 #pragma unroll
-          for (int u = 0; u < KB; ++u) {
-            const bool use = q0 + u < kn;
-            const float wq =
-                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(q0 + u, 63)));
-#pragma unroll
-            for (int e = 0; e < VPL; ++e) o[e] = use ? fmaf(wq, v[u][e], o[e]) : o[e];
-          }
+          for (int e = 0; e < VPL; ++e) o[e] = use ? fmaf(wq, v[u][e], o[e]) : o[e];
         }
       }
-      den = wave_sum(den);
-      const float inv = 1.f / den;
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) o[e] *= inv;
-      lse_b = M + logf(den);
     }
-    if (c.concat) {
+    den = wave_sum(den);
+    const float inv = 1.f / den;
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) o[e] *= c.out_rescale;
-      store_vpl<OutT, VPL>(out + (orow * c.NB + b) * c.DC + lane * VPL, o);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) tot[e] += o[e];
-    }
-    if (lane == 0) c.lse[orow * c.NB + b] = lse_b;
+    for (int e = 0; e < VPL; ++e) o[e] *= inv;
+    lse_b = M + logf(den);
   }
-  if (!c.concat) {
+  if (lane == 0) c.lse[orow * c.NB + b] = lse_b;
+  if (c.concat) {
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) tot[e] *= c.out_rescale;
-    store_vpl<OutT, VPL>(out + orow * c.DC + lane * VPL, tot);
+    for (int e = 0; e < VPL; ++e) o[e] *= c.out_rescale;
+    store_vpl<OutT, VPL>(out + (orow * c.NB + b) * c.DC + lane * VPL, o);
+    return;
   }
+  if (c.NB > 1) {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) red[b * 64 * VPL + lane * VPL + e] = o[e];
+    __syncthreads();
+    if (b != 0) return;
+    float tot[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) tot[e] = 0.f;
+    for (int bb = 0; bb < c.NB; ++bb)
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) tot[e] += red[bb * 64 * VPL + lane * VPL + e];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) o[e] = tot[e];
+  }
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) o[e] *= c.out_rescale;
+  store_vpl<OutT, VPL>(out + orow * c.DC + lane * VPL, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -850,7 +884,9 @@ static hipError_t launch_mfma(const SplitParams& sp, const mlra_decode_plan& pla
       attr_set = true;
     }
   }
-  dim3 grid(plan.splits_per_seq, sp.S);
+  const dim3 grid = sp.nrt == 1
+                       ? dim3(plan.splits_per_seq, sp.S)
+                       : dim3((uint32_t)(((int64_t)sp.S * plan.splits_per_seq + 7) / 8 * 16));
   hipLaunchKernelGGL(kern, grid, dim3(64 * NB * WD * WT), lds, stream, sp);
   return hipGetLastError();
 }
@@ -889,8 +925,7 @@ static hipError_t dispatch_nb(const SplitParams& sp, const mlra_decode_plan& pla
 
 static hipError_t launch_split(const SplitParams& sp, const KernelShape& ks,
                                const mlra_decode_plan& plan, hipStream_t st) {
-  if (ks.variant == kVariantMfmaBf16)
-    return ks.NT == 1 ? dispatch_nb<1>(sp, plan, st) : dispatch_nb<2>(sp, plan, st);
+  if (ks.variant == kVariantMfmaBf16) return dispatch_nb<1>(sp, plan, st);
   dim3 grid(plan.splits_per_seq, sp.S, (sp.rows * sp.NB + 3) / 4);
   switch (sp.DC / 64) {
     case 1: hipLaunchKernelGGL(mlra_split_valu<1>, grid, dim3(256), 0, st, sp); break;
@@ -904,10 +939,11 @@ static hipError_t launch_split(const SplitParams& sp, const KernelShape& ks,
 
 template <int VPL>
 static void launch_combine(bool bf16, dim3 grid, const CombineParams& cp, hipStream_t st) {
+  const dim3 block(64 * cp.NB);  // one wave per branch
   if (bf16)
-    hipLaunchKernelGGL((mlra_combine<__bf16, VPL>), grid, dim3(64), 0, st, cp);
+    hipLaunchKernelGGL((mlra_combine<__bf16, VPL>), grid, block, 0, st, cp);
   else
-    hipLaunchKernelGGL((mlra_combine<float, VPL>), grid, dim3(64), 0, st, cp);
+    hipLaunchKernelGGL((mlra_combine<float, VPL>), grid, block, 0, st, cp);
 }
 
 static int device_cus(int* out) {
@@ -997,6 +1033,7 @@ static mlra_status decode(int phases, const void* q_latent, const void* q_rope,
   sp.num_blocks = r.num_blocks;
   sp.lcap = r.lcap;
   sp.causal = r.causal;
+  sp.nrt = ks.NRT;
   sp.score_scale = scale * kLog2e;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (do_split && launch_split(sp, ks, plan, hs) != hipSuccess) return MLRA_ERR_HIP;
