@@ -67,10 +67,21 @@ struct KernelShape {
 //   RoPE query rows         one                    [NT*32][rpitch]  (unless in registers)
 //   score exchange (WD > 1) [NB*WT][WD][NT][64 lanes][16 floats]
 // and, aliased over all of it after the token loop, the cross-wave merge
-// records when WT > 1: [WT][NB*WD][NT*NDT*4 + 1][64 lanes] float4.
+// records when WT > 1: [WT][NB*WD][NT*NDT*4 + 1][64 lanes] float4. In the
+// slotted layout (below) every wave instead owns one slot holding its latent
+// and RoPE stages and, after its loop, its merge record.
+// Slotted layout: with one latent stage per wave, queries in registers and a
+// token-split merge, each wave's stage and merge record share one slot.
+constexpr bool mfma_slotted(int WD, int WT, bool qreg) { return WD == 1 && WT > 1 && qreg; }
+
 inline int32_t mfma_lds_bytes(int NB, int DCW, int WD, int DR, int NT, int WT, bool qreg) {
   const int waves = NB * WD * WT;
   const int lp = mfma_lpitch(DCW), rp = mfma_rpitch(DR);
+  if (mfma_slotted(WD, WT, qreg)) {
+    const int stage = 32 * (lp + rp) * 16;
+    const int rec = (NT * (DCW / 32) * 4 + 1) * 64 * 16;
+    return waves * (stage > rec ? stage : rec);
+  }
   const int stage = waves * 32 * lp * 16 + NB * WT * 32 * rp * 16;
   const int qry = qreg ? 0 : (NB * WD * lp + rp) * NT * 32 * 16;
   const int xchg = (WD > 1) ? NB * WT * WD * NT * 64 * 16 * 4 : 0;

@@ -268,9 +268,19 @@ mlra_split_mfma(SplitParams p) {
   // wave's slice, or RoPE feature g*DR/2 + 8*st + e. Padding rows are zero.
   // LDS layout (see mfma_lds_bytes). The RoPE query rows are shared by all
   // branches and staged once; RoPE tiles only by the waves that use them.
-  unsigned char* stage_l = smem + wave * kSub * LP * 16;
+  // Slotted layout (one latent and RoPE stage per wave, WD == 1, queries in
+  // registers): each wave owns one slot that later holds its merge record, so
+  // a wave that has finished its tiles publishes its record without waiting
+  // for the others.
+  constexpr int REC_B = (NT * NDT * 4 + 1) * 64 * 16;  // merge record bytes per wave
+  constexpr int STAGE_B = kSub * (LP + RP) * 16;
+  constexpr bool kSlotted = mfma_slotted(WD, WT, QREG);
+  constexpr int SLOT_B = STAGE_B > REC_B ? STAGE_B : REC_B;
+  static_assert(!kSlotted || WAVES * SLOT_B <= 160 * 1024, "slotted LDS layout exceeds 160 KB");
+  unsigned char* stage_l = kSlotted ? smem + wave * SLOT_B : smem + wave * kSub * LP * 16;
   unsigned char* const rope_base = smem + WAVES * kSub * LP * 16;
-  unsigned char* stage_r = rope_base + (wt * NB + b) * kSub * RP * 16;
+  unsigned char* stage_r = kSlotted ? stage_l + kSub * LP * 16
+                                    : rope_base + (wt * NB + b) * kSub * RP * 16;
   unsigned char* const q_base = rope_base + NB * WT * kSub * RP * 16;
   unsigned char* q_l = q_base + (b * WD + wd) * NT * kSub * LP * 16;
   unsigned char* q_r = q_base + NB * WD * NT * kSub * LP * 16;
@@ -561,11 +571,13 @@ mlra_split_mfma(SplitParams p) {
     // Merge the WT token-split waves of each (branch, width slice): every wave
     // publishes its record, then wave wt merges the d-tiles dt = wt, wt+WT, ...
     constexpr int REC = NT * NDT * 4 + 1;  // float4 records per lane
-    __syncthreads();  // all waves are done with the staged tiles
+    // Record of wave (w, gi) starts at M + (w*NB*WD + gi) * RS float4s.
+    constexpr int RS = kSlotted ? SLOT_B / 16 : REC * 64;
+    if constexpr (!kSlotted) __syncthreads();  // all waves are done with the staged tiles
     f32x4* M = reinterpret_cast<f32x4*>(smem);
     const int gi = b * WD + wd;
     {
-      f32x4* my = M + (wt * NB * WD + gi) * REC * 64;
+      f32x4* my = M + (wt * NB * WD + gi) * RS;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -582,7 +594,7 @@ mlra_split_mfma(SplitParams p) {
     float ms[WT][NT], ls[WT][NT];
 #pragma unroll
     for (int w = 0; w < WT; ++w) {
-      const f32x4 ml = M[((w * NB * WD + gi) * REC + REC - 1) * 64 + lane];
+      const f32x4 ml = M[(w * NB * WD + gi) * RS + (REC - 1) * 64 + lane];
       ms[w][0] = ml[0];
       ls[w][0] = ml[1];
       if constexpr (NT > 1) {
@@ -616,7 +628,7 @@ mlra_split_mfma(SplitParams p) {
           f32x4 v = f32x4{};
 #pragma unroll
           for (int w = 0; w < WT; ++w)
-            v += M[((w * NB * WD + gi) * REC + (nt * NDT + dt) * 4 + q) * 64 + lane] * wsc[w];
+            v += M[(w * NB * WD + gi) * RS + ((nt * NDT + dt) * 4 + q) * 64 + lane] * wsc[w];
           *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
         }
         if (g == 0 && wd == 0 && wt == 0)
@@ -769,9 +781,8 @@ __device__ __forceinline__ void load_vpl(float (&v)[VPL], const float* src) {
 // the splits of branch b (weights exp(lse_k - lse_b)), writes lse_b and, for
 // CONCAT, its output slice; for SUM the branch outputs meet in LDS and wave 0
 // adds them in branch order and applies out_rescale.
-template <typename OutT, int VPL>
+template <typename OutT, int VPL, int KB>  // KB: splits whose loads are in flight together
 __global__ void __launch_bounds__(256) mlra_combine(CombineParams c) {
-  constexpr int KB = VPL >= 8 ? 8 : (VPL >= 4 ? 16 : 32);  // splits in flight together
   __shared__ float red[4 * 512];
   const int lane = threadIdx.x & 63;
   const int b = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -937,13 +948,26 @@ static hipError_t launch_split(const SplitParams& sp, const KernelShape& ks,
   return hipGetLastError();
 }
 
-template <int VPL>
-static void launch_combine(bool bf16, dim3 grid, const CombineParams& cp, hipStream_t st) {
+template <int VPL, int KB>
+static void launch_combine_kb(bool bf16, dim3 grid, const CombineParams& cp, hipStream_t st) {
   const dim3 block(64 * cp.NB);  // one wave per branch
   if (bf16)
-    hipLaunchKernelGGL((mlra_combine<__bf16, VPL>), grid, block, 0, st, cp);
+    hipLaunchKernelGGL((mlra_combine<__bf16, VPL, KB>), grid, block, 0, st, cp);
   else
-    hipLaunchKernelGGL((mlra_combine<float, VPL>), grid, block, 0, st, cp);
+    hipLaunchKernelGGL((mlra_combine<float, VPL, KB>), grid, block, 0, st, cp);
+}
+
+// Loads in flight per wave: enough for every split when there are few (loads
+// past the split count are wasted), at most 64 registers of partials.
+template <int VPL>
+static void launch_combine(bool bf16, dim3 grid, const CombineParams& cp, hipStream_t st) {
+  constexpr int kMax = 64 / VPL;
+  if (cp.spl <= 8 || kMax <= 8)
+    launch_combine_kb<VPL, 8>(bf16, grid, cp, st);
+  else if (cp.spl <= 16 || kMax <= 16)
+    launch_combine_kb<VPL, (kMax < 16 ? kMax : 16)>(bf16, grid, cp, st);
+  else
+    launch_combine_kb<VPL, (kMax < 32 ? kMax : 32)>(bf16, grid, cp, st);
 }
 
 static int device_cus(int* out) {
