@@ -101,10 +101,25 @@ KernelShape choose_shape(const Resolved& r) {
     k.groups_per_cu = 2;
     return k;
   }
+  if (r.DC <= 128) {
+    // Streaming kernel: 32 query rows per workgroup, waves split over the
+    // branches and the split's tiles.
+    k.variant = kVariantStreamBf16;
+    k.NT = 1;
+    k.NRT = r.rows > 32 ? 2 : 1;  // 64 rows: two XCD-paired workgroups per split
+    k.WD = 1;
+    const int waves = r.DC == 128 ? (r.DR == 64 ? stream_waves(r.NB, 128, 64, k.NT)
+                                                : stream_waves(r.NB, 128, 32, k.NT))
+                                  : (r.DR == 64 ? stream_waves(r.NB, 64, 64, k.NT)
+                                                : stream_waves(r.NB, 64, 32, k.NT));
+    k.WT = waves / r.NB;
+    k.NPF = stream_pd(k.NT, waves);
+    k.waves = waves;
+    k.groups_per_cu = 1;
+    return k;
+  }
   k.variant = kVariantMfmaBf16;
-  // A wave holds 32 query rows; 64 rows run as two workgroups per split
-  // (register pressure of two row tiles in one wave costs more than reading
-  // each cache tile twice from L2).
+  // A wave holds 32 query rows; 64 rows run as two workgroups per split.
   k.NT = 1;
   k.NRT = r.rows > 32 ? 2 : 1;
   k.WD = mfma_wd(r.DC);
@@ -185,6 +200,8 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
   p.row_groups = k.NRT;
   p.lds_bytes = k.variant == kVariantMfmaBf16
                     ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, r.DR, k.NT, k.WT, mfma_qreg(k.NT, r.DC))
+                : k.variant == kVariantStreamBf16
+                    ? stream_lds(r.NB, r.DC, r.DR, k.NT, k.waves).total
                     : 0;
   // Partials: output [S][spl][NB][rows][DC] and lse [S][spl][NB][rows], fp32.
   const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;

@@ -42,6 +42,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
+// Lazy softmax reference: probabilities exp2(score - m_ref) stay below
+// 2^kLazyLog2 = 256 (exact in fp32 accumulation and bf16 operands).
+constexpr float kLazyLog2 = 8.0f;
 
 struct SplitParams {
   const void* q_lat;
@@ -177,24 +180,29 @@ mlra_split_mfma(SplitParams p) {
   const __bf16* __restrict__ rope = static_cast<const __bf16*>(p.rope);
 
   // Independent loads first: sequence length, this wave's first 64 block ids
-  // (any id below max_blocks lies inside the table) and the queries.
+  // (one per lane; any id below max_blocks lies inside the table) and the
+  // queries.
   const int L_raw = p.seq_lens[s];
   const int64_t tab_base = (int64_t)s * p.max_blocks;
-  // Loads in this prologue are unconditional (clamped, in-bounds addresses,
-  // results selected afterwards) so that the compiler can count outstanding
-  // loads exactly and never waits on more than it needs.
+  // Every global load in this kernel is unconditional (clamped, in-bounds
+  // addresses, results selected afterwards): the compiler then counts the
+  // outstanding loads exactly on every path and waits only for the sub-tile
+  // it needs, which keeps PD sub-tiles per wave in flight.
   int tab = p.table[tab_base + min(t0 + wt + WT * lane, p.max_blocks - 1)];
-  int tab_chunk = 0;
 
-  // Query rows (the B operand of S^T = C . Q^T) are staged once per workgroup
-  // in LDS, padded like the cache tiles: latent rows per (branch, width
-  // slice), RoPE rows once (shared by all branches). Every wave loads a share
-  // first, before its cache loads, so that writing it to LDS waits only on
-  // these loads. K-slot (g, e) of step st is latent feature g*DCW/2 + 8*st + e
-  // of the slice, or RoPE feature g*DR/2 + 8*st + e. Padding rows are zero.
+  // Query rows (the B operand of S^T = C . Q^T) are loaded once per workgroup
+  // with coalesced 16-byte loads (consecutive lanes, consecutive chunks of a
+  // row) and staged in LDS, padded like the cache tiles: latent rows per
+  // (branch, width slice), RoPE rows once (shared by all branches). Every
+  // wave loads a share first, before its cache loads, so that writing it to
+  // LDS waits only on these loads. K-slot (g, e) of step st is latent feature
+  // g*DCW/2 + 8*st + e of the slice, or RoPE feature g*DR/2 + 8*st + e.
+  // Padding rows are zero. (Loading the B operand straight from global memory
+  // would touch 64 cache lines per instruction and hold up the cache loads
+  // queued behind it in the CU's memory pipeline.)
   constexpr int QL_CH = NB * WD * NT * kSub * LCH;  // latent query chunks
   constexpr int Q_CH = QL_CH + NT * kSub * RCH;     // + RoPE query chunks
-  constexpr int QK = QREG ? 0 : (Q_CH + WAVES * 64 - 1) / (WAVES * 64);
+  constexpr int QK = (Q_CH + WAVES * 64 - 1) / (WAVES * 64);
   u32x4 qv[QK > 0 ? QK : 1];
   int qdst[QK > 0 ? QK : 1];  // LDS byte offset in the query region, -1 = none
 #pragma unroll
@@ -228,30 +236,10 @@ mlra_split_mfma(SplitParams p) {
     const int row = row0 + nt * 32 + n;
     jrow[nt] = row < p.rows ? row / p.H : 0;
   }
-  // Register-resident queries: lane (n, g) holds row n's features of K-slot
-  // group g (same K-slot order as the staged layout). Loaded unconditionally
-  // from a clamped row, zeroed for padding rows.
+  // Register-resident queries (QREG): lane (n, g) holds row n's features of
+  // K-slot group g, read from the staged rows once before the token loop.
   constexpr int NLq = QREG ? NL : 1, NRq = QREG ? NR : 1;
   bf16x8 qLr[NLq], qRr[NRq];
-  if constexpr (QREG) {
-    const int row = row0 + n;
-    const bool ok = row < p.rows;
-    const int rs = ok ? row : 0;
-    const int j = rs / p.H, h = rs % p.H;
-    const int64_t head = ((int64_t)s * p.Q + j) * p.H + h;
-    const __bf16* ql = qlat + (head * NB + b) * DC + wd * DCW + g * (DCW / 2);
-    const __bf16* qr = qrop + head * DR + g * (DR / 2);
-#pragma unroll
-    for (int st = 0; st < NL; ++st) {
-      const u32x4 v = ld16(ql + 8 * st);
-      qLr[st] = __builtin_bit_cast(bf16x8, ok ? v : u32x4{});
-    }
-#pragma unroll
-    for (int st = 0; st < NR; ++st) {
-      const u32x4 v = ld16(qr + 8 * st);
-      qRr[st] = __builtin_bit_cast(bf16x8, (ok && has_rope) ? v : u32x4{});
-    }
-  }
 
   const int L = L_raw < 0 ? 0 : (L_raw > p.lcap ? p.lcap : L_raw);
   const int ntiles = (L + kBlock - 1) / kBlock;
@@ -281,10 +269,13 @@ mlra_split_mfma(SplitParams p) {
   unsigned char* const rope_base = smem + WAVES * kSub * LP * 16;
   unsigned char* stage_r = kSlotted ? stage_l + kSub * LP * 16
                                     : rope_base + (wt * NB + b) * kSub * RP * 16;
-  unsigned char* const q_base = rope_base + NB * WT * kSub * RP * 16;
+  // Register-resident queries are staged at the start of LDS, before any
+  // cache sub-tile; a barrier separates their last read from the first stage.
+  unsigned char* const q_base = QREG ? smem : rope_base + NB * WT * kSub * RP * 16;
   unsigned char* q_l = q_base + (b * WD + wd) * NT * kSub * LP * 16;
   unsigned char* q_r = q_base + NB * WD * NT * kSub * LP * 16;
-  float* xchg = reinterpret_cast<float*>(QREG ? q_base : q_r + NT * kSub * RP * 16);
+  unsigned char* const loop_end = rope_base + NB * WT * kSub * RP * 16;  // stages end here
+  float* xchg = reinterpret_cast<float*>(QREG ? loop_end : q_r + NT * kSub * RP * 16);
   f32x16 acc[NT][NDT];
   float m_run[NT], l_run[NT];
 #pragma unroll
@@ -313,11 +304,7 @@ mlra_split_mfma(SplitParams p) {
   auto load_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
     const int i = u >> 1;
     const int ti = t0 + wt + WT * i;
-    const bool valid = (u < nu) && ti < t1;
-    if ((i >> 6) != tab_chunk) {  // uniform: next 64 block ids of this wave
-      tab_chunk = i >> 6;
-      tab = p.table[tab_base + min(t0 + wt + WT * (tab_chunk * 64 + lane), p.max_blocks - 1)];
-    }
+    const bool valid = (u < nu) && ti < t1;  // false past this wave's tiles: block 0 is read
     const int phys = valid ? clamp_block(__builtin_amdgcn_readlane(tab, i & 63), p.num_blocks) : 0;
     const int sub = (u & 1) * kSub;
     // uniform base of this sub-tile (scalar registers) + 32-bit lane offset
@@ -325,12 +312,12 @@ mlra_split_mfma(SplitParams p) {
                      ((int64_t)phys * p.lsb + (int64_t)sub * p.lst + (int64_t)b * p.lsbr + wd * DCW) * 2;
 #pragma unroll
     for (int q = 0; q < LQ; ++q) dl[q] = ld16(lb + (size_t)q * l_step + l_lane);
-    if (has_rope) {
-      const char* rbp = reinterpret_cast<const char*>(rope) +
-                        ((int64_t)phys * p.rsb + (int64_t)sub * p.rst) * 2;
+    // Waves without the RoPE part (WD > 1, wd > 0) load it too, unused, so
+    // that every wave issues the same loads (they hit the lines wave 0 reads).
+    const char* rbp = reinterpret_cast<const char*>(rope) +
+                      ((int64_t)phys * p.rsb + (int64_t)sub * p.rst) * 2;
 #pragma unroll
-      for (int q = 0; q < RQ; ++q) dr[q] = ld16(rbp + (size_t)q * r_step + r_lane);
-    }
+    for (int q = 0; q < RQ; ++q) dr[q] = ld16(rbp + (size_t)q * r_step + r_lane);
   };
   auto zero_tail = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
     const int ti = t0 + wt + WT * (u >> 1);
@@ -380,26 +367,31 @@ mlra_split_mfma(SplitParams p) {
     const int tb = ti * kBlock + (u & 1) * kSub;
 
     // Operands of this sub-tile, read from LDS before the first MFMA so that
-    // their latency overlaps: A of S^T (row-wise), and the C^T operands of
-    // P.C (transpose reads; K-slot e of lane group g in half h2 is token
-    // 16*h2 + 8*(e/4) + 4*g + e%4). With two row tiles the registers are
-    // short, and the C^T operands are read next to their MFMAs instead.
-    constexpr bool kEagerT = NT == 1;
+    // their latency overlaps: A of S^T (row-wise), and, with queries in
+    // registers, the C^T operands of P.C (transpose reads; K-slot e of lane
+    // group g in half h2 is token 16*h2 + 8*(e/4) + 4*g + e%4). Otherwise
+    // the registers hold the sub-tiles in flight, and the C^T operands are
+    // read next to their MFMAs.
+    constexpr bool kEagerT = NT == 1 && QREG;
     auto read_t = [&](int h2, int dt) {
       const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
       const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    bf16x8 aR[NR], aL[NL], aT[2][NDT];
-    if (has_rope) {
-#pragma unroll
-      for (int st = 0; st < NR; ++st)
-        aR[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ar_base + st * 16));
-    }
-#pragma unroll
-    for (int st = 0; st < NL; ++st)
-      aL[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(al_base + st * 16));
+    // A of S^T: all of it up front with queries in registers, else one step
+    // at a time (the compiler overlaps each read with the previous MFMA).
+    auto read_a = [&](const unsigned char* base, int st) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + st * 16));
+    };
+    constexpr int NRe = kEagerT ? NR : 1, NLe = kEagerT ? NL : 1;
+    bf16x8 aR[NRe], aL[NLe], aT[2][NDT];
     if constexpr (kEagerT) {
+      if (has_rope) {
+#pragma unroll
+        for (int st = 0; st < NR; ++st) aR[st] = read_a(ar_base, st);
+      }
+#pragma unroll
+      for (int st = 0; st < NL; ++st) aL[st] = read_a(al_base, st);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -419,7 +411,8 @@ mlra_split_mfma(SplitParams p) {
           if constexpr (QREG) qv = qRr[st];
           else qv = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(qr_base + (nt * kSub * RP + st) * 16));
-          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qv, sc[nt], 0, 0, 0);
+          const bf16x8 a = kEagerT ? aR[kEagerT ? st : 0] : read_a(ar_base, st);
+          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv, sc[nt], 0, 0, 0);
         }
       }
     }
@@ -431,7 +424,8 @@ mlra_split_mfma(SplitParams p) {
         if constexpr (QREG) qv = qLr[st];
         else qv = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(ql_base + (nt * kSub * LP + st) * 16));
-        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qv, sc[nt], 0, 0, 0);
+        const bf16x8 a = kEagerT ? aL[kEagerT ? st : 0] : read_a(al_base, st);
+        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv, sc[nt], 0, 0, 0);
       }
     }
 
@@ -519,28 +513,57 @@ mlra_split_mfma(SplitParams p) {
 
   // Software pipeline: PD sub-tiles in flight in registers. The wave stages
   // the oldest into LDS, refills those registers with the sub-tile PD ahead,
-  // then computes it. The first sub-tile is staged before the wave waits for
-  // the other waves' query rows (when those are staged in LDS).
+  // then computes it. The steady-state loop always issues its loads (past
+  // the wave's last tile they re-read block 0) and the last PD sub-tiles of
+  // each run of 64 tiles (one register of block ids) are peeled off, so the
+  // outstanding-load count is the same on every path. The query rows are
+  // staged, and the workgroup synchronised on them, while the first
+  // sub-tiles are still in flight.
   const int nsteps = (nu + PD - 1) / PD * PD;
 #pragma unroll
   for (int i = 0; i < PD; ++i) load_unit(i, bl[i], br[i]);
-  if constexpr (!QREG) {
 #pragma unroll
-    for (int kq = 0; kq < QK; ++kq)
-      if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(q_base + qdst[kq]) = qv[kq];
+  for (int kq = 0; kq < QK; ++kq)
+    if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(q_base + qdst[kq]) = qv[kq];
+  lds_barrier();  // every wave's share of the query rows is staged
+  if constexpr (QREG) {
+#pragma unroll
+    for (int st = 0; st < NL; ++st)
+      qLr[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ql_base + st * 16));
+#pragma unroll
+    for (int st = 0; st < NR; ++st) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qr_base + st * 16);
+      qRr[st] = __builtin_bit_cast(bf16x8, has_rope ? v : u32x4{});
+    }
+    lds_barrier();  // the query rows are read before any wave stages a sub-tile
   }
-  for (int u0 = 0; u0 < nsteps; u0 += PD) {
+  constexpr int kChunk = 128;  // sub-tiles per register of block ids (64 tiles)
+  static_assert(kChunk % PD == 0, "chunks hold whole pipeline rounds");
+  for (int cb = 0;;) {
+    const int ce = min(nsteps, cb + kChunk);
+    int u0 = cb;
+    for (; u0 + PD < ce; u0 += PD) {
+#pragma unroll
+      for (int i = 0; i < PD; ++i) {
+        const int u = u0 + i;
+        zero_tail(u, bl[i], br[i]);
+        stage_unit(bl[i], br[i]);
+        load_unit(u + PD, bl[i], br[i]);
+        compute_unit(u);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
-      const int u = u0 + i;
-      zero_tail(u, bl[i], br[i]);
+      zero_tail(u0 + i, bl[i], br[i]);
       stage_unit(bl[i], br[i]);
-      if (u + PD < nsteps) load_unit(u + PD, bl[i], br[i]);
-      if constexpr (!QREG) {
-        if (u == 0) lds_barrier();  // queries staged
-      }
-      compute_unit(u);
+      compute_unit(u0 + i);
     }
+    cb = ce;
+    if (cb >= nsteps) break;  // uniform
+    // next 64 block ids of this wave, then the next chunk's first sub-tiles
+    tab = p.table[tab_base + min(t0 + wt + WT * ((cb >> 1) + lane), p.max_blocks - 1)];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) load_unit(cb + i, bl[i], br[i]);
   }
 
 #pragma unroll
@@ -637,6 +660,448 @@ mlra_split_mfma(SplitParams p) {
     }
   }
 
+}
+
+// ---------------------------------------------------------------------------
+// bf16 split kernel for latent widths 64 and 128 (streaming form)
+// ---------------------------------------------------------------------------
+// One workgroup of four waves (one per SIMD, up to 512 registers each) covers
+// one split of one sequence for every query row (NT tiles of 32 rows). Wave w
+// takes branch b = w % NB and tiles t0 + wt + WT*i of the split (wt = w / NB,
+// WT = 4 / NB); with WT > 1 the token-split waves of a branch merge their
+// (m, l, O) through LDS at the end.
+//
+// Why this shape: decode streams each cache byte once, and a wave only hides
+// HBM latency with the loads it has in flight. Each wave requests its next PD
+// 32-token sub-tiles (12 KB each at DC = 128, DR = 64) before computing the
+// first: a workgroup has 4*PD sub-tiles in flight from the start. Every global
+// load is unconditional (clamped addresses, results selected afterwards) and
+// the last PD sub-tiles of each run are peeled off, so on every path the
+// compiler waits only for the sub-tile it is about to use.
+//
+// Per sub-tile (stage -> S^T -> softmax -> P.C), as in the 8-wave kernel: the
+// coalesced loads are written to a padded per-wave LDS stage; S^T = C . Q^T on
+// v_mfma_f32_32x32x16_bf16 with the tile rows as A (row-wise LDS reads) and
+// the query rows as B; base-2 online softmax, lane-local per query row apart
+// from one v_permlane32_swap; O^T += C^T . P^T with C^T from ds_read_b64_tr_b16
+// and P in the registers the softmax left it in.
+template <int NB, int DC, int DR, int NT, int PD, bool QREG, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
+mlra_split_stream(SplitParams p) {
+  constexpr int WT = WAVES / NB;
+  constexpr int NL = DC / 16;   // S^T k-steps over the latent
+  constexpr int NR = DR / 16;   // S^T k-steps over the RoPE key
+  constexpr int NDT = DC / 32;  // 32-wide d tiles of O^T
+  constexpr int LCH = DC / 8;   // 16-byte chunks per latent row
+  constexpr int RCH = DR / 8;
+  constexpr int LQ = kSub * LCH / 64;  // coalesced 16-byte loads per lane per sub-tile
+  constexpr int RQ = kSub * RCH / 64;
+  constexpr int LP = mfma_lpitch(DC), RP = mfma_rpitch(DR);
+  constexpr int ROWS = NT * kSub;  // query rows per workgroup (padded)
+  static_assert(WAVES % NB == 0 && (WAVES == 4 || WAVES == 8), "waves split over the branches");
+  static_assert(LQ >= 1 && RQ >= 1, "bad shape");
+  constexpr StreamLds lay = stream_lds(NB, DC, DR, NT, WAVES);
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = wave % NB, wt = wave / NB;
+  const int n = lane & 31, g = lane >> 5;
+  // Workgroup -> (split k, sequence s, 32-row group rt). With two row groups
+  // (64 query rows, one row tile per workgroup), ids 16c + i and 16c + 8 + i
+  // (i < 8) are the two row groups of split pair 8c + i: workgroups are dealt
+  // round-robin over the 8 XCDs, so both land on one XCD at about the same
+  // time and the second finds the tiles in that XCD's L2.
+  int k, s, rt = 0;
+  if (p.nrt == 1) {
+    k = blockIdx.x;
+    s = blockIdx.y;
+  } else {
+    const int id = blockIdx.x;
+    const int pr = (id >> 4) * 8 + (id & 7);
+    if (pr >= p.S * p.spl) return;  // grid rounded up to 16
+    rt = (id >> 3) & 1;
+    s = pr / p.spl;
+    k = pr % p.spl;
+  }
+  const int row0 = rt * ROWS;  // first query row of this workgroup
+  const int t0 = k * p.tps;
+  const __bf16* __restrict__ qlat = static_cast<const __bf16*>(p.q_lat);
+  const __bf16* __restrict__ qrop = static_cast<const __bf16*>(p.q_rope);
+  const __bf16* __restrict__ lat = static_cast<const __bf16*>(p.lat);
+  const __bf16* __restrict__ rope = static_cast<const __bf16*>(p.rope);
+  unsigned char* const stage_l = smem + lay.stage + wave * lay.stage_bytes;
+  unsigned char* const stage_r = stage_l + kSub * LP * 16;
+  unsigned char* const q_l = smem + lay.query + b * ROWS * LP * 16;  // this branch's rows
+  unsigned char* const q_r = smem + lay.query + NB * ROWS * LP * 16;
+
+  // Prologue loads, all independent: length, this wave's first 64 block ids
+  // (one per lane; any id below max_blocks lies inside the table) and the
+  // workgroup's query rows, coalesced (consecutive threads, consecutive
+  // 16-byte chunks of a row). Query rows past H*Q are zero.
+  const int L_raw = p.seq_lens[s];
+  const int64_t tab_base = (int64_t)s * p.max_blocks;
+  int tab = p.table[tab_base + min(t0 + wt + WT * lane, p.max_blocks - 1)];
+  constexpr int QL_CH = NB * ROWS * LCH;
+  constexpr int Q_CH = QL_CH + ROWS * RCH;
+  constexpr int QK = (Q_CH + 64 * WAVES - 1) / (64 * WAVES);
+  u32x4 qv[QK];
+  int qdst[QK];
+#pragma unroll
+  for (int kq = 0; kq < QK; ++kq) {
+    const int x = kq * 64 * WAVES + threadIdx.x;
+    const bool is_lat = x < QL_CH;
+    const bool is_rope = !is_lat && x < Q_CH;
+    const int bb = x / (ROWS * LCH), rem = x % (ROWS * LCH);
+    const int rl = rem / LCH, cl = rem % LCH;
+    const int xr = is_rope ? x - QL_CH : 0;
+    const int rr = xr / RCH, cr = xr % RCH;
+    const int r = row0 + (is_lat ? rl : rr);
+    const bool live = (is_lat || is_rope) && r < p.rows;
+    const int rs = live ? r : 0;
+    const int64_t head = ((int64_t)s * p.Q + rs / p.H) * p.H + rs % p.H;
+    const __bf16* src = is_lat ? qlat + (head * NB + (is_lat ? bb : 0)) * DC + cl * 8
+                               : qrop + head * DR + cr * 8;
+    const u32x4 v = ld16(src);
+    qv[kq] = live ? v : u32x4{};
+    qdst[kq] = is_lat ? lay.query + ((bb * ROWS + rl) * LP + cl) * 16
+                      : (is_rope ? lay.query + NB * ROWS * LP * 16 + (rr * RP + cr) * 16 : -1);
+  }
+
+  const int L = L_raw < 0 ? 0 : (L_raw > p.lcap ? p.lcap : L_raw);
+  const int ntiles = (L + kBlock - 1) / kBlock;
+  if (t0 >= ntiles) return;  // uniform over the workgroup: no barrier skipped
+  const int t1 = min(t0 + p.tps, ntiles);
+  // Sub-tiles per wave: the same count for every wave of the workgroup (the
+  // extra ones of short waves are invalid and skipped).
+  const int nu = 2 * ((t1 - t0 + WT - 1) / WT);
+  const int nu_w = 2 * max(0, (t1 - t0 - wt + WT - 1) / WT);  // this wave's valid sub-tiles
+  int vis[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = row0 + nt * kSub + n;
+    const int j = row < p.rows ? row / p.H : 0;
+    vis[nt] = p.causal ? L - (p.Q - 1 - j) : L;
+  }
+  const int min_vis = p.causal ? L - (p.Q - 1) : L;
+
+  f32x16 acc[NT][NDT];
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[nt][dt] = f32x16{};
+  }
+
+  // Coalesced loads of one sub-tile: instruction q, lane -> 16-byte chunk
+  // 64*q + lane, i.e. row (64*q + lane) / CH, chunk (64*q + lane) % CH. A
+  // sub-tile past this wave's tiles reads block 0; rows past L stay inside
+  // their block and are zeroed before any arithmetic.
+  u32x4 bl[PD][LQ], br[PD][RQ];
+  const uint32_t l_lane = (uint32_t)((lane / LCH) * p.lst * 2 + (lane % LCH) * 16);
+  const uint32_t l_step = (uint32_t)((64 / LCH) * p.lst * 2);
+  const uint32_t r_lane = (uint32_t)((lane / RCH) * p.rst * 2 + (lane % RCH) * 16);
+  const uint32_t r_step = (uint32_t)((64 / RCH) * p.rst * 2);
+  auto load_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
+    const int i = u >> 1;
+    const bool valid = u < nu_w;
+    const int phys = valid ? clamp_block(__builtin_amdgcn_readlane(tab, i & 63), p.num_blocks) : 0;
+    const int sub = (u & 1) * kSub;
+    const char* lb = reinterpret_cast<const char*>(lat) +
+                     ((int64_t)phys * p.lsb + (int64_t)sub * p.lst + (int64_t)b * p.lsbr) * 2;
+    const char* rb = reinterpret_cast<const char*>(rope) +
+                     ((int64_t)phys * p.rsb + (int64_t)sub * p.rst) * 2;
+    // 32-bit offsets within the block (checked on the host): a scalar base
+    // plus one vector offset per load.
+#pragma unroll
+    for (int q = 0; q < LQ; ++q) dl[q] = ld16(lb + (uint32_t)(q * l_step + l_lane));
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) dr[q] = ld16(rb + (uint32_t)(q * r_step + r_lane));
+  };
+  // Stage one sub-tile in this wave's LDS slot, rows past L zeroed.
+  unsigned char* const wl_base = stage_l + ((lane / LCH) * LP + lane % LCH) * 16;
+  unsigned char* const wr_base = stage_r + ((lane / RCH) * RP + lane % RCH) * 16;
+  auto stage_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
+    const int tok0 = (t0 + wt + WT * (u >> 1)) * kBlock + (u & 1) * kSub;
+    if (tok0 + kSub > L) {  // uniform: the sub-tile holds the sequence end
+#pragma unroll
+      for (int q = 0; q < LQ; ++q)
+        dl[q] = tok0 + (q * 64 + lane) / LCH < L ? dl[q] : u32x4{};
+#pragma unroll
+      for (int q = 0; q < RQ; ++q)
+        dr[q] = tok0 + (q * 64 + lane) / RCH < L ? dr[q] : u32x4{};
+    }
+#pragma unroll
+    for (int q = 0; q < LQ; ++q)
+      *reinterpret_cast<u32x4*>(wl_base + q * (64 / LCH) * LP * 16) = dl[q];
+#pragma unroll
+    for (int q = 0; q < RQ; ++q)
+      *reinterpret_cast<u32x4*>(wr_base + q * (64 / RCH) * RP * 16) = dr[q];
+  };
+
+  // Operand addresses: row n, chunk g*CH/2 (row-wise reads); the transpose
+  // reads of C^T start at row 4*(lane/32) + (lane%16)/4, column
+  // 16*((lane/16)%2) + 4*(lane%4). K-slot (g, e) of step st is feature
+  // g*CH*4 + 8*st + e, on both sides of S^T.
+  const unsigned char* const al_base = stage_l + (n * LP + g * (LCH / 2)) * 16;
+  const unsigned char* const ar_base = stage_r + (n * RP + g * (RCH / 2)) * 16;
+  const unsigned char* const ql_base = q_l + (n * LP + g * (LCH / 2)) * 16;
+  const unsigned char* const qr_base = q_r + (n * RP + g * (RCH / 2)) * 16;
+  const unsigned char* const tr_base =
+      stage_l + (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
+      (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  auto rd16 = [](const unsigned char* a) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
+  };
+  auto read_t = [&](int h2, int dt) {
+    const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
+    const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // Stage the query rows and synchronise the workgroup on them before the
+  // first cache loads. Once every CU streams its tiles a load queues behind
+  // megabytes of requests, and a wave stalls in issue while its CU's memory
+  // pipeline is full: a barrier after the cache loads would wait for the
+  // slowest wave to get them issued.
+#pragma unroll
+  for (int kq = 0; kq < QK; ++kq)
+    if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(smem + qdst[kq]) = qv[kq];
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < PD; ++i) load_unit(i, bl[i], br[i]);
+  constexpr int NLq = QREG ? NL : 1, NRq = QREG ? NR : 1;
+  bf16x8 qL[NT][NLq], qR[NT][NRq];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int st = 0; st < NL; ++st) qL[nt][st] = rd16(ql_base + (nt * kSub * LP + st) * 16);
+#pragma unroll
+      for (int st = 0; st < NR; ++st) qR[nt][st] = rd16(qr_base + (nt * kSub * RP + st) * 16);
+    }
+  }
+  auto qlat_op = [&](int nt, int st) {
+    if constexpr (QREG) return qL[nt][st];
+    else return rd16(ql_base + (nt * kSub * LP + st) * 16);
+  };
+  auto qrope_op = [&](int nt, int st) {
+    if constexpr (QREG) return qR[nt][st];
+    else return rd16(qr_base + (nt * kSub * RP + st) * 16);
+  };
+
+  // One staged sub-tile: scores, masking, online softmax, P.C.
+  auto compute_unit = [&](int u) {
+    const int tb = (t0 + wt + WT * (u >> 1)) * kBlock + (u & 1) * kSub;
+    // S^T[token][row] = C . Q^T; with one row tile, two accumulation chains
+    // (even latent steps; RoPE and odd latent steps) for more MFMAs in flight.
+    f32x16 sc[NT], sd[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      sc[nt] = f32x16{};
+      sd[nt] = f32x16{};
+    }
+#pragma unroll
+    for (int st = 0; st < NR; ++st) {
+      const bf16x8 a = rd16(ar_base + st * 16);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        sd[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qrope_op(nt, st), sd[nt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int st = 0; st < NL; ++st) {
+      const bf16x8 a = rd16(al_base + st * 16);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (NT == 1 && WAVES == 4 && st % 2 == 1)
+          sd[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlat_op(nt, st), sd[nt], 0, 0, 0);
+        else
+          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlat_op(nt, st), sc[nt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sc[nt] += sd[nt];
+
+    // Mask tokens past a row's visible length (only where the sub-tile
+    // reaches past the shortest row).
+    if (tb + kSub > min_vis) {  // uniform
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = tb + 8 * (r >> 2) + 4 * g + (r & 3);
+          sc[nt][r] = tok < vis[nt] ? sc[nt][r] : -INFINITY;
+        }
+    }
+
+    // Online softmax per query row against a lazily updated reference m_run:
+    // it moves (and the accumulator is rescaled) only when a row's maximum
+    // passes it by more than kLazyLog2, so probabilities stay below
+    // 2^kLazyLog2 and after the first sub-tiles the rescale is rare. Softmax
+    // is shift-invariant: the result does not depend on the reference.
+    bf16x8 pB[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nt][r]);
+      mx = wave_max_halves(mx) * p.score_scale;
+      const bool first = m_run[nt] == -INFINITY;
+      const bool grow = first ? mx > -INFINITY : mx > m_run[nt] + kLazyLog2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[nt] - mx) : 1.f;
+        m_run[nt] = grow ? mx : m_run[nt];
+        l_run[nt] *= alpha;
+        if (__builtin_amdgcn_ballot_w64(grow && !first)) {  // else the accumulator is zero
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[nt][dt] *= alpha;
+        }
+      }
+      const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
+      float sum = 0.f;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sc[nt][8 * h2 + e], p.score_scale, -m_use));
+          sum += pe;
+          pB[nt][h2][e] = (__bf16)pe;
+        }
+      l_run[nt] += sum;
+    }
+
+    // O^T[d][row] += C^T[d][t] . P^T[t][row]
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 at = read_t(h2, dt);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pB[nt][h2], acc[nt][dt], 0, 0, 0);
+      }
+  };
+  auto run_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
+    if (u < nu_w) {  // uniform; holds no global loads
+      stage_unit(u, dl, dr);
+      compute_unit(u);
+    }
+  };
+
+  // Steady state: refill each buffer right after staging it. Runs of 64
+  // tiles per wave (one register of block ids) end with PD peeled sub-tiles.
+  const int nsteps = (nu + PD - 1) / PD * PD;
+  constexpr int kChunk = 128;  // sub-tiles per register of block ids
+  static_assert(kChunk % PD == 0, "chunks hold whole pipeline rounds");
+  for (int cb = 0;;) {
+    const int ce = min(nsteps, cb + kChunk);
+    int u0 = cb;
+    for (; u0 + PD < ce; u0 += PD) {
+#pragma unroll
+      for (int i = 0; i < PD; ++i) {
+        const int u = u0 + i;
+        if (u < nu_w) stage_unit(u, bl[i], br[i]);
+        load_unit(u + PD, bl[i], br[i]);
+        if (u < nu_w) compute_unit(u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PD; ++i) run_unit(u0 + i, bl[i], br[i]);
+    cb = ce;
+    if (cb >= nsteps) break;  // uniform
+    tab = p.table[tab_base + min(t0 + wt + WT * ((cb >> 1) + lane), p.max_blocks - 1)];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) load_unit(cb + i, bl[i], br[i]);
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) l_run[nt] = wave_sum_halves(l_run[nt]);
+
+  const int64_t slot = (int64_t)s * p.spl + k;
+  if constexpr (WT == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int row = row0 + nt * kSub + n;
+      if (row >= p.rows) continue;
+      const float l = l_run[nt];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int64_t ri = (slot * NB + b) * p.rows + row;
+      float* o = p.part_o + ri * DC;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
+              f32x4{acc[nt][dt][4 * q], acc[nt][dt][4 * q + 1], acc[nt][dt][4 * q + 2],
+                    acc[nt][dt][4 * q + 3]} * inv;
+      if (g == 0) p.part_lse[ri] = l > 0.f ? (m_run[nt] + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  } else {
+    // Merge the WT token-split waves of branch b: every wave publishes
+    // (O, m, l), then wave wt merges the float4 items it = wt, wt + WT, ...
+    constexpr int REC = NT * NDT * 4 + 1;  // float4 records per lane
+    if constexpr (lay.merge_aliases) __syncthreads();  // stages and queries are free
+    f32x4* M = reinterpret_cast<f32x4*>(smem + lay.merge);
+    {
+      f32x4* my = M + wave * REC * 64;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            my[((nt * NDT + dt) * 4 + q) * 64 + lane] =
+                f32x4{acc[nt][dt][4 * q], acc[nt][dt][4 * q + 1], acc[nt][dt][4 * q + 2],
+                      acc[nt][dt][4 * q + 3]};
+      my[(REC - 1) * 64 + lane] = f32x4{m_run[0], l_run[0], NT > 1 ? m_run[NT - 1] : 0.f,
+                                        NT > 1 ? l_run[NT - 1] : 0.f};
+    }
+    __syncthreads();
+    float ms[WT][NT], ls[WT][NT];
+#pragma unroll
+    for (int w = 0; w < WT; ++w) {
+      const f32x4 ml = M[((w * NB + b) * REC + REC - 1) * 64 + lane];
+      ms[w][0] = ml[0];
+      ls[w][0] = ml[1];
+      if constexpr (NT > 1) {
+        ms[w][NT - 1] = ml[2];
+        ls[w][NT - 1] = ml[3];
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WT; ++w) mm = fmaxf(mm, ms[w][nt]);
+      const float m_use = mm == -INFINITY ? 0.f : mm;
+      float wsc[WT];
+      float l = 0.f;
+#pragma unroll
+      for (int w = 0; w < WT; ++w) {
+        wsc[w] = __builtin_amdgcn_exp2f(ms[w][nt] - m_use);
+        l += ls[w][nt] * wsc[w];
+      }
+      const int row = row0 + nt * kSub + n;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int64_t ri = (slot * NB + b) * p.rows + row;
+      if (row < p.rows) {
+        float* o = p.part_o + ri * DC;
+#pragma unroll
+        for (int it = 0; it < NDT * 4; ++it) {
+          if (it % WT != wt) continue;
+          const int dt = it / 4, q = it % 4;
+          f32x4 v = f32x4{};
+#pragma unroll
+          for (int w = 0; w < WT; ++w)
+            v += M[((w * NB + b) * REC + (nt * NDT + dt) * 4 + q) * 64 + lane] * wsc[w];
+          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
+        }
+        if (g == 0 && wt == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -910,32 +1375,63 @@ static hipError_t dispatch_dr(const SplitParams& sp, const mlra_decode_plan& pla
   return hipErrorInvalidValue;
 }
 
-template <int NB, int NT>
-static hipError_t dispatch_dc(const SplitParams& sp, const mlra_decode_plan& plan,
-                              hipStream_t st) {
-  switch (sp.DC) {
-    case 64: return dispatch_dr<NB, 64, NT>(sp, plan, st);
-    case 128: return dispatch_dr<NB, 128, NT>(sp, plan, st);
-    case 512:
-      if constexpr (NB == 1) return dispatch_dr<NB, 512, NT>(sp, plan, st);
-      return hipErrorInvalidValue;
-  }
-  return hipErrorInvalidValue;
-}
-
+// The 8-wave width-split kernel serves the 512-wide single latent.
 template <int NT>
 static hipError_t dispatch_nb(const SplitParams& sp, const mlra_decode_plan& plan,
                               hipStream_t st) {
+  if (sp.NB == 1 && sp.DC == 512) return dispatch_dr<1, 512, NT>(sp, plan, st);
+  return hipErrorInvalidValue;
+}
+
+template <int NB, int DC, int DR, int NT>
+static hipError_t launch_stream(const SplitParams& sp, const mlra_decode_plan& plan,
+                                hipStream_t stream) {
+  constexpr int W = stream_waves(NB, DC, DR, NT);
+  constexpr bool QREG = stream_qreg(NT, W);
+  auto kern = mlra_split_stream<NB, DC, DR, NT, stream_pd(NT, W), QREG, W>;
+  constexpr int lds = stream_lds(NB, DC, DR, NT, W).total;
+  static_assert(lds <= 160 * 1024, "streaming workgroup exceeds the CU's LDS");
+  if constexpr (lds > 64 * 1024) {
+    static bool attr_set = false;  // per instance; the call is idempotent
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+  }
+  const dim3 grid = sp.nrt == 1
+                       ? dim3(plan.splits_per_seq, sp.S)
+                       : dim3((uint32_t)(((int64_t)sp.S * plan.splits_per_seq + 7) / 8 * 16));
+  hipLaunchKernelGGL(kern, grid, dim3(64 * W), lds, stream, sp);
+  return hipGetLastError();
+}
+
+template <int NB, int DC, int NT>
+static hipError_t stream_dr(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
+  if (sp.DR == 64) return launch_stream<NB, DC, 64, NT>(sp, plan, st);
+  return launch_stream<NB, DC, 32, NT>(sp, plan, st);
+}
+
+template <int NB, int NT>
+static hipError_t stream_dc(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
+  if (sp.DC == 128) return stream_dr<NB, 128, NT>(sp, plan, st);
+  return stream_dr<NB, 64, NT>(sp, plan, st);
+}
+
+template <int NT>
+static hipError_t stream_nb(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
   switch (sp.NB) {
-    case 1: return dispatch_dc<1, NT>(sp, plan, st);
-    case 2: return dispatch_dc<2, NT>(sp, plan, st);
-    case 4: return dispatch_dc<4, NT>(sp, plan, st);
+    case 1: return stream_dc<1, NT>(sp, plan, st);
+    case 2: return stream_dc<2, NT>(sp, plan, st);
+    case 4: return stream_dc<4, NT>(sp, plan, st);
   }
   return hipErrorInvalidValue;
 }
 
 static hipError_t launch_split(const SplitParams& sp, const KernelShape& ks,
                                const mlra_decode_plan& plan, hipStream_t st) {
+  if (ks.variant == kVariantStreamBf16) return stream_nb<1>(sp, plan, st);
   if (ks.variant == kVariantMfmaBf16) return dispatch_nb<1>(sp, plan, st);
   dim3 grid(plan.splits_per_seq, sp.S, (sp.rows * sp.NB + 3) / 4);
   switch (sp.DC / 64) {
