@@ -102,19 +102,15 @@ KernelShape choose_shape(const Resolved& r) {
     return k;
   }
   if (r.DC <= 128) {
-    // Streaming kernel: 32 query rows per workgroup, waves split over the
-    // branches and the split's tiles.
-    k.variant = kVariantStreamBf16;
+    // Loader/compute kernel: 32 query rows per workgroup, four loader waves
+    // and four compute waves; any tile count per split (up to kPcMaxTiles).
+    k.variant = kVariantPcBf16;
     k.NT = 1;
     k.NRT = r.rows > 32 ? 2 : 1;  // 64 rows: two XCD-paired workgroups per split
     k.WD = 1;
-    const int waves = r.DC == 128 ? (r.DR == 64 ? stream_waves(r.NB, 128, 64, k.NT)
-                                                : stream_waves(r.NB, 128, 32, k.NT))
-                                  : (r.DR == 64 ? stream_waves(r.NB, 64, 64, k.NT)
-                                                : stream_waves(r.NB, 64, 32, k.NT));
-    k.WT = waves / r.NB;
-    k.NPF = stream_pd(k.NT, waves);
-    k.waves = waves;
+    k.WT = 1;
+    k.NPF = 0;
+    k.waves = 8;
     k.groups_per_cu = 1;
     return k;
   }
@@ -148,7 +144,8 @@ static int64_t choose_tiles_per_split(const Resolved& r, const KernelShape& k,
   const double fixed = 2.0 + 2.0 * partial_bytes / tile_bytes;
   const bool uniform = sum_seq_lens <= 0 || sum_seq_lens >= (int64_t)r.S * r.lcap;
   const int64_t total = uniform ? (int64_t)r.S * max_tiles : cdiv(sum_seq_lens, kBlock);
-  const int64_t top = std::max<int64_t>(cdiv(std::max<int64_t>(max_tiles, 1), k.WT) * k.WT, k.WT);
+  int64_t top = std::max<int64_t>(cdiv(std::max<int64_t>(max_tiles, 1), k.WT) * k.WT, k.WT);
+  if (k.variant == kVariantPcBf16) top = std::min<int64_t>(top, kPcMaxTiles);
   int64_t best = top;
   double best_cost = -1.0;
   for (int64_t tps = top; tps >= k.WT; tps -= k.WT) {
@@ -189,6 +186,9 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
     tps = cdiv(std::max<int64_t>(max_tiles, 1), num_splits);
     tps = std::max<int64_t>(tps, k.WT);
     tps = cdiv(tps, k.WT) * k.WT;  // every token-split wave gets the same tile count
+    // The loader/compute kernel stages a split's block ids in LDS: a request
+    // for fewer splits than that allows is raised.
+    if (k.variant == kVariantPcBf16) tps = std::min<int64_t>(tps, kPcMaxTiles);
   } else {
     tps = choose_tiles_per_split(r, k, p.target_groups, max_tiles, sum_seq_lens);
   }
@@ -200,8 +200,8 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
   p.row_groups = k.NRT;
   p.lds_bytes = k.variant == kVariantMfmaBf16
                     ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, r.DR, k.NT, k.WT, mfma_qreg(k.NT, r.DC))
-                : k.variant == kVariantStreamBf16
-                    ? stream_lds(r.NB, r.DC, r.DR, k.NT, k.waves).total
+                : k.variant == kVariantPcBf16
+                    ? pc_lds(r.NB, r.DC, r.DR).total
                     : 0;
   // Partials: output [S][spl][NB][rows][DC] and lse [S][spl][NB][rows], fp32.
   const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;

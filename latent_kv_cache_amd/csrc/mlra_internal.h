@@ -20,13 +20,11 @@ constexpr int kSub = 32;        // tokens per MFMA sub-tile (M of the 32x32 MFMA
 constexpr int mfma_wd(int DC) { return DC == 512 ? 4 : 1; }
 constexpr int mfma_waves_per_simd(int NT, int DC) { return (NT == 1 && DC != 512) ? 2 : 1; }
 // 32-token sub-tiles each wave keeps in flight in registers (48 VGPRs each at
-// DC = 128, DR = 64): a wave requests PD sub-tiles before it computes the
-// first, and refills each buffer as soon as it is staged in LDS.
-constexpr int mfma_pd(int /*NT*/, int /*DC*/) { return 2; }
-// Query rows in each wave's registers (true: 48 VGPRs at DC = 128) or read
-// from the staged copy in LDS before each MFMA (false). With two sub-tiles in
-// flight only the 512-wide latent (one wave per SIMD) has room for them.
-constexpr bool mfma_qreg(int NT, int DC) { return NT == 1 && DC == 512; }
+// DC = 128, DR = 64); a wave requests PD sub-tiles ahead of the one it computes.
+// With two row tiles a CU runs only 4 waves, so each requests two ahead.
+constexpr int mfma_pd(int NT, int DC) { return (NT == 2 && DC != 512) ? 2 : 1; }
+// Query rows in each wave's registers (true) or staged once per workgroup in LDS.
+constexpr bool mfma_qreg(int NT, int /*DC*/) { return NT == 1; }
 constexpr int mfma_wt(int NB, int DC, int NT) {
   return 4 * mfma_waves_per_simd(NT, DC) / (NB * mfma_wd(DC)) > 0
              ? 4 * mfma_waves_per_simd(NT, DC) / (NB * mfma_wd(DC))
@@ -38,47 +36,45 @@ constexpr int mfma_lpitch(int DCW) { return DCW / 8 + 2; }
 constexpr int mfma_rpitch(int DR) { return DR / 8 + 1; }
 
 enum Variant : int32_t {
-  kVariantValuFp32 = 1,    // float32 inputs: one wave per (row, branch), vector ALU
-  kVariantMfmaBf16 = 2,    // bfloat16, latent 512: 32x32x16 bf16 MFMA, waves split the width
-  kVariantStreamBf16 = 3,  // bfloat16, latent 64/128: four waves, deep per-wave prefetch
+  kVariantValuFp32 = 1,  // float32 inputs: one wave per (row, branch), vector ALU
+  kVariantMfmaBf16 = 2,  // bfloat16, latent 512: 32x32x16 bf16 MFMA, waves split the width
+  kVariantPcBf16 = 4,    // bfloat16, latent 64/128: loader waves fill an LDS ring for compute waves
 };
 
-// Streaming kernel (latent 64 or 128): 4 or 8 waves per workgroup (one or
-// two per SIMD); each keeps stream_pd(NT) sub-tiles in flight. Query rows sit
-// in registers when stream_qreg(NT), else in LDS.
-
-// LDS layout of one streaming workgroup (byte offsets):
-//   stage  [waves][32 rows][lpitch + rpitch chunks]  latent then RoPE sub-tile
-//   query  [NB][NT*32][lpitch] latent rows, then [NT*32][rpitch] RoPE rows
-//   merge  [waves][NT*DC/32*4 + 1][64 lanes] float4, when waves / NB > 1;
-//          after the stages and queries if it fits, else over them.
-struct StreamLds {
-  int32_t stage, stage_bytes, query, merge, total;
-  bool merge_aliases;
+// Loader/compute kernel: block ids of one split are staged in LDS, so a split
+// holds at most kPcMaxTiles 64-token tiles (the planner splits longer runs).
+constexpr int kPcMaxTiles = 1024;
+// LDS layout (byte offsets): ring [nslot][slot_bytes] at 0 (the staged query
+// rows, and at the end the merge records, alias it), then the block ids,
+// then the counters ready[nslot], consumed[nslot], qdone.
+struct PcLds {
+  int32_t slot_bytes, nslot, table, flags, total;
 };
-constexpr StreamLds stream_lds(int NB, int DC, int DR, int NT, int waves) {
-  const int lp = DC / 8 + 2, rp = DR / 8 + 1;
-  const int stage_bytes = kSub * (lp + rp) * 16;
-  const int query = waves * stage_bytes;
-  const int loop_end = query + (NB * NT * kSub * lp + NT * kSub * rp) * 16;
-  const int merge_bytes = (waves / NB > 1) ? waves * (NT * (DC / 32) * 4 + 1) * 64 * 16 : 0;
-  const bool fits = loop_end + merge_bytes <= 160 * 1024;
-  return StreamLds{0, stage_bytes, query, fits ? loop_end : 0,
-                   fits ? loop_end + merge_bytes : (loop_end > merge_bytes ? loop_end : merge_bytes),
-                   !fits};
+constexpr PcLds pc_lds(int NB, int DC, int DR) {
+  const int slot = (NB * kSub * (DC / 8 + 2) + kSub * (DR / 8 + 1)) * 16;
+  const int fixed = kPcMaxTiles * 4 + 256;
+  int nslot = (160 * 1024 - fixed) / slot;
+  if (nslot > 12) nslot = 12;
+  const int ring = nslot * slot;
+  const int qry = (NB * kSub * (DC / 8 + 2) + kSub * (DR / 8 + 1)) * 16;
+  const int merge = (NB < 4) ? 4 * ((DC / 32) * 4 + 1) * 64 * 16 : 0;
+  int front = ring > qry ? ring : qry;
+  front = front > merge ? front : merge;
+  return PcLds{slot, nslot, front, front + kPcMaxTiles * 4, front + fixed};
 }
-// Eight waves (two per SIMD, to hide each other's latencies) when their
-// stages, queries and merge records fit in the CU's 160 KB of LDS.
-// Two row tiles need more registers than two waves per SIMD leave.
-constexpr int stream_waves(int NB, int DC, int DR, int NT) {
-  return NT == 1 && stream_lds(NB, DC, DR, NT, 8).total <= 160 * 1024 ? 8 : 4;
+// Sub-tiles each loader keeps in flight: about kPcLoaderKB KB of loads per
+// loader (4x that per CU). A CU accepts some 32-48 KB of outstanding loads
+// before issue starts to stall; a loader stalled in issue cannot hand over
+// the slots whose data has already arrived.
+constexpr int kPcLoaderKB = 12;
+constexpr int pc_pl(int NB, int DC, int DR) {
+  const int nload = NB * (DC / 16) + DR / 16;  // 16-byte-per-lane loads per sub-tile
+  const int per = (nload + 3) / 4;
+  const int pl = (kPcLoaderKB + per - 1) / per;
+  return pl < 2 ? 2 : (pl > 12 ? 12 : pl);
 }
-// Sub-tiles in flight while a wave computes one: one at two waves per SIMD
-// (eight waves keep 96 KB per CU requested), two at one wave per SIMD.
-constexpr int stream_pd(int /*NT*/, int waves) { return waves == 8 ? 1 : 2; }
-// Query rows in registers (48 VGPRs at DC = 128) when one row tile does;
-// otherwise read from LDS per MFMA.
-constexpr bool stream_qreg(int NT, int /*waves*/) { return NT == 1; }
+
+
 
 // Dims after validation, with defaults resolved.
 struct Resolved {
@@ -117,13 +113,10 @@ constexpr bool mfma_slotted(int WD, int WT, bool qreg) { return WD == 1 && WT > 
 inline int32_t mfma_lds_bytes(int NB, int DCW, int WD, int DR, int NT, int WT, bool qreg) {
   const int waves = NB * WD * WT;
   const int lp = mfma_lpitch(DCW), rp = mfma_rpitch(DR);
-  // Register-resident queries are first staged at the start of LDS.
-  const int qstage = qreg ? (NB * WD * lp + rp) * NT * 32 * 16 : 0;
   if (mfma_slotted(WD, WT, qreg)) {
     const int stage = 32 * (lp + rp) * 16;
     const int rec = (NT * (DCW / 32) * 4 + 1) * 64 * 16;
-    const int slots = waves * (stage > rec ? stage : rec);
-    return slots > qstage ? slots : qstage;
+    return waves * (stage > rec ? stage : rec);
   }
   const int stage = waves * 32 * lp * 16 + NB * WT * 32 * rp * 16;
   const int qry = qreg ? 0 : (NB * WD * lp + rp) * NT * 32 * 16;
@@ -131,8 +124,7 @@ inline int32_t mfma_lds_bytes(int NB, int DCW, int WD, int DR, int NT, int WT, b
   const int ndt = DCW / 32;
   const int merge = (WT > 1) ? WT * NB * WD * 64 * (NT * ndt * 16 + 4) * 4 : 0;
   const int loop = stage + qry + xchg;
-  const int most = loop > merge ? loop : merge;
-  return most > qstage ? most : qstage;
+  return loop > merge ? loop : merge;
 }
 
 mlra_status resolve_dims(const mlra_decode_dims* d, int32_t n_branch, Resolved* r);

@@ -180,29 +180,24 @@ mlra_split_mfma(SplitParams p) {
   const __bf16* __restrict__ rope = static_cast<const __bf16*>(p.rope);
 
   // Independent loads first: sequence length, this wave's first 64 block ids
-  // (one per lane; any id below max_blocks lies inside the table) and the
-  // queries.
+  // (any id below max_blocks lies inside the table) and the queries.
   const int L_raw = p.seq_lens[s];
   const int64_t tab_base = (int64_t)s * p.max_blocks;
-  // Every global load in this kernel is unconditional (clamped, in-bounds
-  // addresses, results selected afterwards): the compiler then counts the
-  // outstanding loads exactly on every path and waits only for the sub-tile
-  // it needs, which keeps PD sub-tiles per wave in flight.
+  // Loads in this prologue are unconditional (clamped, in-bounds addresses,
+  // results selected afterwards) so that the compiler can count outstanding
+  // loads exactly and never waits on more than it needs.
   int tab = p.table[tab_base + min(t0 + wt + WT * lane, p.max_blocks - 1)];
+  int tab_chunk = 0;
 
-  // Query rows (the B operand of S^T = C . Q^T) are loaded once per workgroup
-  // with coalesced 16-byte loads (consecutive lanes, consecutive chunks of a
-  // row) and staged in LDS, padded like the cache tiles: latent rows per
-  // (branch, width slice), RoPE rows once (shared by all branches). Every
-  // wave loads a share first, before its cache loads, so that writing it to
-  // LDS waits only on these loads. K-slot (g, e) of step st is latent feature
-  // g*DCW/2 + 8*st + e of the slice, or RoPE feature g*DR/2 + 8*st + e.
-  // Padding rows are zero. (Loading the B operand straight from global memory
-  // would touch 64 cache lines per instruction and hold up the cache loads
-  // queued behind it in the CU's memory pipeline.)
+  // Query rows (the B operand of S^T = C . Q^T) are staged once per workgroup
+  // in LDS, padded like the cache tiles: latent rows per (branch, width
+  // slice), RoPE rows once (shared by all branches). Every wave loads a share
+  // first, before its cache loads, so that writing it to LDS waits only on
+  // these loads. K-slot (g, e) of step st is latent feature g*DCW/2 + 8*st + e
+  // of the slice, or RoPE feature g*DR/2 + 8*st + e. Padding rows are zero.
   constexpr int QL_CH = NB * WD * NT * kSub * LCH;  // latent query chunks
   constexpr int Q_CH = QL_CH + NT * kSub * RCH;     // + RoPE query chunks
-  constexpr int QK = (Q_CH + WAVES * 64 - 1) / (WAVES * 64);
+  constexpr int QK = QREG ? 0 : (Q_CH + WAVES * 64 - 1) / (WAVES * 64);
   u32x4 qv[QK > 0 ? QK : 1];
   int qdst[QK > 0 ? QK : 1];  // LDS byte offset in the query region, -1 = none
 #pragma unroll
@@ -236,10 +231,30 @@ mlra_split_mfma(SplitParams p) {
     const int row = row0 + nt * 32 + n;
     jrow[nt] = row < p.rows ? row / p.H : 0;
   }
-  // Register-resident queries (QREG): lane (n, g) holds row n's features of
-  // K-slot group g, read from the staged rows once before the token loop.
+  // Register-resident queries: lane (n, g) holds row n's features of K-slot
+  // group g (same K-slot order as the staged layout). Loaded unconditionally
+  // from a clamped row, zeroed for padding rows.
   constexpr int NLq = QREG ? NL : 1, NRq = QREG ? NR : 1;
   bf16x8 qLr[NLq], qRr[NRq];
+  if constexpr (QREG) {
+    const int row = row0 + n;
+    const bool ok = row < p.rows;
+    const int rs = ok ? row : 0;
+    const int j = rs / p.H, h = rs % p.H;
+    const int64_t head = ((int64_t)s * p.Q + j) * p.H + h;
+    const __bf16* ql = qlat + (head * NB + b) * DC + wd * DCW + g * (DCW / 2);
+    const __bf16* qr = qrop + head * DR + g * (DR / 2);
+#pragma unroll
+    for (int st = 0; st < NL; ++st) {
+      const u32x4 v = ld16(ql + 8 * st);
+      qLr[st] = __builtin_bit_cast(bf16x8, ok ? v : u32x4{});
+    }
+#pragma unroll
+    for (int st = 0; st < NR; ++st) {
+      const u32x4 v = ld16(qr + 8 * st);
+      qRr[st] = __builtin_bit_cast(bf16x8, (ok && has_rope) ? v : u32x4{});
+    }
+  }
 
   const int L = L_raw < 0 ? 0 : (L_raw > p.lcap ? p.lcap : L_raw);
   const int ntiles = (L + kBlock - 1) / kBlock;
@@ -269,13 +284,10 @@ mlra_split_mfma(SplitParams p) {
   unsigned char* const rope_base = smem + WAVES * kSub * LP * 16;
   unsigned char* stage_r = kSlotted ? stage_l + kSub * LP * 16
                                     : rope_base + (wt * NB + b) * kSub * RP * 16;
-  // Register-resident queries are staged at the start of LDS, before any
-  // cache sub-tile; a barrier separates their last read from the first stage.
-  unsigned char* const q_base = QREG ? smem : rope_base + NB * WT * kSub * RP * 16;
+  unsigned char* const q_base = rope_base + NB * WT * kSub * RP * 16;
   unsigned char* q_l = q_base + (b * WD + wd) * NT * kSub * LP * 16;
   unsigned char* q_r = q_base + NB * WD * NT * kSub * LP * 16;
-  unsigned char* const loop_end = rope_base + NB * WT * kSub * RP * 16;  // stages end here
-  float* xchg = reinterpret_cast<float*>(QREG ? loop_end : q_r + NT * kSub * RP * 16);
+  float* xchg = reinterpret_cast<float*>(QREG ? q_base : q_r + NT * kSub * RP * 16);
   f32x16 acc[NT][NDT];
   float m_run[NT], l_run[NT];
 #pragma unroll
@@ -304,7 +316,11 @@ mlra_split_mfma(SplitParams p) {
   auto load_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
     const int i = u >> 1;
     const int ti = t0 + wt + WT * i;
-    const bool valid = (u < nu) && ti < t1;  // false past this wave's tiles: block 0 is read
+    const bool valid = (u < nu) && ti < t1;
+    if ((i >> 6) != tab_chunk) {  // uniform: next 64 block ids of this wave
+      tab_chunk = i >> 6;
+      tab = p.table[tab_base + min(t0 + wt + WT * (tab_chunk * 64 + lane), p.max_blocks - 1)];
+    }
     const int phys = valid ? clamp_block(__builtin_amdgcn_readlane(tab, i & 63), p.num_blocks) : 0;
     const int sub = (u & 1) * kSub;
     // uniform base of this sub-tile (scalar registers) + 32-bit lane offset
@@ -312,12 +328,12 @@ mlra_split_mfma(SplitParams p) {
                      ((int64_t)phys * p.lsb + (int64_t)sub * p.lst + (int64_t)b * p.lsbr + wd * DCW) * 2;
 #pragma unroll
     for (int q = 0; q < LQ; ++q) dl[q] = ld16(lb + (size_t)q * l_step + l_lane);
-    // Waves without the RoPE part (WD > 1, wd > 0) load it too, unused, so
-    // that every wave issues the same loads (they hit the lines wave 0 reads).
-    const char* rbp = reinterpret_cast<const char*>(rope) +
-                      ((int64_t)phys * p.rsb + (int64_t)sub * p.rst) * 2;
+    if (has_rope) {
+      const char* rbp = reinterpret_cast<const char*>(rope) +
+                        ((int64_t)phys * p.rsb + (int64_t)sub * p.rst) * 2;
 #pragma unroll
-    for (int q = 0; q < RQ; ++q) dr[q] = ld16(rbp + (size_t)q * r_step + r_lane);
+      for (int q = 0; q < RQ; ++q) dr[q] = ld16(rbp + (size_t)q * r_step + r_lane);
+    }
   };
   auto zero_tail = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
     const int ti = t0 + wt + WT * (u >> 1);
@@ -367,31 +383,26 @@ mlra_split_mfma(SplitParams p) {
     const int tb = ti * kBlock + (u & 1) * kSub;
 
     // Operands of this sub-tile, read from LDS before the first MFMA so that
-    // their latency overlaps: A of S^T (row-wise), and, with queries in
-    // registers, the C^T operands of P.C (transpose reads; K-slot e of lane
-    // group g in half h2 is token 16*h2 + 8*(e/4) + 4*g + e%4). Otherwise
-    // the registers hold the sub-tiles in flight, and the C^T operands are
-    // read next to their MFMAs.
-    constexpr bool kEagerT = NT == 1 && QREG;
+    // their latency overlaps: A of S^T (row-wise), and the C^T operands of
+    // P.C (transpose reads; K-slot e of lane group g in half h2 is token
+    // 16*h2 + 8*(e/4) + 4*g + e%4). With two row tiles the registers are
+    // short, and the C^T operands are read next to their MFMAs instead.
+    constexpr bool kEagerT = NT == 1;
     auto read_t = [&](int h2, int dt) {
       const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
       const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // A of S^T: all of it up front with queries in registers, else one step
-    // at a time (the compiler overlaps each read with the previous MFMA).
-    auto read_a = [&](const unsigned char* base, int st) {
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + st * 16));
-    };
-    constexpr int NRe = kEagerT ? NR : 1, NLe = kEagerT ? NL : 1;
-    bf16x8 aR[NRe], aL[NLe], aT[2][NDT];
+    bf16x8 aR[NR], aL[NL], aT[2][NDT];
+    if (has_rope) {
+#pragma unroll
+      for (int st = 0; st < NR; ++st)
+        aR[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ar_base + st * 16));
+    }
+#pragma unroll
+    for (int st = 0; st < NL; ++st)
+      aL[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(al_base + st * 16));
     if constexpr (kEagerT) {
-      if (has_rope) {
-#pragma unroll
-        for (int st = 0; st < NR; ++st) aR[st] = read_a(ar_base, st);
-      }
-#pragma unroll
-      for (int st = 0; st < NL; ++st) aL[st] = read_a(al_base, st);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -411,8 +422,7 @@ mlra_split_mfma(SplitParams p) {
           if constexpr (QREG) qv = qRr[st];
           else qv = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(qr_base + (nt * kSub * RP + st) * 16));
-          const bf16x8 a = kEagerT ? aR[kEagerT ? st : 0] : read_a(ar_base, st);
-          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv, sc[nt], 0, 0, 0);
+          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qv, sc[nt], 0, 0, 0);
         }
       }
     }
@@ -424,8 +434,7 @@ mlra_split_mfma(SplitParams p) {
         if constexpr (QREG) qv = qLr[st];
         else qv = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(ql_base + (nt * kSub * LP + st) * 16));
-        const bf16x8 a = kEagerT ? aL[kEagerT ? st : 0] : read_a(al_base, st);
-        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv, sc[nt], 0, 0, 0);
+        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qv, sc[nt], 0, 0, 0);
       }
     }
 
@@ -513,57 +522,28 @@ mlra_split_mfma(SplitParams p) {
 
   // Software pipeline: PD sub-tiles in flight in registers. The wave stages
   // the oldest into LDS, refills those registers with the sub-tile PD ahead,
-  // then computes it. The steady-state loop always issues its loads (past
-  // the wave's last tile they re-read block 0) and the last PD sub-tiles of
-  // each run of 64 tiles (one register of block ids) are peeled off, so the
-  // outstanding-load count is the same on every path. The query rows are
-  // staged, and the workgroup synchronised on them, while the first
-  // sub-tiles are still in flight.
+  // then computes it. The first sub-tile is staged before the wave waits for
+  // the other waves' query rows (when those are staged in LDS).
   const int nsteps = (nu + PD - 1) / PD * PD;
 #pragma unroll
   for (int i = 0; i < PD; ++i) load_unit(i, bl[i], br[i]);
+  if constexpr (!QREG) {
 #pragma unroll
-  for (int kq = 0; kq < QK; ++kq)
-    if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(q_base + qdst[kq]) = qv[kq];
-  lds_barrier();  // every wave's share of the query rows is staged
-  if constexpr (QREG) {
-#pragma unroll
-    for (int st = 0; st < NL; ++st)
-      qLr[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ql_base + st * 16));
-#pragma unroll
-    for (int st = 0; st < NR; ++st) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qr_base + st * 16);
-      qRr[st] = __builtin_bit_cast(bf16x8, has_rope ? v : u32x4{});
-    }
-    lds_barrier();  // the query rows are read before any wave stages a sub-tile
+    for (int kq = 0; kq < QK; ++kq)
+      if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(q_base + qdst[kq]) = qv[kq];
   }
-  constexpr int kChunk = 128;  // sub-tiles per register of block ids (64 tiles)
-  static_assert(kChunk % PD == 0, "chunks hold whole pipeline rounds");
-  for (int cb = 0;;) {
-    const int ce = min(nsteps, cb + kChunk);
-    int u0 = cb;
-    for (; u0 + PD < ce; u0 += PD) {
-#pragma unroll
-      for (int i = 0; i < PD; ++i) {
-        const int u = u0 + i;
-        zero_tail(u, bl[i], br[i]);
-        stage_unit(bl[i], br[i]);
-        load_unit(u + PD, bl[i], br[i]);
-        compute_unit(u);
-      }
-    }
+  for (int u0 = 0; u0 < nsteps; u0 += PD) {
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
-      zero_tail(u0 + i, bl[i], br[i]);
+      const int u = u0 + i;
+      zero_tail(u, bl[i], br[i]);
       stage_unit(bl[i], br[i]);
-      compute_unit(u0 + i);
+      if (u + PD < nsteps) load_unit(u + PD, bl[i], br[i]);
+      if constexpr (!QREG) {
+        if (u == 0) lds_barrier();  // queries staged
+      }
+      compute_unit(u);
     }
-    cb = ce;
-    if (cb >= nsteps) break;  // uniform
-    // next 64 block ids of this wave, then the next chunk's first sub-tiles
-    tab = p.table[tab_base + min(t0 + wt + WT * ((cb >> 1) + lane), p.max_blocks - 1)];
-#pragma unroll
-    for (int i = 0; i < PD; ++i) load_unit(cb + i, bl[i], br[i]);
   }
 
 #pragma unroll
@@ -663,444 +643,369 @@ mlra_split_mfma(SplitParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 split kernel for latent widths 64 and 128 (streaming form)
+// bf16 split kernel for latent widths 64 and 128: loader and compute waves
 // ---------------------------------------------------------------------------
-// One workgroup of four waves (one per SIMD, up to 512 registers each) covers
-// one split of one sequence for every query row (NT tiles of 32 rows). Wave w
-// takes branch b = w % NB and tiles t0 + wt + WT*i of the split (wt = w / NB,
-// WT = 4 / NB); with WT > 1 the token-split waves of a branch merge their
-// (m, l, O) through LDS at the end.
+// A wave that issues loads while its CU's memory pipeline is full stalls in
+// issue, and a wave that waits for its own loads idles: both cost a wave that
+// also computes. Here the roles are split. Of the eight waves of a workgroup
+// (two per SIMD), the four loader waves stream every 32-token sub-tile of the
+// split into a ring of LDS slots, keeping PL sub-tiles each in flight in
+// registers; the four compute waves (one per SIMD) take ready slots and never
+// touch global memory in their loop. Loader l loads part l of every sub-tile
+// (every fourth of its 16-byte-per-lane load instructions, all branches and
+// the shared RoPE key once), so the RoPE key is read once per token.
 //
-// Why this shape: decode streams each cache byte once, and a wave only hides
-// HBM latency with the loads it has in flight. Each wave requests its next PD
-// 32-token sub-tiles (12 KB each at DC = 128, DR = 64) before computing the
-// first: a workgroup has 4*PD sub-tiles in flight from the start. Every global
-// load is unconditional (clamped addresses, results selected afterwards) and
-// the last PD sub-tiles of each run are peeled off, so on every path the
-// compiler waits only for the sub-tile it is about to use.
+// Slot hand-off uses two cumulative LDS counters per slot: ready (loader parts
+// written, 4 per use) and consumed (compute waves done, NB per use). A loader
+// refills slot j % NSLOT for sub-tile j only when the previous occupant was
+// consumed NB times; a compute wave reads it once it is ready 4 times. Every
+// wait is a bounded spin (it ends even if the protocol were broken, leaving
+// wrong results rather than a hung GPU).
 //
-// Per sub-tile (stage -> S^T -> softmax -> P.C), as in the 8-wave kernel: the
-// coalesced loads are written to a padded per-wave LDS stage; S^T = C . Q^T on
-// v_mfma_f32_32x32x16_bf16 with the tile rows as A (row-wise LDS reads) and
-// the query rows as B; base-2 online softmax, lane-local per query row apart
-// from one v_permlane32_swap; O^T += C^T . P^T with C^T from ds_read_b64_tr_b16
-// and P in the registers the softmax left it in.
-template <int NB, int DC, int DR, int NT, int PD, bool QREG, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
-mlra_split_stream(SplitParams p) {
-  constexpr int WT = WAVES / NB;
-  constexpr int NL = DC / 16;   // S^T k-steps over the latent
-  constexpr int NR = DR / 16;   // S^T k-steps over the RoPE key
-  constexpr int NDT = DC / 32;  // 32-wide d tiles of O^T
-  constexpr int LCH = DC / 8;   // 16-byte chunks per latent row
-  constexpr int RCH = DR / 8;
-  constexpr int LQ = kSub * LCH / 64;  // coalesced 16-byte loads per lane per sub-tile
-  constexpr int RQ = kSub * RCH / 64;
+// Compute wave c takes branch b = c % NB and sub-tiles j = c / NB + WT*i
+// (WT = 4 / NB); per sub-tile it runs S^T = C . Q^T (MFMA, A = slot rows,
+// B = query rows in registers), the online softmax, and O^T += C^T . P^T
+// (A = transpose reads of the slot). With WT > 1 the token-split compute waves
+// of a branch merge (m, l, O) through LDS at the end.
+__device__ __forceinline__ void lds_wait_geq(const int* flag, int target) {
+  // A few million polls (s_sleep 1 each) is far longer than any wait here.
+  for (int it = 0; it < (1 << 22); ++it) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ void lds_signal(int* flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+template <int NB, int DC, int DR, int NSLOT, int PL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mlra_split_pc(SplitParams p) {
+  constexpr int WT = 4 / NB;     // compute waves per branch (token streams)
+  constexpr int NL = DC / 16, NR = DR / 16, NDT = DC / 32;
+  constexpr int LCH = DC / 8, RCH = DR / 8;
+  constexpr int LQ = kSub * LCH / 64, RQ = kSub * RCH / 64;  // load instructions per sub-tile part
+  constexpr int NLOAD = NB * LQ + RQ;                        // per sub-tile
+  constexpr int P = (NLOAD + 3) / 4;                         // per loader per sub-tile
   constexpr int LP = mfma_lpitch(DC), RP = mfma_rpitch(DR);
-  constexpr int ROWS = NT * kSub;  // query rows per workgroup (padded)
-  static_assert(WAVES % NB == 0 && (WAVES == 4 || WAVES == 8), "waves split over the branches");
-  static_assert(LQ >= 1 && RQ >= 1, "bad shape");
-  constexpr StreamLds lay = stream_lds(NB, DC, DR, NT, WAVES);
+  constexpr PcLds lay = pc_lds(NB, DC, DR);
+  static_assert(lay.nslot == NSLOT && NSLOT >= 2, "slot count");
+  static_assert(lay.total <= 160 * 1024, "LDS");
+  static_assert((PL - 1) * P <= 63, "outstanding loads fit the counter");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int* const ready = reinterpret_cast<int*>(smem + lay.flags);
+  int* const consumed = ready + NSLOT;
+  int* const qdone = consumed + NSLOT;
+  int* const tabl = reinterpret_cast<int*>(smem + lay.table);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = wave % NB, wt = wave / NB;
   const int n = lane & 31, g = lane >> 5;
-  // Workgroup -> (split k, sequence s, 32-row group rt). With two row groups
-  // (64 query rows, one row tile per workgroup), ids 16c + i and 16c + 8 + i
-  // (i < 8) are the two row groups of split pair 8c + i: workgroups are dealt
-  // round-robin over the 8 XCDs, so both land on one XCD at about the same
-  // time and the second finds the tiles in that XCD's L2.
   int k, s, rt = 0;
   if (p.nrt == 1) {
     k = blockIdx.x;
     s = blockIdx.y;
-  } else {
+  } else {  // two row groups per split, XCD-paired (see the streaming kernel)
     const int id = blockIdx.x;
     const int pr = (id >> 4) * 8 + (id & 7);
-    if (pr >= p.S * p.spl) return;  // grid rounded up to 16
+    if (pr >= p.S * p.spl) return;
     rt = (id >> 3) & 1;
     s = pr / p.spl;
     k = pr % p.spl;
   }
-  const int row0 = rt * ROWS;  // first query row of this workgroup
+  const int row0 = rt * kSub;
   const int t0 = k * p.tps;
   const __bf16* __restrict__ qlat = static_cast<const __bf16*>(p.q_lat);
   const __bf16* __restrict__ qrop = static_cast<const __bf16*>(p.q_rope);
   const __bf16* __restrict__ lat = static_cast<const __bf16*>(p.lat);
   const __bf16* __restrict__ rope = static_cast<const __bf16*>(p.rope);
-  unsigned char* const stage_l = smem + lay.stage + wave * lay.stage_bytes;
-  unsigned char* const stage_r = stage_l + kSub * LP * 16;
-  unsigned char* const q_l = smem + lay.query + b * ROWS * LP * 16;  // this branch's rows
-  unsigned char* const q_r = smem + lay.query + NB * ROWS * LP * 16;
 
-  // Prologue loads, all independent: length, this wave's first 64 block ids
-  // (one per lane; any id below max_blocks lies inside the table) and the
-  // workgroup's query rows, coalesced (consecutive threads, consecutive
-  // 16-byte chunks of a row). Query rows past H*Q are zero.
+  // Prologue. Loader waves read the split's first 64 block ids into a
+  // register and issue their first PL sub-tiles at once; compute waves stage
+  // the split's block ids and the query rows (coalesced) in LDS, over the
+  // ring, and clear the counters. The first cache loads thus leave as soon as
+  // the block table arrives, not after the queries.
   const int L_raw = p.seq_lens[s];
   const int64_t tab_base = (int64_t)s * p.max_blocks;
-  int tab = p.table[tab_base + min(t0 + wt + WT * lane, p.max_blocks - 1)];
-  constexpr int QL_CH = NB * ROWS * LCH;
-  constexpr int Q_CH = QL_CH + ROWS * RCH;
-  constexpr int QK = (Q_CH + 64 * WAVES - 1) / (64 * WAVES);
-  u32x4 qv[QK];
-  int qdst[QK];
+  const bool is_loader = wave >= 4;
+  const int ld = wave & 3;
+  constexpr int LAT_B = kSub * LP * 16;  // one branch's latent rows in a slot
+  u32x4 buf[PL][P];
+  // Load instruction x of a sub-tile (x = q*4 + ld, wrapping: loaders with
+  // fewer real loads repeat one, writing the same bytes twice): branch
+  // latent x / LQ instruction x % LQ, or RoPE instruction x - NB*LQ.
+  auto issue = [&](int j, int phys, u32x4 (&d)[P]) {
+    const int sub = (j & 1) * kSub;
+    const char* lb = reinterpret_cast<const char*>(lat) + ((int64_t)phys * p.lsb + (int64_t)sub * p.lst) * 2;
+    const char* rb = reinterpret_cast<const char*>(rope) + ((int64_t)phys * p.rsb + (int64_t)sub * p.rst) * 2;
 #pragma unroll
-  for (int kq = 0; kq < QK; ++kq) {
-    const int x = kq * 64 * WAVES + threadIdx.x;
-    const bool is_lat = x < QL_CH;
-    const bool is_rope = !is_lat && x < Q_CH;
-    const int bb = x / (ROWS * LCH), rem = x % (ROWS * LCH);
-    const int rl = rem / LCH, cl = rem % LCH;
-    const int xr = is_rope ? x - QL_CH : 0;
-    const int rr = xr / RCH, cr = xr % RCH;
-    const int r = row0 + (is_lat ? rl : rr);
-    const bool live = (is_lat || is_rope) && r < p.rows;
-    const int rs = live ? r : 0;
-    const int64_t head = ((int64_t)s * p.Q + rs / p.H) * p.H + rs % p.H;
-    const __bf16* src = is_lat ? qlat + (head * NB + (is_lat ? bb : 0)) * DC + cl * 8
-                               : qrop + head * DR + cr * 8;
-    const u32x4 v = ld16(src);
-    qv[kq] = live ? v : u32x4{};
-    qdst[kq] = is_lat ? lay.query + ((bb * ROWS + rl) * LP + cl) * 16
-                      : (is_rope ? lay.query + NB * ROWS * LP * 16 + (rr * RP + cr) * 16 : -1);
-  }
-
-  const int L = L_raw < 0 ? 0 : (L_raw > p.lcap ? p.lcap : L_raw);
-  const int ntiles = (L + kBlock - 1) / kBlock;
-  if (t0 >= ntiles) return;  // uniform over the workgroup: no barrier skipped
-  const int t1 = min(t0 + p.tps, ntiles);
-  // Sub-tiles per wave: the same count for every wave of the workgroup (the
-  // extra ones of short waves are invalid and skipped).
-  const int nu = 2 * ((t1 - t0 + WT - 1) / WT);
-  const int nu_w = 2 * max(0, (t1 - t0 - wt + WT - 1) / WT);  // this wave's valid sub-tiles
-  int vis[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = row0 + nt * kSub + n;
-    const int j = row < p.rows ? row / p.H : 0;
-    vis[nt] = p.causal ? L - (p.Q - 1 - j) : L;
-  }
-  const int min_vis = p.causal ? L - (p.Q - 1) : L;
-
-  f32x16 acc[NT][NDT];
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[nt][dt] = f32x16{};
-  }
-
-  // Coalesced loads of one sub-tile: instruction q, lane -> 16-byte chunk
-  // 64*q + lane, i.e. row (64*q + lane) / CH, chunk (64*q + lane) % CH. A
-  // sub-tile past this wave's tiles reads block 0; rows past L stay inside
-  // their block and are zeroed before any arithmetic.
-  u32x4 bl[PD][LQ], br[PD][RQ];
-  const uint32_t l_lane = (uint32_t)((lane / LCH) * p.lst * 2 + (lane % LCH) * 16);
-  const uint32_t l_step = (uint32_t)((64 / LCH) * p.lst * 2);
-  const uint32_t r_lane = (uint32_t)((lane / RCH) * p.rst * 2 + (lane % RCH) * 16);
-  const uint32_t r_step = (uint32_t)((64 / RCH) * p.rst * 2);
-  auto load_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
-    const int i = u >> 1;
-    const bool valid = u < nu_w;
-    const int phys = valid ? clamp_block(__builtin_amdgcn_readlane(tab, i & 63), p.num_blocks) : 0;
-    const int sub = (u & 1) * kSub;
-    const char* lb = reinterpret_cast<const char*>(lat) +
-                     ((int64_t)phys * p.lsb + (int64_t)sub * p.lst + (int64_t)b * p.lsbr) * 2;
-    const char* rb = reinterpret_cast<const char*>(rope) +
-                     ((int64_t)phys * p.rsb + (int64_t)sub * p.rst) * 2;
-    // 32-bit offsets within the block (checked on the host): a scalar base
-    // plus one vector offset per load.
-#pragma unroll
-    for (int q = 0; q < LQ; ++q) dl[q] = ld16(lb + (uint32_t)(q * l_step + l_lane));
-#pragma unroll
-    for (int q = 0; q < RQ; ++q) dr[q] = ld16(rb + (uint32_t)(q * r_step + r_lane));
-  };
-  // Stage one sub-tile in this wave's LDS slot, rows past L zeroed.
-  unsigned char* const wl_base = stage_l + ((lane / LCH) * LP + lane % LCH) * 16;
-  unsigned char* const wr_base = stage_r + ((lane / RCH) * RP + lane % RCH) * 16;
-  auto stage_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
-    const int tok0 = (t0 + wt + WT * (u >> 1)) * kBlock + (u & 1) * kSub;
-    if (tok0 + kSub > L) {  // uniform: the sub-tile holds the sequence end
-#pragma unroll
-      for (int q = 0; q < LQ; ++q)
-        dl[q] = tok0 + (q * 64 + lane) / LCH < L ? dl[q] : u32x4{};
-#pragma unroll
-      for (int q = 0; q < RQ; ++q)
-        dr[q] = tok0 + (q * 64 + lane) / RCH < L ? dr[q] : u32x4{};
+    for (int q = 0; q < P; ++q) {
+      const int x = (q * 4 + ld) % NLOAD;
+      const bool isl = x < NB * LQ;
+      const int bb = isl ? x / LQ : 0, ql = isl ? x % LQ : x - NB * LQ;
+      const uint32_t off = isl ? (uint32_t)(bb * p.lsbr * 2 + (ql * (64 / LCH) + lane / LCH) * p.lst * 2 + (lane % LCH) * 16)
+                               : (uint32_t)((ql * (64 / RCH) + lane / RCH) * p.rst * 2 + (lane % RCH) * 16);
+      d[q] = ld16((isl ? lb : rb) + off);
     }
-#pragma unroll
-    for (int q = 0; q < LQ; ++q)
-      *reinterpret_cast<u32x4*>(wl_base + q * (64 / LCH) * LP * 16) = dl[q];
-#pragma unroll
-    for (int q = 0; q < RQ; ++q)
-      *reinterpret_cast<u32x4*>(wr_base + q * (64 / RCH) * RP * 16) = dr[q];
   };
-
-  // Operand addresses: row n, chunk g*CH/2 (row-wise reads); the transpose
-  // reads of C^T start at row 4*(lane/32) + (lane%16)/4, column
-  // 16*((lane/16)%2) + 4*(lane%4). K-slot (g, e) of step st is feature
-  // g*CH*4 + 8*st + e, on both sides of S^T.
-  const unsigned char* const al_base = stage_l + (n * LP + g * (LCH / 2)) * 16;
-  const unsigned char* const ar_base = stage_r + (n * RP + g * (RCH / 2)) * 16;
-  const unsigned char* const ql_base = q_l + (n * LP + g * (LCH / 2)) * 16;
-  const unsigned char* const qr_base = q_r + (n * RP + g * (RCH / 2)) * 16;
-  const unsigned char* const tr_base =
-      stage_l + (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
-      (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-  auto rd16 = [](const unsigned char* a) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
+  int L, nsub;
+  auto sizes = [&]() {
+    L = L_raw < 0 ? 0 : (L_raw > p.lcap ? p.lcap : L_raw);
+    const int ntiles = (L + kBlock - 1) / kBlock;
+    nsub = t0 >= ntiles ? 0 : 2 * (min(t0 + p.tps, ntiles) - t0);  // sub-tiles of this split
   };
-  auto read_t = [&](int h2, int dt) {
-    const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
-    const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-
-  // Stage the query rows and synchronise the workgroup on them before the
-  // first cache loads. Once every CU streams its tiles a load queues behind
-  // megabytes of requests, and a wave stalls in issue while its CU's memory
-  // pipeline is full: a barrier after the cache loads would wait for the
-  // slowest wave to get them issued.
+  f32x16 acc[NDT];
+  float m_run = -INFINITY, l_run = 0.f;
+  const int b = wave % NB;          // compute waves: branch
+  const int strm = (wave % 4) / NB;  // compute waves: token stream
+  // Each role synchronises once with the other (s_barrier counts waves)
+  // inside its own branch, so no register of one role is live in the other.
+  if (is_loader) {
+    const int tab0 = p.table[tab_base + min(t0 + lane, p.max_blocks - 1)];
+    sizes();
+    if (nsub == 0) return;  // uniform over the workgroup
 #pragma unroll
-  for (int kq = 0; kq < QK; ++kq)
-    if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(smem + qdst[kq]) = qv[kq];
-  lds_barrier();
-#pragma unroll
-  for (int i = 0; i < PD; ++i) load_unit(i, bl[i], br[i]);
-  constexpr int NLq = QREG ? NL : 1, NRq = QREG ? NR : 1;
-  bf16x8 qL[NT][NLq], qR[NT][NRq];
-  if constexpr (QREG) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int st = 0; st < NL; ++st) qL[nt][st] = rd16(ql_base + (nt * kSub * LP + st) * 16);
-#pragma unroll
-      for (int st = 0; st < NR; ++st) qR[nt][st] = rd16(qr_base + (nt * kSub * RP + st) * 16);
+    for (int i = 0; i < PL; ++i) {
+      const int phys = i < nsub ? clamp_block(__builtin_amdgcn_readlane(tab0, (i >> 1) & 63), p.num_blocks) : 0;
+      issue(i, phys, buf[i]);
     }
-  }
-  auto qlat_op = [&](int nt, int st) {
-    if constexpr (QREG) return qL[nt][st];
-    else return rd16(ql_base + (nt * kSub * LP + st) * 16);
-  };
-  auto qrope_op = [&](int nt, int st) {
-    if constexpr (QREG) return qR[nt][st];
-    else return rd16(qr_base + (nt * kSub * RP + st) * 16);
-  };
-
-  // One staged sub-tile: scores, masking, online softmax, P.C.
-  auto compute_unit = [&](int u) {
-    const int tb = (t0 + wt + WT * (u >> 1)) * kBlock + (u & 1) * kSub;
-    // S^T[token][row] = C . Q^T; with one row tile, two accumulation chains
-    // (even latent steps; RoPE and odd latent steps) for more MFMAs in flight.
-    f32x16 sc[NT], sd[NT];
+    lds_barrier();
+    // ---------------- loader ----------------
+    auto write = [&](int j, u32x4 (&d)[P]) {
+      const int slot = j % NSLOT;
+      lds_wait_geq(consumed + slot, (j / NSLOT) * NB);  // previous occupant done
+      unsigned char* sb = smem + slot * lay.slot_bytes;
+      const int tok0 = (t0 + (j >> 1)) * kBlock + (j & 1) * kSub;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      sc[nt] = f32x16{};
-      sd[nt] = f32x16{};
-    }
+      for (int q = 0; q < P; ++q) {
+        const int x = (q * 4 + ld) % NLOAD;
+        const bool isl = x < NB * LQ;
+        const int bb = isl ? x / LQ : 0, ql = isl ? x % LQ : x - NB * LQ;
+        const int row = isl ? ql * (64 / LCH) + lane / LCH : ql * (64 / RCH) + lane / RCH;
+        const int dst = isl ? bb * LAT_B + (row * LP + lane % LCH) * 16
+                            : NB * LAT_B + (row * RP + lane % RCH) * 16;
+        *reinterpret_cast<u32x4*>(sb + dst) = tok0 + row < L ? d[q] : u32x4{};
+      }
+      lds_signal(ready + slot);
+    };
+    const int nsteps = (nsub + PL - 1) / PL * PL;
+    lds_wait_geq(qdone, 4);  // the ring aliases the staged query rows
+    int j0 = 0;
+    for (; j0 + PL < nsteps; j0 += PL) {  // every sub-tile here is < nsub
 #pragma unroll
-    for (int st = 0; st < NR; ++st) {
-      const bf16x8 a = rd16(ar_base + st * 16);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        sd[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qrope_op(nt, st), sd[nt], 0, 0, 0);
-    }
-#pragma unroll
-    for (int st = 0; st < NL; ++st) {
-      const bf16x8 a = rd16(al_base + st * 16);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (NT == 1 && WAVES == 4 && st % 2 == 1)
-          sd[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlat_op(nt, st), sd[nt], 0, 0, 0);
-        else
-          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlat_op(nt, st), sc[nt], 0, 0, 0);
+      for (int i = 0; i < PL; ++i) {
+        const int j = j0 + i + PL;
+        write(j0 + i, buf[i]);
+        issue(j, j < nsub ? tabl[min(j >> 1, kPcMaxTiles - 1)] : 0, buf[i]);
       }
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sc[nt] += sd[nt];
-
-    // Mask tokens past a row's visible length (only where the sub-tile
-    // reaches past the shortest row).
-    if (tb + kSub > min_vis) {  // uniform
+    for (int i = 0; i < PL; ++i)
+      if (j0 + i < nsub) write(j0 + i, buf[i]);
+  } else {
+    constexpr int TK = (kPcMaxTiles + 255) / 256;
+    int tv[TK];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+    for (int kt = 0; kt < TK; ++kt)
+      tv[kt] = p.table[tab_base + min(t0 + kt * 256 + (int)threadIdx.x, p.max_blocks - 1)];
+    constexpr int QL_CH = NB * kSub * LCH;
+    constexpr int Q_CH = QL_CH + kSub * RCH;
+    constexpr int QK = (Q_CH + 255) / 256;
+    u32x4 qv[QK];
+    int qdst[QK];
+#pragma unroll
+    for (int kq = 0; kq < QK; ++kq) {
+      const int x = kq * 256 + threadIdx.x;
+      const bool is_lat = x < QL_CH;
+      const bool is_rope = !is_lat && x < Q_CH;
+      const int bb = x / (kSub * LCH), rem = x % (kSub * LCH);
+      const int rl = rem / LCH, cl = rem % LCH;
+      const int xr = is_rope ? x - QL_CH : 0;
+      const int rr = xr / RCH, cr = xr % RCH;
+      const int r = row0 + (is_lat ? rl : rr);
+      const bool live = (is_lat || is_rope) && r < p.rows;
+      const int rs = live ? r : 0;
+      const int64_t head = ((int64_t)s * p.Q + rs / p.H) * p.H + rs % p.H;
+      const __bf16* src = is_lat ? qlat + (head * NB + (is_lat ? bb : 0)) * DC + cl * 8
+                                 : qrop + head * DR + cr * 8;
+      const u32x4 v = ld16(src);
+      qv[kq] = live ? v : u32x4{};
+      qdst[kq] = is_lat ? ((bb * kSub + rl) * LP + cl) * 16
+                        : (is_rope ? NB * kSub * LP * 16 + (rr * RP + cr) * 16 : -1);
+    }
+    sizes();
+    if (nsub == 0) return;  // uniform over the workgroup
+#pragma unroll
+    for (int kt = 0; kt < TK; ++kt) tabl[kt * 256 + threadIdx.x] = clamp_block(tv[kt], p.num_blocks);
+#pragma unroll
+    for (int kq = 0; kq < QK; ++kq)
+      if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(smem + qdst[kq]) = qv[kq];
+    if (threadIdx.x < 2 * NSLOT + 1) ready[threadIdx.x] = 0;  // ready, consumed, qdone
+    lds_barrier();
+    // ---------------- compute ----------------
+    const unsigned char* const qb = smem + b * kSub * LP * 16 + (n * LP + g * (LCH / 2)) * 16;
+    const unsigned char* const qrb = smem + NB * kSub * LP * 16 + (n * RP + g * (RCH / 2)) * 16;
+    auto rd16 = [](const unsigned char* a) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
+    };
+    bf16x8 qL[NL], qR[NR];
+#pragma unroll
+    for (int st = 0; st < NL; ++st) qL[st] = rd16(qb + st * 16);
+#pragma unroll
+    for (int st = 0; st < NR; ++st) qR[st] = rd16(qrb + st * 16);
+    lds_signal(qdone);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+    const int row = row0 + n;
+    const int jr = row < p.rows ? row / p.H : 0;
+    const int vis = p.causal ? L - (p.Q - 1 - jr) : L;
+    const int min_vis = p.causal ? L - (p.Q - 1) : L;
+    const int a_l = (n * LP + g * (LCH / 2)) * 16 + b * LAT_B;  // S^T A operand, row n
+    const int a_r = (n * RP + g * (RCH / 2)) * 16 + NB * LAT_B;
+    const int a_t = b * LAT_B + (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
+                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    for (int j = strm; j < nsub; j += WT) {
+      const int slot = j % NSLOT;
+      lds_wait_geq(ready + slot, (j / NSLOT + 1) * 4);
+      const unsigned char* sb = smem + slot * lay.slot_bytes;
+      const int tb = (t0 + (j >> 1)) * kBlock + (j & 1) * kSub;
+      f32x16 sc = f32x16{}, sd = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NR; ++st)
+        sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(sb + a_r + st * 16), qR[st], sd, 0, 0, 0);
+#pragma unroll
+      for (int st = 0; st < NL; ++st) {
+        if (st % 2 == 0)
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(sb + a_l + st * 16), qL[st], sc, 0, 0, 0);
+        else
+          sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(sb + a_l + st * 16), qL[st], sd, 0, 0, 0);
+      }
+      // C^T operands of P.C (transpose reads), issued before the softmax
+      bf16x8 aT[2][NDT];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const i16x4 lo = lds_read_tr(sb + a_t + (16 * h2) * LP * 16 + dt * 64);
+          const i16x4 hi = lds_read_tr(sb + a_t + (16 * h2 + 8) * LP * 16 + dt * 64);
+          aT[h2][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      // every read of the slot is issued: hand it back once they complete
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      lds_signal(consumed + slot);
+      sc += sd;
+      if (tb + kSub > min_vis) {  // uniform
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int tok = tb + 8 * (r >> 2) + 4 * g + (r & 3);
-          sc[nt][r] = tok < vis[nt] ? sc[nt][r] : -INFINITY;
-        }
-    }
-
-    // Online softmax per query row against a lazily updated reference m_run:
-    // it moves (and the accumulator is rescaled) only when a row's maximum
-    // passes it by more than kLazyLog2, so probabilities stay below
-    // 2^kLazyLog2 and after the first sub-tiles the rescale is rare. Softmax
-    // is shift-invariant: the result does not depend on the reference.
-    bf16x8 pB[NT][2];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nt][r]);
-      mx = wave_max_halves(mx) * p.score_scale;
-      const bool first = m_run[nt] == -INFINITY;
-      const bool grow = first ? mx > -INFINITY : mx > m_run[nt] + kLazyLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[nt] - mx) : 1.f;
-        m_run[nt] = grow ? mx : m_run[nt];
-        l_run[nt] *= alpha;
-        if (__builtin_amdgcn_ballot_w64(grow && !first)) {  // else the accumulator is zero
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) acc[nt][dt] *= alpha;
+          sc[r] = tok < vis ? sc[r] : -INFINITY;
         }
       }
-      const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
+      // online softmax against a lazily updated reference (see the streaming kernel)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      mx = wave_max_halves(mx) * p.score_scale;
+      const bool first = m_run == -INFINITY;
+      const bool grow = first ? mx > -INFINITY : mx > m_run + kLazyLog2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+        m_run = grow ? mx : m_run;
+        l_run *= alpha;
+        if (__builtin_amdgcn_ballot_w64(grow && !first)) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        }
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      bf16x8 pB[2];
       float sum = 0.f;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(sc[nt][8 * h2 + e], p.score_scale, -m_use));
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sc[8 * h2 + e], p.score_scale, -m_use));
           sum += pe;
-          pB[nt][h2][e] = (__bf16)pe;
+          pB[h2][e] = (__bf16)pe;
         }
-      l_run[nt] += sum;
+      l_run += sum;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aT[h2][dt], pB[h2], acc[dt], 0, 0, 0);
     }
-
-    // O^T[d][row] += C^T[d][t] . P^T[t][row]
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8 at = read_t(h2, dt);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pB[nt][h2], acc[nt][dt], 0, 0, 0);
-      }
-  };
-  auto run_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
-    if (u < nu_w) {  // uniform; holds no global loads
-      stage_unit(u, dl, dr);
-      compute_unit(u);
-    }
-  };
-
-  // Steady state: refill each buffer right after staging it. Runs of 64
-  // tiles per wave (one register of block ids) end with PD peeled sub-tiles.
-  const int nsteps = (nu + PD - 1) / PD * PD;
-  constexpr int kChunk = 128;  // sub-tiles per register of block ids
-  static_assert(kChunk % PD == 0, "chunks hold whole pipeline rounds");
-  for (int cb = 0;;) {
-    const int ce = min(nsteps, cb + kChunk);
-    int u0 = cb;
-    for (; u0 + PD < ce; u0 += PD) {
-#pragma unroll
-      for (int i = 0; i < PD; ++i) {
-        const int u = u0 + i;
-        if (u < nu_w) stage_unit(u, bl[i], br[i]);
-        load_unit(u + PD, bl[i], br[i]);
-        if (u < nu_w) compute_unit(u);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PD; ++i) run_unit(u0 + i, bl[i], br[i]);
-    cb = ce;
-    if (cb >= nsteps) break;  // uniform
-    tab = p.table[tab_base + min(t0 + wt + WT * ((cb >> 1) + lane), p.max_blocks - 1)];
-#pragma unroll
-    for (int i = 0; i < PD; ++i) load_unit(cb + i, bl[i], br[i]);
+    l_run = wave_sum_halves(l_run);
   }
 
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) l_run[nt] = wave_sum_halves(l_run[nt]);
-
-  const int64_t slot = (int64_t)s * p.spl + k;
+  const int64_t slotp = (int64_t)s * p.spl + k;
   if constexpr (WT == 1) {
+    if (wave >= 4) return;
+    const int row = row0 + n;
+    if (row >= p.rows) return;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const int64_t ri = (slotp * NB + b) * p.rows + row;
+    float* o = p.part_o + ri * DC;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int row = row0 + nt * kSub + n;
-      if (row >= p.rows) continue;
-      const float l = l_run[nt];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int64_t ri = (slot * NB + b) * p.rows + row;
-      float* o = p.part_o + ri * DC;
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
+            f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} * inv;
+    if (g == 0) p.part_lse[ri] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+  } else {
+    // Merge the WT token streams of each branch: records over the ring.
+    constexpr int REC = NDT * 4 + 1;
+    __syncthreads();  // every slot is consumed and no loader writes any more
+    f32x4* M = reinterpret_cast<f32x4*>(smem);
+    if (wave < 4) {
+      f32x4* my = M + wave * REC * 64;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
-              f32x4{acc[nt][dt][4 * q], acc[nt][dt][4 * q + 1], acc[nt][dt][4 * q + 2],
-                    acc[nt][dt][4 * q + 3]} * inv;
-      if (g == 0) p.part_lse[ri] = l > 0.f ? (m_run[nt] + __log2f(l)) * kLn2 : -INFINITY;
-    }
-  } else {
-    // Merge the WT token-split waves of branch b: every wave publishes
-    // (O, m, l), then wave wt merges the float4 items it = wt, wt + WT, ...
-    constexpr int REC = NT * NDT * 4 + 1;  // float4 records per lane
-    if constexpr (lay.merge_aliases) __syncthreads();  // stages and queries are free
-    f32x4* M = reinterpret_cast<f32x4*>(smem + lay.merge);
-    {
-      f32x4* my = M + wave * REC * 64;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            my[((nt * NDT + dt) * 4 + q) * 64 + lane] =
-                f32x4{acc[nt][dt][4 * q], acc[nt][dt][4 * q + 1], acc[nt][dt][4 * q + 2],
-                      acc[nt][dt][4 * q + 3]};
-      my[(REC - 1) * 64 + lane] = f32x4{m_run[0], l_run[0], NT > 1 ? m_run[NT - 1] : 0.f,
-                                        NT > 1 ? l_run[NT - 1] : 0.f};
+          my[(dt * 4 + q) * 64 + lane] =
+              f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]};
+      my[(REC - 1) * 64 + lane] = f32x4{m_run, l_run, 0.f, 0.f};
     }
     __syncthreads();
-    float ms[WT][NT], ls[WT][NT];
+    if (wave >= 4) return;
+    float ms[WT], ls[WT];
 #pragma unroll
     for (int w = 0; w < WT; ++w) {
       const f32x4 ml = M[((w * NB + b) * REC + REC - 1) * 64 + lane];
-      ms[w][0] = ml[0];
-      ls[w][0] = ml[1];
-      if constexpr (NT > 1) {
-        ms[w][NT - 1] = ml[2];
-        ls[w][NT - 1] = ml[3];
-      }
+      ms[w] = ml[0];
+      ls[w] = ml[1];
     }
+    float mm = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mm = -INFINITY;
+    for (int w = 0; w < WT; ++w) mm = fmaxf(mm, ms[w]);
+    const float m_use = mm == -INFINITY ? 0.f : mm;
+    float wsc[WT];
+    float l = 0.f;
 #pragma unroll
-      for (int w = 0; w < WT; ++w) mm = fmaxf(mm, ms[w][nt]);
-      const float m_use = mm == -INFINITY ? 0.f : mm;
-      float wsc[WT];
-      float l = 0.f;
-#pragma unroll
-      for (int w = 0; w < WT; ++w) {
-        wsc[w] = __builtin_amdgcn_exp2f(ms[w][nt] - m_use);
-        l += ls[w][nt] * wsc[w];
-      }
-      const int row = row0 + nt * kSub + n;
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int64_t ri = (slot * NB + b) * p.rows + row;
-      if (row < p.rows) {
-        float* o = p.part_o + ri * DC;
-#pragma unroll
-        for (int it = 0; it < NDT * 4; ++it) {
-          if (it % WT != wt) continue;
-          const int dt = it / 4, q = it % 4;
-          f32x4 v = f32x4{};
-#pragma unroll
-          for (int w = 0; w < WT; ++w)
-            v += M[((w * NB + b) * REC + (nt * NDT + dt) * 4 + q) * 64 + lane] * wsc[w];
-          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
-        }
-        if (g == 0 && wt == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
-      }
+    for (int w = 0; w < WT; ++w) {
+      wsc[w] = __builtin_amdgcn_exp2f(ms[w] - m_use);
+      l += ls[w] * wsc[w];
     }
+    const int row = row0 + n;
+    if (row >= p.rows) return;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t ri = (slotp * NB + b) * p.rows + row;
+    float* o = p.part_o + ri * DC;
+#pragma unroll
+    for (int it = 0; it < NDT * 4; ++it) {
+      if (it % WT != strm) continue;
+      const int dt = it / 4, q = it % 4;
+      f32x4 v = f32x4{};
+#pragma unroll
+      for (int w = 0; w < WT; ++w) v += M[((w * NB + b) * REC + dt * 4 + q) * 64 + lane] * wsc[w];
+      *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
+    }
+    if (g == 0 && strm == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -1383,55 +1288,49 @@ static hipError_t dispatch_nb(const SplitParams& sp, const mlra_decode_plan& pla
   return hipErrorInvalidValue;
 }
 
-template <int NB, int DC, int DR, int NT>
-static hipError_t launch_stream(const SplitParams& sp, const mlra_decode_plan& plan,
-                                hipStream_t stream) {
-  constexpr int W = stream_waves(NB, DC, DR, NT);
-  constexpr bool QREG = stream_qreg(NT, W);
-  auto kern = mlra_split_stream<NB, DC, DR, NT, stream_pd(NT, W), QREG, W>;
-  constexpr int lds = stream_lds(NB, DC, DR, NT, W).total;
-  static_assert(lds <= 160 * 1024, "streaming workgroup exceeds the CU's LDS");
-  if constexpr (lds > 64 * 1024) {
-    static bool attr_set = false;  // per instance; the call is idempotent
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+template <int NB, int DC, int DR>
+static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
+                            hipStream_t stream) {
+  constexpr PcLds lay = pc_lds(NB, DC, DR);
+  auto kern = mlra_split_pc<NB, DC, DR, lay.nslot, pc_pl(NB, DC, DR)>;
+  static bool attr_set = false;  // per instance; the call is idempotent
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
+    if (e != hipSuccess) return e;
+    attr_set = true;
   }
   const dim3 grid = sp.nrt == 1
                        ? dim3(plan.splits_per_seq, sp.S)
                        : dim3((uint32_t)(((int64_t)sp.S * plan.splits_per_seq + 7) / 8 * 16));
-  hipLaunchKernelGGL(kern, grid, dim3(64 * W), lds, stream, sp);
+  hipLaunchKernelGGL(kern, grid, dim3(512), lay.total, stream, sp);
   return hipGetLastError();
 }
 
-template <int NB, int DC, int NT>
-static hipError_t stream_dr(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
-  if (sp.DR == 64) return launch_stream<NB, DC, 64, NT>(sp, plan, st);
-  return launch_stream<NB, DC, 32, NT>(sp, plan, st);
+template <int NB, int DC>
+static hipError_t pc_dr(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
+  if (sp.DR == 64) return launch_pc<NB, DC, 64>(sp, plan, st);
+  return launch_pc<NB, DC, 32>(sp, plan, st);
 }
 
-template <int NB, int NT>
-static hipError_t stream_dc(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
-  if (sp.DC == 128) return stream_dr<NB, 128, NT>(sp, plan, st);
-  return stream_dr<NB, 64, NT>(sp, plan, st);
+template <int NB>
+static hipError_t pc_dc(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
+  if (sp.DC == 128) return pc_dr<NB, 128>(sp, plan, st);
+  return pc_dr<NB, 64>(sp, plan, st);
 }
 
-template <int NT>
-static hipError_t stream_nb(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
+static hipError_t pc_nb(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
   switch (sp.NB) {
-    case 1: return stream_dc<1, NT>(sp, plan, st);
-    case 2: return stream_dc<2, NT>(sp, plan, st);
-    case 4: return stream_dc<4, NT>(sp, plan, st);
+    case 1: return pc_dc<1>(sp, plan, st);
+    case 2: return pc_dc<2>(sp, plan, st);
+    case 4: return pc_dc<4>(sp, plan, st);
   }
   return hipErrorInvalidValue;
 }
 
 static hipError_t launch_split(const SplitParams& sp, const KernelShape& ks,
                                const mlra_decode_plan& plan, hipStream_t st) {
-  if (ks.variant == kVariantStreamBf16) return stream_nb<1>(sp, plan, st);
+  if (ks.variant == kVariantPcBf16) return pc_nb(sp, plan, st);
   if (ks.variant == kVariantMfmaBf16) return dispatch_nb<1>(sp, plan, st);
   dim3 grid(plan.splits_per_seq, sp.S, (sp.rows * sp.NB + 3) / 4);
   switch (sp.DC / 64) {

@@ -1,0 +1,60 @@
+"""Compile-time resource checks of the HIP kernels (CPU only: hipcc cross-compiles gfx950).
+
+The split kernels keep several 32-token sub-tiles of loads in flight per wave
+and wait for each with a partial vector-memory count; a register spill would
+add scratch loads to that count and serialise the pipeline. Every kernel must
+therefore compile without spills, and the loader/compute kernel must fit two
+waves per SIMD (at most 256 VGPRs).
+"""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+from latent_kv_cache_amd import build
+
+pytestmark = pytest.mark.skipif(shutil.which(build.hipcc()) is None and not os.path.exists(build.hipcc()),
+                                reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def remarks():
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [build.hipcc(), *build.HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+               os.path.join(build.CSRC, "mlra_kernels.hip"), "-o", os.path.join(tmp, "k.o")]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-2000:]
+        text = res.stdout + res.stderr
+    kernels = {}
+    name = None
+    for line in text.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            kernels[name] = {}
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|VGPRs Spill|SGPRs Spill|Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and name:
+            kernels[name][m.group(1)] = int(m.group(2))
+    return kernels
+
+
+def test_every_kernel_is_reported(remarks):
+    names = " ".join(remarks)
+    for kern in ("mlra_split_pc", "mlra_split_mfma", "mlra_split_valu", "mlra_combine"):
+        assert kern in names
+
+
+def test_no_kernel_spills(remarks):
+    spilled = {k: v for k, v in remarks.items() if v.get("VGPRs Spill", 0) or v.get("SGPRs Spill", 0)}
+    assert not spilled, spilled
+
+
+def test_loader_compute_kernel_runs_two_waves_per_simd(remarks):
+    pc = {k: v for k, v in remarks.items() if "mlra_split_pc" in k}
+    assert pc
+    for k, v in pc.items():
+        assert v["VGPRs"] + v.get("AGPRs", 0) <= 256, (k, v)
