@@ -62,11 +62,15 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+# Split kernel that serves each plan.kernel_variant (include/mlra.h).
+SPLIT_KERNELS = {1: "mlra_split_valu", 2: "mlra_split_mfma", 4: "mlra_split_pc"}
+
+
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per split-kernel launch from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
     when there is none for this workload or the kernel source has changed."""
-    path = os.path.join(ROOT, "profiles", f"mlra_split_mfma_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -259,7 +263,8 @@ def main() -> int:
     torch.cuda.synchronize()
     per_step = sorted(a.elapsed_time(b) for a, b in evs)
     med_ms = per_step[len(per_step) // 2]
-    traffic = measured_traffic(cfg.name)
+    split_kernel = SPLIT_KERNELS.get(plan.kernel_variant, f"variant{plan.kernel_variant}")
+    traffic = measured_traffic(split_kernel, cfg.name)
 
     gbs = ab["total"] / (ms * 1e-3) / 1e9
     res = {
@@ -288,7 +293,7 @@ def main() -> int:
         "kernels": {"split_avg_us": round(split_avg * 1e3, 3),
                     "combine_avg_us": round(comb_avg * 1e3, 3),
                     "split_algorithmic_bytes": split_bytes},
-        "roofline": {"bound": "hbm", "kernel": "mlra_split_mfma" if cfg.dtype == "bf16" else "mlra_split_valu", "achieved": round(split_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": split_kernel, "achieved": round(split_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
     }

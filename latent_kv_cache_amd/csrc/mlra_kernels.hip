@@ -791,15 +791,19 @@ mlra_split_pc(SplitParams p) {
       }
       lds_signal(ready + slot);
     };
-    const int nsteps = (nsub + PL - 1) / PL * PL;
+    auto phys_of = [&](int j) { return j < nsub ? tabl[min(j >> 1, kPcMaxTiles - 1)] : 0; };
     lds_wait_geq(qdone, 4);  // the ring aliases the staged query rows
+    // Steady state: write j, issue j + PL into the same registers (every
+    // written sub-tile here is < nsub); then the last PL without new loads.
+    // (Issuing fewer sub-tiles first and ramping up to PL was measured
+    // slower: the memory system is best fed from the start.)
     int j0 = 0;
-    for (; j0 + PL < nsteps; j0 += PL) {  // every sub-tile here is < nsub
+    for (; j0 + PL < nsub; j0 += PL) {
 #pragma unroll
       for (int i = 0; i < PL; ++i) {
-        const int j = j0 + i + PL;
-        write(j0 + i, buf[i]);
-        issue(j, j < nsub ? tabl[min(j >> 1, kPcMaxTiles - 1)] : 0, buf[i]);
+        const int j = j0 + i;
+        write(j, buf[i]);
+        issue(j + PL, phys_of(j + PL), buf[i]);
       }
     }
 #pragma unroll
@@ -1292,7 +1296,8 @@ template <int NB, int DC, int DR>
 static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
                             hipStream_t stream) {
   constexpr PcLds lay = pc_lds(NB, DC, DR);
-  auto kern = mlra_split_pc<NB, DC, DR, lay.nslot, pc_pl(NB, DC, DR)>;
+  constexpr int PL = pc_pl(NB, DC, DR);
+  auto kern = mlra_split_pc<NB, DC, DR, lay.nslot, PL>;
   static bool attr_set = false;  // per instance; the call is idempotent
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
