@@ -45,22 +45,24 @@ enum Variant : int32_t {
 // holds at most kPcMaxTiles 64-token tiles (the planner splits longer runs).
 constexpr int kPcMaxTiles = 1024;
 // LDS layout (byte offsets): ring [nslot][slot_bytes] at 0 (the staged query
-// rows, and at the end the merge records, alias it), then the block ids,
-// then the counters ready[nslot], consumed[nslot], qdone.
+// rows alias it), then the merge records of the token streams that finish
+// before the last one of their branch (NB * (4/NB - 1) records of
+// (DC/32 * 4 + 1) x 64 x 16 bytes; none with four branches), then the block
+// ids, then the counters ready[nslot], consumed[nslot], qdone, arrived[NB],
+// recorded[NB].
 struct PcLds {
-  int32_t slot_bytes, nslot, table, flags, total;
+  int32_t slot_bytes, nslot, merge, table, flags, total;
 };
 constexpr PcLds pc_lds(int NB, int DC, int DR) {
   const int slot = (NB * kSub * (DC / 8 + 2) + kSub * (DR / 8 + 1)) * 16;
   const int fixed = kPcMaxTiles * 4 + 256;
-  int nslot = (160 * 1024 - fixed) / slot;
+  const int rec = NB * (4 / NB - 1) * ((DC / 32) * 4 + 1) * 64 * 16;
+  int nslot = (160 * 1024 - fixed - rec) / slot;
   if (nslot > 12) nslot = 12;
   const int ring = nslot * slot;
-  const int qry = (NB * kSub * (DC / 8 + 2) + kSub * (DR / 8 + 1)) * 16;
-  const int merge = (NB < 4) ? 4 * ((DC / 32) * 4 + 1) * 64 * 16 : 0;
-  int front = ring > qry ? ring : qry;
-  front = front > merge ? front : merge;
-  return PcLds{slot, nslot, front, front + kPcMaxTiles * 4, front + fixed};
+  const int qry = slot;  // the query rows use one slot's layout
+  const int front = ring > qry ? ring : qry;
+  return PcLds{slot, nslot, front, front + rec, front + rec + kPcMaxTiles * 4, front + rec + fixed};
 }
 // Sub-tiles each loader keeps in flight: about kPcLoaderKB KB of loads per
 // loader, 48 KB per CU (measured best of 36..72 KB at B=16, T=8192). A CU

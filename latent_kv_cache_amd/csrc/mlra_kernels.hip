@@ -665,8 +665,12 @@ mlra_split_mfma(SplitParams p) {
 // Compute wave c takes branch b = c % NB and sub-tiles j = c / NB + WT*i
 // (WT = 4 / NB); per sub-tile it runs S^T = C . Q^T (MFMA, A = slot rows,
 // B = query rows in registers), the online softmax, and O^T += C^T . P^T
-// (A = transpose reads of the slot). With WT > 1 the token-split compute waves
-// of a branch merge (m, l, O) through LDS at the end.
+// (A = transpose reads of the slot). With WT > 1 the token streams of a
+// branch merge (m, l, O) at the end without a workgroup barrier: each stream
+// takes an arrival number from an LDS counter; all but the last of a branch
+// leave their state as a record in a dedicated LDS area and exit, and the
+// last one merges those records with its own registers and writes the
+// partial.
 __device__ __forceinline__ void lds_wait_geq(const int* flag, int target) {
   // A few million polls (s_sleep 1 each) is far longer than any wait here.
   for (int it = 0; it < (1 << 22); ++it) {
@@ -699,6 +703,8 @@ mlra_split_pc(SplitParams p) {
   int* const ready = reinterpret_cast<int*>(smem + lay.flags);
   int* const consumed = ready + NSLOT;
   int* const qdone = consumed + NSLOT;
+  int* const arrived = qdone + 1;     // [NB] token streams done, per branch
+  int* const recorded = arrived + NB;  // [NB] merge records written, per branch
   int* const tabl = reinterpret_cast<int*>(smem + lay.table);
 
   const int lane = threadIdx.x & 63;
@@ -708,7 +714,7 @@ mlra_split_pc(SplitParams p) {
   if (p.nrt == 1) {
     k = blockIdx.x;
     s = blockIdx.y;
-  } else {  // two row groups per split, XCD-paired (see the streaming kernel)
+  } else {  // two row groups per split: ids 16c+i and 16c+8+i, dealt to one XCD together
     const int id = blockIdx.x;
     const int pr = (id >> 4) * 8 + (id & 7);
     if (pr >= p.S * p.spl) return;
@@ -847,7 +853,7 @@ mlra_split_pc(SplitParams p) {
 #pragma unroll
     for (int kq = 0; kq < QK; ++kq)
       if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(smem + qdst[kq]) = qv[kq];
-    if (threadIdx.x < 2 * NSLOT + 1) ready[threadIdx.x] = 0;  // ready, consumed, qdone
+    if (threadIdx.x < 2 * NSLOT + 1 + 2 * NB) ready[threadIdx.x] = 0;  // every counter
     lds_barrier();
     // ---------------- compute ----------------
     const unsigned char* const qb = smem + b * kSub * LP * 16 + (n * LP + g * (LCH / 2)) * 16;
@@ -876,39 +882,53 @@ mlra_split_pc(SplitParams p) {
       lds_wait_geq(ready + slot, (j / NSLOT + 1) * 4);
       const unsigned char* sb = smem + slot * lay.slot_bytes;
       const int tb = (t0 + (j >> 1)) * kBlock + (j & 1) * kSub;
-      f32x16 sc = f32x16{}, sd = f32x16{};
-#pragma unroll
-      for (int st = 0; st < NR; ++st)
-        sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(sb + a_r + st * 16), qR[st], sd, 0, 0, 0);
-#pragma unroll
-      for (int st = 0; st < NL; ++st) {
-        if (st % 2 == 0)
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(sb + a_l + st * 16), qL[st], sc, 0, 0, 0);
-        else
-          sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(sb + a_l + st * 16), qL[st], sd, 0, 0, 0);
-      }
-      // C^T operands of P.C (transpose reads), issued before the softmax
-      bf16x8 aT[2][NDT];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      // LDS reads are batched ahead of the MFMAs that use them: the score
+      // operands (A = slot rows) first, then the C^T operands of P.C
+      // (transpose reads) in two halves slotted between the score MFMAs. LDS
+      // returns in order, so each MFMA waits only for its own operand, and at
+      // most 15 reads are outstanding past any wait (the counter's limit;
+      // beyond it the wait would be for every read).
+      bf16x8 aR[NR], aL[NL], aT[2][NDT];
+      auto read_t = [&](int h2) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const i16x4 lo = lds_read_tr(sb + a_t + (16 * h2) * LP * 16 + dt * 64);
           const i16x4 hi = lds_read_tr(sb + a_t + (16 * h2 + 8) * LP * 16 + dt * 64);
           aT[h2][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+      };
+#pragma unroll
+      for (int st = 0; st < NR; ++st) aR[st] = rd16(sb + a_r + st * 16);
+#pragma unroll
+      for (int st = 0; st < NL; ++st) aL[st] = rd16(sb + a_l + st * 16);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 sc = f32x16{}, sd = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NR; ++st) sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qR[st], sd, 0, 0, 0);
+      read_t(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < NL; ++st) {
+        if (st % 2 == 0)
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[st], sc, 0, 0, 0);
+        else
+          sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[st], sd, 0, 0, 0);
+      }
+      read_t(1);
+      __builtin_amdgcn_sched_barrier(0);
       // every read of the slot is issued: hand it back once they complete
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       lds_signal(consumed + slot);
       sc += sd;
       if (tb + kSub > min_vis) {  // uniform
+        // element r holds token tb + 4g + 8(r/4) + r%4: compare the constant
+        // part against a per-lane limit
+        const int lim = vis - tb - 4 * g;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = tb + 8 * (r >> 2) + 4 * g + (r & 3);
-          sc[r] = tok < vis ? sc[r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) sc[r] = 8 * (r >> 2) + (r & 3) < lim ? sc[r] : -INFINITY;
       }
-      // online softmax against a lazily updated reference (see the streaming kernel)
+      // online softmax against a lazily moved reference maximum: rescale only
+      // when a row maximum exceeds it by more than kLazyLog2 (log2 units)
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
@@ -926,16 +946,16 @@ mlra_split_pc(SplitParams p) {
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
       bf16x8 pB[2];
-      float sum = 0.f;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float pe = __builtin_amdgcn_exp2f(fmaf(sc[8 * h2 + e], p.score_scale, -m_use));
-          sum += pe;
+          ps[e & 3] += pe;
           pB[h2][e] = (__bf16)pe;
         }
-      l_run += sum;
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -961,12 +981,15 @@ mlra_split_pc(SplitParams p) {
             f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} * inv;
     if (g == 0) p.part_lse[ri] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   } else {
-    // Merge the WT token streams of each branch: records over the ring.
-    constexpr int REC = NDT * 4 + 1;
-    __syncthreads();  // every slot is consumed and no loader writes any more
-    f32x4* M = reinterpret_cast<f32x4*>(smem);
-    if (wave < 4) {
-      f32x4* my = M + wave * REC * 64;
+    // Merge the WT token streams of each branch (see above).
+    constexpr int REC = NDT * 4 + 1;  // 64-lane f32x4 rows per record
+    if (wave >= 4) return;
+    int a = 0;
+    if (lane == 0) a = __hip_atomic_fetch_add(arrived + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    a = __builtin_amdgcn_readfirstlane(a);
+    f32x4* const M = reinterpret_cast<f32x4*>(smem + lay.merge) + b * (WT - 1) * REC * 64;
+    if (a < WT - 1) {
+      f32x4* my = M + a * REC * 64;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -974,13 +997,18 @@ mlra_split_pc(SplitParams p) {
           my[(dt * 4 + q) * 64 + lane] =
               f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]};
       my[(REC - 1) * 64 + lane] = f32x4{m_run, l_run, 0.f, 0.f};
+      lds_signal(recorded + b);
+      return;
     }
-    __syncthreads();
-    if (wave >= 4) return;
+    // The last stream of the branch: the others are done and write one
+    // record each, so this wait is short and always ends.
+    lds_wait_geq(recorded + b, WT - 1);
     float ms[WT], ls[WT];
+    ms[WT - 1] = m_run;
+    ls[WT - 1] = l_run;
 #pragma unroll
-    for (int w = 0; w < WT; ++w) {
-      const f32x4 ml = M[((w * NB + b) * REC + REC - 1) * 64 + lane];
+    for (int w = 0; w < WT - 1; ++w) {
+      const f32x4 ml = M[(w * REC + REC - 1) * 64 + lane];
       ms[w] = ml[0];
       ls[w] = ml[1];
     }
@@ -1001,15 +1029,16 @@ mlra_split_pc(SplitParams p) {
     const int64_t ri = (slotp * NB + b) * p.rows + row;
     float* o = p.part_o + ri * DC;
 #pragma unroll
-    for (int it = 0; it < NDT * 4; ++it) {
-      if (it % WT != strm) continue;
-      const int dt = it / 4, q = it % 4;
-      f32x4 v = f32x4{};
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int w = 0; w < WT; ++w) v += M[((w * NB + b) * REC + dt * 4 + q) * 64 + lane] * wsc[w];
-      *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
-    }
-    if (g == 0 && strm == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v = f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} *
+                  wsc[WT - 1];
+#pragma unroll
+        for (int w = 0; w < WT - 1; ++w) v += M[(w * REC + dt * 4 + q) * 64 + lane] * wsc[w];
+        *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
+      }
+    if (g == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -1045,30 +1074,45 @@ __global__ void __launch_bounds__(256) mlra_split_valu(SplitParams p) {
   float m = -INFINITY, l = 0.f, acc[NDC];
 #pragma unroll
   for (int i = 0; i < NDC; ++i) acc[i] = 0.f;
-  for (int t = t0 * kBlock; t < tend; ++t) {
-    const int phys = clamp_block(p.table[(int64_t)s * p.max_blocks + t / kBlock], p.num_blocks);
-    const int slot = t % kBlock;
-    const float* cp = lat + (int64_t)phys * p.lsb + (int64_t)slot * p.lst + (int64_t)b * p.lsbr;
-    float c[NDC];
-    float dot = 0.f;
+  // kU tokens per step: their loads are all issued before the first is used
+  // (indices clamped to the last visible token; the extra ones are skipped).
+  constexpr int kU = 8;
+  for (int tb = t0 * kBlock; tb < tend; tb += kU) {
+    float c[kU][NDC], dot[kU];
 #pragma unroll
-    for (int i = 0; i < NDC; ++i) {
-      c[i] = cp[lane + 64 * i];
-      dot = fmaf(q[i], c[i], dot);
+    for (int u = 0; u < kU; ++u) {
+      const int t = min(tb + u, tend - 1);
+      const int phys = clamp_block(p.table[(int64_t)s * p.max_blocks + t / kBlock], p.num_blocks);
+      const int slot = t % kBlock;
+      const float* cp = lat + (int64_t)phys * p.lsb + (int64_t)slot * p.lst + (int64_t)b * p.lsbr;
+#pragma unroll
+      for (int i = 0; i < NDC; ++i) c[u][i] = cp[lane + 64 * i];
+      dot[u] = lane < p.DR ? rope[(int64_t)phys * p.rsb + (int64_t)slot * p.rst + lane] : 0.f;
     }
-    if (lane < p.DR) dot = fmaf(qr, rope[(int64_t)phys * p.rsb + (int64_t)slot * p.rst + lane], dot);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
-    // one value for the whole wave (the butterfly's rounding differs per lane)
-    const float x = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dot))) *
-                    p.score_scale;
-    const float m_new = fmaxf(m, x);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    const float w = __builtin_amdgcn_exp2f(x - m_new);
-    l = l * alpha + w;
+    for (int u = 0; u < kU; ++u) {
+      float d = 0.f;
 #pragma unroll
-    for (int i = 0; i < NDC; ++i) acc[i] = acc[i] * alpha + w * c[i];
-    m = m_new;
+      for (int i = 0; i < NDC; ++i) d = fmaf(q[i], c[u][i], d);
+      if (lane < p.DR) d = fmaf(qr, dot[u], d);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      dot[u] = d;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (tb + u >= tend) break;  // uniform
+      // one value for the whole wave (the butterfly's rounding differs per lane)
+      const float x = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dot[u]))) *
+                      p.score_scale;
+      const float m_new = fmaxf(m, x);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      const float w = __builtin_amdgcn_exp2f(x - m_new);
+      l = l * alpha + w;
+#pragma unroll
+      for (int i = 0; i < NDC; ++i) acc[i] = acc[i] * alpha + w * c[u][i];
+      m = m_new;
+    }
   }
   const int64_t ri = (((int64_t)s * p.spl + k) * p.NB + b) * p.rows + row;
   const float inv = l > 0.f ? 1.f / l : 0.f;
