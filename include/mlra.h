@@ -73,7 +73,10 @@ typedef struct mlra_decode_dims {
   int32_t num_seqs;            /* S  >= 1 */
   int32_t q_len;               /* Q  in {1, 2}: new query tokens per sequence */
   int32_t num_heads;           /* H  >= 1, H * Q <= 64 */
-  int32_t d_latent;            /* DC per branch: bf16 {64, 128, 512}, fp32 {64, 128, 256, 512} */
+  int32_t d_latent;            /* DC per branch: fp32 {64, 128, 256, 512}; bf16 {64, 128} with
+                                  any n_branch, 256 with n_branch <= 2 and DR = 64 (MLRA-2:
+                                  MLA's 512-wide latent in two branches), 512 with n_branch = 1
+                                  and DR = 64 (MLA); other bf16 shapes: MLRA_ERR_UNSUPPORTED */
   int32_t d_rope;              /* DR in {32, 64} */
   int32_t block_size;          /* tokens per cache block; must be 64 */
   int32_t max_blocks_per_seq;  /* columns of block_table */

@@ -89,5 +89,26 @@ RAGGED_Q2 = DecodeConfig(
     d_latent=128, d_rope=64, dtype="bf16", context=None, context_range=(1024, 32768),
     seed=5, causal=True, scale=_mlra_scale(128, 64), out_rescale=0.5)
 
+# MLRA-2: MLA's 512-wide latent in two branches of 256 plus the shared RoPE
+# key; same cache bytes per token as MLRA-4 and MLA. Output factor 1/sqrt(2),
+# the two-branch analogue of MLRA-4's 1/sqrt(4).
+MLRA2_FUSED = DecodeConfig(
+    name="mlra2_fused_b32_t16384", num_seqs=32, q_len=1, num_heads=32, n_branch=2,
+    d_latent=256, d_rope=64, dtype="bf16", context=16384, seed=6,
+    scale=_mlra_scale(256, 64), out_rescale=1.0 / math.sqrt(2))
+
+# One sequence at 1M and 2M tokens of context (the latency-vs-length sweep's
+# long end), all four MLRA-4 branches: split-K planning at extreme lengths.
+MLRA4_B1_T1M = DecodeConfig(
+    name="mlra4_b1_t1m", num_seqs=1, q_len=1, num_heads=32, n_branch=4,
+    d_latent=128, d_rope=64, dtype="bf16", context=1 << 20, seed=7,
+    scale=_mlra_scale(128, 64), out_rescale=0.5)
+MLRA4_B1_T2M = DecodeConfig(
+    name="mlra4_b1_t2m", num_seqs=1, q_len=1, num_heads=32, n_branch=4,
+    d_latent=128, d_rope=64, dtype="bf16", context=1 << 21, seed=8,
+    scale=_mlra_scale(128, 64), out_rescale=0.5)
+
 ALL = [TINY_MLRA4_FP32, MLRA4_TP_SHARE, MLRA4_FUSED, LONG_CONTEXT, RAGGED_Q2]
-BY_NAME = {c.name: c for c in ALL + [MLA_COMPARE]}
+# Variants and stress workloads beyond the five above.
+EXTRA = [MLRA2_FUSED, MLRA4_B1_T1M, MLRA4_B1_T2M]
+BY_NAME = {c.name: c for c in ALL + [MLA_COMPARE] + EXTRA}

@@ -34,8 +34,9 @@ mlra_status resolve_dims(const mlra_decode_dims* d, int32_t n_branch, Resolved* 
   if (d->d_latent < 1 || d->d_rope < 1) return MLRA_ERR_BAD_DIMS;
   if (!pow2_in(d->d_rope, {32, 64})) return MLRA_ERR_UNSUPPORTED;
   if (d->dtype == MLRA_BF16) {
-    if (!pow2_in(d->d_latent, {64, 128, 512})) return MLRA_ERR_UNSUPPORTED;
+    if (!pow2_in(d->d_latent, {64, 128, 256, 512})) return MLRA_ERR_UNSUPPORTED;
     if (d->d_latent == 512 && (n_branch != 1 || d->d_rope != 64)) return MLRA_ERR_UNSUPPORTED;
+    if (d->d_latent == 256 && (n_branch > 2 || d->d_rope != 64)) return MLRA_ERR_UNSUPPORTED;
   } else {
     if (!pow2_in(d->d_latent, {64, 128, 256, 512})) return MLRA_ERR_UNSUPPORTED;
   }

@@ -12,13 +12,14 @@ constexpr int kBlock = 64;      // tokens per cache block (= one split-K tile)
 constexpr int kMaxSeqs = 65535;  // grid y limit
 constexpr int kSub = 32;        // tokens per MFMA sub-tile (M of the 32x32 MFMA)
 
-// Workgroup shape of the bf16 MFMA split kernel, shared by planner and
-// launcher. One workgroup fills one CU: 2 waves per SIMD when a wave holds 32
-// query rows (4 SIMDs -> 8 waves), 1 per SIMD with 64 rows or the 512-wide
-// latent. Its waves split the branches (NB), the latent width (WD) and the
-// workgroup's tiles (WT).
-constexpr int mfma_wd(int DC) { return DC == 512 ? 4 : 1; }
-constexpr int mfma_waves_per_simd(int NT, int DC) { return (NT == 1 && DC != 512) ? 2 : 1; }
+// Workgroup shape of the bf16 MFMA split kernel (latent widths 256 and 512),
+// shared by planner and launcher. One workgroup fills one CU: 2 waves per SIMD
+// when a wave holds 32 query rows of a latent of at most 128 (4 SIMDs -> 8
+// waves), else 1 per SIMD (the width-split score exchange needs more than the
+// 256 registers two waves per SIMD leave). Its waves split the branches (NB),
+// the latent width (WD, 128 columns per wave) and the workgroup's tiles (WT).
+constexpr int mfma_wd(int DC) { return DC == 512 ? 4 : (DC == 256 ? 2 : 1); }
+constexpr int mfma_waves_per_simd(int NT, int DC) { return (NT == 1 && DC <= 128) ? 2 : 1; }
 // 32-token sub-tiles each wave keeps in flight in registers (48 VGPRs each at
 // DC = 128, DR = 64); a wave requests PD sub-tiles ahead of the one it computes.
 // With two row tiles a CU runs only 4 waves, so each requests two ahead.
@@ -37,7 +38,7 @@ constexpr int mfma_rpitch(int DR) { return DR / 8 + 1; }
 
 enum Variant : int32_t {
   kVariantValuFp32 = 1,  // float32 inputs: one wave per (row, branch), vector ALU
-  kVariantMfmaBf16 = 2,  // bfloat16, latent 512: 32x32x16 bf16 MFMA, waves split the width
+  kVariantMfmaBf16 = 2,  // bfloat16, latent 256/512: 32x32x16 bf16 MFMA, waves split the width
   kVariantPcBf16 = 4,    // bfloat16, latent 64/128: loader waves fill an LDS ring for compute waves
 };
 

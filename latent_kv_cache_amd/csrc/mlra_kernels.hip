@@ -1324,15 +1324,18 @@ template <int NB, int DC, int NT>
 static hipError_t dispatch_dr(const SplitParams& sp, const mlra_decode_plan& plan,
                               hipStream_t st) {
   if (sp.DR == 64) return launch_mfma<NB, DC, 64, NT>(sp, plan, st);
-  if constexpr (DC != 512) return launch_mfma<NB, DC, 32, NT>(sp, plan, st);
-  return hipErrorInvalidValue;
+  return hipErrorInvalidValue;  // wide latents take the 64-wide RoPE key only
 }
 
-// The 8-wave width-split kernel serves the 512-wide single latent.
+// The 8-wave width-split kernel serves the wide latents: the 512-wide single
+// latent (four 128-column slices) and 256-wide latents with one or two
+// branches (two slices).
 template <int NT>
 static hipError_t dispatch_nb(const SplitParams& sp, const mlra_decode_plan& plan,
                               hipStream_t st) {
   if (sp.NB == 1 && sp.DC == 512) return dispatch_dr<1, 512, NT>(sp, plan, st);
+  if (sp.NB == 1 && sp.DC == 256) return dispatch_dr<1, 256, NT>(sp, plan, st);
+  if (sp.NB == 2 && sp.DC == 256) return dispatch_dr<2, 256, NT>(sp, plan, st);
   return hipErrorInvalidValue;
 }
 

@@ -62,7 +62,8 @@ def test_status_strings_and_version(lib):
     assert lib.mlra_version() >= 100
 
 
-@pytest.mark.parametrize("cfg", configs.ALL + [configs.MLA_COMPARE], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", configs.ALL + [configs.MLA_COMPARE] + configs.EXTRA,
+                         ids=lambda c: c.name)
 def test_plan_covers_every_tile(lib, cfg):
     d = _dims(cfg)
     st, p = _plan(lib, d, cfg.n_branch)
@@ -70,16 +71,17 @@ def test_plan_covers_every_tile(lib, cfg):
     max_tiles = -(-d.max_seq_len // 64)
     assert p.splits_per_seq * p.tiles_per_split >= max_tiles
     assert (p.splits_per_seq - 1) * p.tiles_per_split < max(max_tiles, 1)
-    if cfg.dtype == "bf16" and cfg.d_latent == 512:  # token-split waves get equal tile counts
-        assert p.tiles_per_split % (p.waves_per_group // 4) == 0
+    if cfg.dtype == "bf16" and cfg.d_latent >= 256:  # token-split waves get equal tile counts
+        wt = p.waves_per_group // (cfg.n_branch * (cfg.d_latent // 128))
+        assert p.tiles_per_split % wt == 0
     if cfg.dtype == "bf16" and cfg.d_latent <= 128:  # block ids of a split fit the LDS table
         assert p.tiles_per_split <= 1024
     rows = cfg.num_heads * cfg.q_len
     slots = cfg.num_seqs * p.splits_per_seq * cfg.n_branch * rows
     assert p.workspace_bytes >= slots * (cfg.d_latent + 1) * 4
-    # 1: fp32 vector ALU; 2: bf16, 512-wide latent (width-split waves);
+    # 1: fp32 vector ALU; 2: bf16, 256/512-wide latent (width-split waves);
     # 4: bf16, latent 64/128 (loader and compute waves)
-    expect = 1 if cfg.dtype != "bf16" else (2 if cfg.d_latent == 512 else 4)
+    expect = 1 if cfg.dtype != "bf16" else (2 if cfg.d_latent >= 256 else 4)
     assert p.kernel_variant == expect
     assert p.lds_bytes <= 160 * 1024
 
@@ -128,6 +130,11 @@ def test_branch_and_width_rules(lib):
     assert _plan(lib, d, 0)[0] == 2
     d.dtype = _lib.MLRA_FP32
     assert _plan(lib, d, 2)[0] == 0
+    d = _dims(configs.MLRA2_FUSED)             # bf16 256-wide latent: up to two branches, RoPE 64
+    assert _plan(lib, d, 2)[0] == 0 and _plan(lib, d, 1)[0] == 0
+    assert _plan(lib, d, 4)[0] == 3
+    d.d_rope = 32
+    assert _plan(lib, d, 2)[0] == 3
 
 
 def test_pointer_and_alignment_errors_before_any_device_call(lib):

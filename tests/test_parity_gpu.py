@@ -79,6 +79,7 @@ for nb in (1, 2, 4):
             for h, q in ((16, 1), (24, 2)):
                 SHAPES.append((nb, dc, dr, h, q))
 SHAPES += [(1, 512, 64, 32, 1), (1, 512, 64, 32, 2)]
+SHAPES += [(1, 256, 64, 32, 1), (2, 256, 64, 16, 1), (2, 256, 64, 24, 2)]
 
 
 @pytest.mark.parametrize("nb,dc,dr,h,q", SHAPES)
@@ -109,6 +110,51 @@ def test_full_size_mla_comparison_call():
     out, lse = run_gpu(inp, entry="mla")
     ro, rl = oracle(inp)
     assert_parity(out, lse, ro, rl)
+
+
+def test_full_size_mlra2():
+    cfg = configs.MLRA2_FUSED
+    _say(f"full {cfg.name}")
+    inp = make_inputs(cfg)
+    for reduce in ("sum", "concat"):
+        out, lse = run_gpu(inp, reduce)
+        assert_parity(out, lse, *oracle(inp, reduce))
+
+
+def oracle_heads_by_branch(inp, heads):
+    """Oracle outputs for a sample of heads, one branch at a time.
+
+    Heads and branches are independent in the method, so branch b of heads
+    `heads` is the oracle run on the one-branch problem made of branch b's
+    latents and queries (host memory then holds one branch in float64).
+    Returns (concat out [S][Q][len(heads)][NB][DC], lse [S][Q][len(heads)][NB]).
+    """
+    c = inp.cfg
+    outs, lses = [], []
+    for b in range(c.n_branch):
+        o, l = mlra_decode(inp.q_latent[:, :, heads, b:b + 1], inp.q_rope[:, :, heads],
+                           inp.latent_cache[:, :, b:b + 1], inp.rope_cache, inp.block_table,
+                           inp.seq_lens, c.scale, c.out_rescale, "concat", c.causal,
+                           c.block_size)
+        outs.append(o[:, :, :, 0])
+        lses.append(l[:, :, :, 0])
+    return np.stack(outs, axis=3), np.stack(lses, axis=3)
+
+
+@pytest.mark.parametrize("cfg", [configs.MLRA4_B1_T1M, configs.MLRA4_B1_T2M], ids=lambda c: c.name)
+def test_single_sequence_million_token_context_sampled_heads(cfg):
+    _say(f"{cfg.name}: inputs")
+    inp = make_inputs(cfg)
+    dev = to_device(inp)
+    _say(f"{cfg.name}: GPU sum and concat")
+    out_s, lse_s = run_gpu(inp, "sum", dev=dev)
+    out_c, lse_c = run_gpu(inp, "concat", dev=dev)
+    assert np.array_equal(lse_s, lse_c)
+    heads = [0, 11, 31]
+    _say(f"{cfg.name}: oracle on heads {heads}, branch by branch")
+    ro, rl = oracle_heads_by_branch(inp, heads)
+    assert_parity(out_c[:, :, heads], lse_c[:, :, heads], ro, rl)
+    assert_parity(out_s[:, :, heads], lse_s[:, :, heads], ro.sum(axis=3), rl)
 
 
 def test_fp32_path_small_shapes():
