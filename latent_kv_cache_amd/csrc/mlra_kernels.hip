@@ -1290,6 +1290,92 @@ __global__ void __launch_bounds__(256) mlra_combine(CombineParams c) {
   store_vpl<OutT, VPL>(out + orow * c.DC + lane * VPL, o);
 }
 
+// Column-sliced combine, for calls with few (sequence, query row) pairs and
+// many splits (one long sequence): one workgroup per (sequence, row, CC-column
+// slice), one wave per branch. Lane (kp, c) = (lane / CC, lane % CC) merges
+// column c of the splits k = kp (mod 64 / CC) with a private running
+// log-sum-exp, 32 splits' loads in flight per step; the split phases then
+// merge through lane exchanges. Same result as mlra_combine up to the order
+// of the fp32 sums.
+__device__ __forceinline__ void lse_merge(float& m, float& d, float& o, float m2, float d2, float o2) {
+  const float mm = fmaxf(m, m2);
+  const float mu = mm == -INFINITY ? 0.f : mm;
+  const float a = expf(m - mu), b = expf(m2 - mu);
+  d = d * a + d2 * b;
+  o = o * a + o2 * b;
+  m = mm;
+}
+template <typename OutT, int kCombCols>
+__global__ void __launch_bounds__(256) mlra_combine_cols(CombineParams c) {
+  constexpr int KP = 64 / kCombCols;  // split phases per wave
+  constexpr int U = 32;               // splits per lane per step
+  __shared__ float red[4 * kCombCols];
+  const int lane = threadIdx.x & 63;
+  const int b = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = blockIdx.x, slice = blockIdx.y;
+  const int s = pair / c.rows, row = pair % c.rows;
+  const int L_raw = c.seq_lens[s];
+  const int j = row / c.H, h = row % c.H;
+  const int64_t orow = ((int64_t)s * c.Q + j) * c.H + h;
+  const int64_t kstride = (int64_t)c.NB * c.rows;  // between splits, in rows
+  const int last = c.spl - 1;
+  const int64_t base = ((int64_t)s * c.spl * c.NB + b) * c.rows + row;
+  const float* lse_p = c.part_lse + base;
+  const int col = slice * kCombCols + lane % kCombCols, kp = lane / kCombCols;
+  const float* o_p = c.part_o + base * c.DC + col;
+  const int L = L_raw < 0 ? 0 : (L_raw > c.lcap ? c.lcap : L_raw);
+  const int nsplit = min((L + kBlock * c.tps - 1) / (kBlock * c.tps), c.spl);
+
+  float m = -INFINITY, d = 0.f, o = 0.f;
+  for (int k0 = 0; k0 < nsplit; k0 += KP * U) {
+    float v[U], lk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // clamped, unconditional: all in flight
+      const int64_t k = min(k0 + kp + KP * u, last);
+      v[u] = o_p[k * kstride * c.DC];
+      lk[u] = lse_p[k * kstride];
+    }
+    // Splits past the sequence's count were never written in this call:
+    // select them away (a zero weight times stale data could be NaN).
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (k0 + kp + KP * u < nsplit) mc = fmaxf(mc, lk[u]);
+    const float mu = mc == -INFINITY ? 0.f : mc;
+    const float sc = expf(m - mu);
+    d *= sc;
+    o *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool use = k0 + kp + KP * u < nsplit;
+      const float w = expf(lk[u] - mu);
+      d = use ? d + w : d;
+      o = use ? fmaf(w, v[u], o) : o;
+    }
+    m = mc;
+  }
+#pragma unroll
+  for (int off = kCombCols; off < 64; off <<= 1)
+    lse_merge(m, d, o, __shfl_xor(m, off), __shfl_xor(d, off), __shfl_xor(o, off));
+  const float lse_b = d > 0.f ? m + logf(d) : -INFINITY;
+  o = d > 0.f ? o / d : 0.f;
+  if (slice == 0 && lane == 0) c.lse[orow * c.NB + b] = lse_b;
+  OutT* out = static_cast<OutT*>(c.out);
+  if (c.concat) {
+    if (kp == 0) out[(orow * c.NB + b) * c.DC + col] = (OutT)(o * c.out_rescale);
+    return;
+  }
+  if (c.NB > 1) {
+    if (kp == 0) red[b * kCombCols + lane] = o;
+    __syncthreads();
+    if (b != 0) return;
+    float tot = 0.f;
+    for (int bb = 0; bb < c.NB; ++bb) tot += red[bb * kCombCols + lane % kCombCols];
+    o = tot;
+  }
+  if (kp == 0) out[orow * c.DC + col] = (OutT)(o * c.out_rescale);
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -1527,8 +1613,24 @@ static mlra_status decode(int phases, const void* q_latent, const void* q_rope,
   cp.lcap = r.lcap;
   cp.concat = r.reduce == MLRA_BRANCH_CONCAT;
   cp.out_rescale = out_rescale;
-  dim3 cgrid(r.S * r.rows);
   const bool bf = r.dtype == MLRA_BF16;
+  // Few (sequence, row) pairs and many splits: slice the columns across
+  // workgroups so that the partials are read by most of the CUs, with enough
+  // split phases per wave that one step keeps a lane's loads in flight.
+  if (2 * (int64_t)r.S * r.rows < plan.num_cus && plan.splits_per_seq >= 32) {
+    const bool narrow = plan.splits_per_seq > 128;  // 8 columns, 8 split phases
+    const dim3 grid((uint32_t)(r.S * r.rows), (uint32_t)(r.DC / (narrow ? 8 : 16)));
+    const dim3 block(64 * r.NB);
+    if (narrow) {
+      if (bf) hipLaunchKernelGGL((mlra_combine_cols<__bf16, 8>), grid, block, 0, hs, cp);
+      else hipLaunchKernelGGL((mlra_combine_cols<float, 8>), grid, block, 0, hs, cp);
+    } else {
+      if (bf) hipLaunchKernelGGL((mlra_combine_cols<__bf16, 16>), grid, block, 0, hs, cp);
+      else hipLaunchKernelGGL((mlra_combine_cols<float, 16>), grid, block, 0, hs, cp);
+    }
+    return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
+  }
+  dim3 cgrid(r.S * r.rows);
   switch (r.DC / 64) {
     case 1: launch_combine<1>(bf, cgrid, cp, hs); break;
     case 2: launch_combine<2>(bf, cgrid, cp, hs); break;

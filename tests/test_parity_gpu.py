@@ -261,6 +261,35 @@ def test_seq_len_above_max_is_clamped_not_read_out_of_bounds():
     assert_parity(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy(), ro, rl)
 
 
+@pytest.mark.parametrize("num_splits", [0, 40, 200])
+def test_workspace_contents_are_never_read_before_written(num_splits):
+    # Ragged lengths leave split slots of short sequences unwritten. With many
+    # splits over a few (sequence, row) pairs the column-sliced combine runs
+    # (16- and 8-column slices); with the library's plan the per-row one.
+    # Poisoned workspaces must not leak into the output.
+    cfg = _cfg(num_seqs=2, context_range=(100, 30000), seed=41)
+    inp = make_inputs(cfg)
+    d = to_device(inp)
+    args = (d["q_latent"], d["q_rope"], d["latent_cache"], d["rope_cache"], d["block_table"],
+            d["seq_lens"], cfg.n_branch)
+    kw = dict(max_seq_len=inp.max_seq_len, num_splits=num_splits)
+    dims = api.make_dims(d["q_latent"], d["q_rope"], d["latent_cache"], d["rope_cache"],
+                         d["block_table"], **kw)
+    nbytes = api.make_plan(dims, cfg.n_branch).workspace_bytes
+    ro, rl = oracle(inp)
+    results = []
+    for fill in (float("nan"), float("inf"), -float("inf")):
+        ws = torch.full((nbytes // 4,), fill, dtype=torch.float32, device="cuda")
+        _say(f"poisoned workspace {fill} num_splits={num_splits}")
+        o, l = api.mlra_decode_attention(*args, cfg.scale, cfg.out_rescale, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        results.append((o.clone(), l.clone()))
+        assert_parity(o.float().cpu().numpy().astype(np.float64),
+                      l.cpu().numpy().astype(np.float64), ro, rl)
+    for o, l in results[1:]:
+        assert torch.equal(o, results[0][0]) and torch.equal(l, results[0][1])
+
+
 def test_two_phase_and_prepared_calls_match_the_single_call_bitwise():
     cfg = _cfg(num_seqs=3, context_range=(100, 3000), seed=31)
     inp = make_inputs(cfg)
