@@ -16,8 +16,12 @@ combine kernel), bracketed by events: roofline.achieved is the split kernel's
 algorithmic bytes (everything above but the outputs) over its average
 per-launch time.
 
+With --append the line instead measures the cache append (mlra_cache_append:
+the new tokens' calibrated latents and rotated position keys written into the
+paged caches) on the workload's layout, default mlra4_append_b4096_q2.
+
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
-                       [--workload NAME] [--no-cpu-baseline] [--graph]
+                       [--workload NAME] [--no-cpu-baseline] [--graph] [--append]
 """
 from __future__ import annotations
 
@@ -94,6 +98,93 @@ def flops(inp) -> int:
     return int(L.sum()) * c.q_len * c.num_heads * per
 
 
+def append_bytes(cfg) -> int:
+    """Algorithmic bytes of one append call: the float32 new values read, the
+    cache rows written, one block-table entry per token and seq_lens."""
+    el = 2 if cfg.dtype == "bf16" else 4
+    tokens = cfg.num_seqs * cfg.q_len
+    row = cfg.n_branch * cfg.d_latent + cfg.d_rope
+    return tokens * (row * 4 + row * el + 4) + cfg.num_seqs * 4
+
+
+def bench_append(torch, args) -> int:
+    from latent_kv_cache_amd import api, configs
+    from latent_kv_cache_amd.inputs import make_append_inputs, make_inputs, to_device
+
+    name = args.workload or "mlra4_append_b4096_q2"
+    cfg = configs.BY_NAME[name]
+    inp = make_inputs(cfg)
+    lat_new, rope_new = make_append_inputs(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = to_device(inp, dev)
+    nbytes = append_bytes(cfg)
+    cache_bytes = d["latent_cache"].numel() * d["latent_cache"].element_size()
+    # copies of the caches and of the new values, so that consecutive calls
+    # touch memory the Infinity Cache does not hold
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / max(nbytes, 1)))
+    copies = min(copies, max(2, int(40e9 // max(cache_bytes, 1))))
+    nb = inp.num_blocks
+    lat_all = d["latent_cache"].repeat(copies, 1, 1, 1)
+    rope_all = d["rope_cache"].repeat(copies, 1, 1)
+    tables = [(d["block_table"] + k * nb).contiguous() for k in range(copies)]
+    lat_in = [torch.from_numpy(lat_new).to(dev) for _ in range(copies)]
+    rope_in = [torch.from_numpy(rope_new).to(dev) for _ in range(copies)]
+    scale = 1.0 / math.sqrt(2.0)
+
+    def step(i):
+        k = i % copies
+        api.mlra_cache_append(lat_in[k], rope_in[k], lat_all, rope_all, tables[k],
+                              d["seq_lens"], scale)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(args.steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "cache append HBM GB/s (% of peak) + new tokens/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) float32 new tokens, shuffled paged blocks)",
+        "config": {"workload": cfg.name, "batch": cfg.num_seqs, "new_tokens": cfg.q_len,
+                   "n_branch": cfg.n_branch, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope,
+                   "block_size": cfg.block_size, "copies": copies},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(cfg.num_seqs * cfg.q_len / (ms * 1e-3), 1),
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "mlra_append", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("mlra_append", cfg.name)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import cache_append
+        reps, t_total = 0, 0.0
+        while t_total < 12.0 and reps < 100:
+            t0 = time.perf_counter()
+            cache_append(lat_new, rope_new, inp.latent_cache, inp.rope_cache, inp.block_table,
+                         inp.seq_lens, scale, 10000.0, cfg.block_size)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        per = t_total / reps
+        res["cpu_baseline"] = {
+            "value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full passes of the {cfg.name} batch through the float64 oracle "
+                      f"(single-threaded Python loop over tokens; {per * 1e3:.1f} ms per pass, "
+                      f"{cfg.num_seqs * cfg.q_len / per:.0f} new tokens/s)"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     """Time the float64 oracle on the host over repeated passes of the batch."""
     from oracle import mlra_decode
@@ -140,12 +231,19 @@ def copy_calibration(torch, mib: int, steps: int, warmup: int) -> int:
     return 0
 
 
+DEFAULT_WORKLOAD = "mlra4_tp_share_b16_t8192"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mlra4_tp_share_b16_t8192")
+    ap.add_argument("--workload", default=None,
+                    help=f"workload name (default {DEFAULT_WORKLOAD}; with --append "
+                         "mlra4_append_b4096_q2)")
+    ap.add_argument("--append", action="store_true",
+                    help="measure the cache append instead of decode attention")
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0: enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
@@ -163,10 +261,12 @@ def main() -> int:
     import torch
     if args.copy_calibration:
         return copy_calibration(torch, args.copy_calibration, args.steps, args.warmup)
+    if args.append:
+        return bench_append(torch, args)
     from latent_kv_cache_amd import api, configs
     from latent_kv_cache_amd.inputs import make_inputs, to_device
 
-    cfg = configs.BY_NAME[args.workload]
+    cfg = configs.BY_NAME[args.workload or DEFAULT_WORKLOAD]
     inp = make_inputs(cfg)
     ab = algorithmic_bytes(inp)
     dev = torch.device("cuda:0")

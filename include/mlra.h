@@ -212,6 +212,42 @@ mlra_status mlra_decode_combine(const int32_t* seq_lens, int32_t n_branch, float
                                 void* out, float* lse, const mlra_decode_dims* dims,
                                 const void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Append the Q new tokens of every sequence to the paged caches: the step
+ * before decode attention. What a token holds follows the wispaper.ai blog
+ * "MLRA: Breaking the Sharding Bottleneck in Latent Attention", "The Core
+ * Insight" (one latent per branch plus one decoupled position key shared by
+ * the branches) and "Mathematical Calibration" (the latents are multiplied by
+ * a calibration factor, here a caller argument).
+ *
+ *  latent_new   [S][Q][n_branch][DC] float32, dense: the new tokens' projected
+ *               branch latents
+ *  rope_new     [S][Q][DR] float32, dense: their projected position keys, not
+ *               yet rotated
+ *  latent_cache, rope_cache, block_table, seq_lens, n_branch, dims: as for
+ *               mlra_decode_attention (same dims; num_heads, max_seq_len,
+ *               causal, num_splits, reduce and sum_seq_lens are validated
+ *               but not used here)
+ *  latent_scale calibration factor on the latents (finite)
+ *  rope_base    rotary base (finite, > 0; 10000 is the usual value)
+ *
+ * seq_lens counts the new tokens, so token j of sequence s lands at position
+ * p = seq_lens[s] - Q + j: block block_table[s][p / 64], slot p % 64.
+ *   latent row b   = latent_scale * latent_new[s][j][b]
+ *   key pair i     = rotary embedding: (k[2i], k[2i+1]) turned by
+ *                    the angle p * rope_base^(-2i/DR)
+ * Each value is formed in double and rounded once to the cache dtype
+ * (bf16: nearest, ties to even). Tokens whose position is negative or lies
+ * past max_blocks_per_seq * 64, or whose block id is outside
+ * [0, num_blocks), are not written. Asynchronous on stream; alignment as for
+ * mlra_decode_attention (inputs and caches 16-byte aligned).
+ */
+mlra_status mlra_cache_append(const float* latent_new, const float* rope_new,
+                              void* latent_cache, void* rope_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int32_t n_branch, float latent_scale, float rope_base,
+                              const mlra_decode_dims* dims, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* mlra_status_string(mlra_status status);
 

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "MLRA_OK", 1: "MLRA_ERR_NULL_PTR", 2: "MLRA_ERR_BAD_DIMS",
 # Functions include/mlra.h declares (checked against the header by the tests).
 EXPORTS = ("mlra_decode_make_plan", "mlra_decode_workspace_size", "mlra_decode_attention",
            "mla_decode_attention", "mlra_decode_partials", "mlra_decode_combine",
-           "mlra_status_string", "mlra_version")
+           "mlra_cache_append", "mlra_status_string", "mlra_version")
 
 
 class DecodeDims(ctypes.Structure):
@@ -90,6 +90,8 @@ def load() -> ctypes.CDLL:
         lib.mlra_decode_partials.restype = i32
         lib.mlra_decode_combine.argtypes = [vp, i32, f32, vp, vp, dims_p, vp, sz, vp]
         lib.mlra_decode_combine.restype = i32
+        lib.mlra_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, f32, f32, dims_p, vp]
+        lib.mlra_cache_append.restype = i32
         lib.mlra_status_string.argtypes = [i32]
         lib.mlra_status_string.restype = ctypes.c_char_p
         lib.mlra_version.argtypes = []

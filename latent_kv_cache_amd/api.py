@@ -147,6 +147,47 @@ def _call(entry: str, q_latent, q_rope, latent_cache, rope_cache, block_table, s
     return out, lse
 
 
+def mlra_cache_append(latent_new: torch.Tensor, rope_new: torch.Tensor,
+                      latent_cache: torch.Tensor, rope_cache: torch.Tensor,
+                      block_table: torch.Tensor, seq_lens: torch.Tensor, latent_scale: float,
+                      rope_base: float = 10000.0, *, stream=None) -> None:
+    """Write the Q new tokens of every sequence into the paged caches, in place.
+
+    latent_new [S][Q][NB][DC] and rope_new [S][Q][DR] are float32 (projected;
+    the key not yet rotated); the caches are laid out as for the decode call.
+    Token j of sequence s lands at position seq_lens[s] - Q + j (include/mlra.h).
+    """
+    lib = _lib.load()
+    tensors = (latent_new, rope_new, latent_cache, rope_cache, block_table, seq_lens)
+    dev = latent_new.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must be on the same GPU")
+    if latent_new.dtype != torch.float32 or rope_new.dtype != torch.float32:
+        raise TypeError("latent_new and rope_new must be float32")
+    if latent_new.dim() != 4 or rope_new.dim() != 3 or rope_new.shape[:2] != latent_new.shape[:2]:
+        raise ValueError("latent_new must be [S][Q][NB][DC] and rope_new [S][Q][DR]")
+    for name, t in (("latent_new", latent_new), ("rope_new", rope_new),
+                    ("block_table", block_table), ("seq_lens", seq_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    S, Q, NB, DC = latent_new.shape
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (S,):
+        raise TypeError("seq_lens must be an int32 tensor of shape [S]")
+    # dims as the decode call sees these caches (one head: only the layout matters here)
+    dims = make_dims(torch.empty((S, Q, 1, NB, DC), dtype=latent_cache.dtype, device="meta"),
+                     torch.empty((S, Q, 1, rope_new.shape[2]), dtype=latent_cache.dtype,
+                                 device="meta"),
+                     latent_cache, rope_cache, block_table,
+                     max_seq_len=block_table.shape[1] * latent_cache.shape[1])
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    status = lib.mlra_cache_append(latent_new.data_ptr(), rope_new.data_ptr(),
+                                   latent_cache.data_ptr(), rope_cache.data_ptr(),
+                                   block_table.data_ptr(), seq_lens.data_ptr(), int(NB),
+                                   float(latent_scale), float(rope_base), dims, stream)
+    _lib.check(status, "mlra_cache_append")
+
+
 def mlra_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
                           latent_cache: torch.Tensor, rope_cache: torch.Tensor,
                           block_table: torch.Tensor, seq_lens: torch.Tensor, n_branch: int,

@@ -108,7 +108,14 @@ MLRA4_B1_T2M = DecodeConfig(
     d_latent=128, d_rope=64, dtype="bf16", context=1 << 21, seed=8,
     scale=_mlra_scale(128, 64), out_rescale=0.5)
 
+# Cache append at a large serving batch: 4096 sequences, 2 new tokens each,
+# all four MLRA-4 branches (one head: the append does not read queries).
+APPEND_B4096_Q2 = DecodeConfig(
+    name="mlra4_append_b4096_q2", num_seqs=4096, q_len=2, num_heads=1, n_branch=4,
+    d_latent=128, d_rope=64, dtype="bf16", context=64, seed=9,
+    scale=_mlra_scale(128, 64), out_rescale=0.5)
+
 ALL = [TINY_MLRA4_FP32, MLRA4_TP_SHARE, MLRA4_FUSED, LONG_CONTEXT, RAGGED_Q2]
 # Variants and stress workloads beyond the five above.
-EXTRA = [MLRA2_FUSED, MLRA4_B1_T1M, MLRA4_B1_T2M]
+EXTRA = [MLRA2_FUSED, MLRA4_B1_T1M, MLRA4_B1_T2M, APPEND_B4096_Q2]
 BY_NAME = {c.name: c for c in ALL + [MLA_COMPARE] + EXTRA}

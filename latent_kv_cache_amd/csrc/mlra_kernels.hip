@@ -1377,6 +1377,96 @@ __global__ void __launch_bounds__(256) mlra_combine_cols(CombineParams c) {
 }
 
 // ---------------------------------------------------------------------------
+// cache append: the new tokens' latents and rotated position keys
+// ---------------------------------------------------------------------------
+// What a token holds in the cache follows the wispaper.ai blog "MLRA: Breaking
+// the Sharding Bottleneck in Latent Attention", "The Core Insight" (one latent
+// per branch plus one decoupled position key shared by the branches) and
+// "Mathematical Calibration" (latents multiplied by a calibration factor).
+// The key is rotated by the rotary position embedding (adjacent pairs
+// (2i, 2i+1) turned by p * base^(-2i/DR)). Threads are numbered over (token,
+// piece), so every lane of a wave has work: a latent piece is one 16-byte
+// chunk, a key piece one pair (its double-precision sine and cosine are the
+// long pole, so each thread takes one). The new values and the sequence
+// length are loaded before the block id, which depends on the length. Values
+// are formed in double (the latent product of two floats is exact there;
+// angles keep full precision at positions in the millions) and rounded once
+// to the cache type.
+struct AppendParams {
+  const float* lat_new;   // [S][Q][NB][DC]
+  const float* rope_new;  // [S][Q][DR]
+  void* lat;
+  void* rope;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  int32_t S, Q, NB, DC, DR, max_blocks, num_blocks;
+  int64_t lsb, lst, lsbr, rsb, rst;
+  double latent_scale;
+  double theta[64];  // rope_base^(-2i/DR) for pair i < DR/2, computed on the host
+};
+
+// Nearest bf16 of a double, ties to even, in one rounding: round the double
+// to 8 significant bits in place, after which narrowing to float and to bf16
+// is exact (finite values in float's normal range).
+__device__ __forceinline__ __bf16 bf16_from_double(double x) {
+  uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  u += ((u >> 45) & 1) + ((uint64_t(1) << 44) - 1);
+  u &= ~((uint64_t(1) << 45) - 1);
+  return (__bf16)(float)__longlong_as_double(static_cast<long long>(u));
+}
+__device__ __forceinline__ void cvt_from_double(__bf16& d, double x) { d = bf16_from_double(x); }
+__device__ __forceinline__ void cvt_from_double(float& d, double x) { d = (float)x; }
+
+template <typename T>
+__global__ void __launch_bounds__(256) mlra_append(AppendParams a) {
+  constexpr int CH = 16 / sizeof(T);  // latent elements per 16-byte store
+  const int lch = a.DC / CH, nl = a.NB * lch, per_tok = nl + a.DR / 2;
+  const int x = blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= a.S * a.Q * per_tok) return;
+  const int tok = x / per_tok;  // = s * Q + j
+  const int c = x - tok * per_tok;
+  const int s = tok / a.Q, j = tok - s * a.Q;
+  const bool is_lat = c < nl;
+  const int b = is_lat ? c / lch : 0;
+  const int c0 = is_lat ? (c - b * lch) * CH : 2 * (c - nl);
+  float in[CH];
+  if (is_lat) {
+    const float* src = a.lat_new + ((int64_t)tok * a.NB + b) * a.DC + c0;
+#pragma unroll
+    for (int q = 0; q < CH / 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) in[4 * q + e] = v[e];
+    }
+  } else {
+    const float2 v = *reinterpret_cast<const float2*>(a.rope_new + (int64_t)tok * a.DR + c0);
+    in[0] = v.x;
+    in[1] = v.y;
+  }
+  const int64_t p = (int64_t)a.seq_lens[s] - a.Q + j;  // position of new token j
+  if (p < 0 || p >= (int64_t)a.max_blocks * kBlock) return;
+  const int blk = a.table[(int64_t)s * a.max_blocks + p / kBlock];
+  if (blk < 0 || blk >= a.num_blocks) return;  // never write outside the cache
+  const int slot = (int)(p % kBlock);
+  if (is_lat) {
+    T outv[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) cvt_from_double(outv[e], (double)in[e] * a.latent_scale);
+    T* dst = static_cast<T*>(a.lat) + blk * a.lsb + slot * a.lst + b * a.lsbr + c0;
+    *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, outv);
+  } else {
+    double sn, cs;
+    sincos((double)p * a.theta[c0 / 2], &sn, &cs);
+    T o2[2];
+    cvt_from_double(o2[0], (double)in[0] * cs - (double)in[1] * sn);
+    cvt_from_double(o2[1], (double)in[0] * sn + (double)in[1] * cs);
+    T* dst = static_cast<T*>(a.rope) + blk * a.rsb + slot * a.rst + c0;
+    dst[0] = o2[0];
+    dst[1] = o2[1];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <int NB, int DC, int DR, int NT>
@@ -1706,4 +1796,52 @@ extern "C" mlra_status mlra_decode_combine(const int32_t* seq_lens, int32_t n_br
   return mlra::decode(mlra::kCombine, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens,
                       n_branch, 1.0f, out_rescale, out, lse, dims, const_cast<void*>(workspace),
                       workspace_bytes, stream);
+}
+
+extern "C" mlra_status mlra_cache_append(const float* latent_new, const float* rope_new,
+                                         void* latent_cache, void* rope_cache,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         int32_t n_branch, float latent_scale, float rope_base,
+                                         const mlra_decode_dims* dims, void* stream) {
+  mlra::Resolved r;
+  const mlra_status st = mlra::resolve_dims(dims, n_branch, &r);
+  if (st != MLRA_OK) return st;
+  if (!latent_new || !rope_new || !latent_cache || !rope_cache || !block_table || !seq_lens)
+    return MLRA_ERR_NULL_PTR;
+  if (!std::isfinite(latent_scale) || !std::isfinite(rope_base) || !(rope_base > 0.f))
+    return MLRA_ERR_BAD_DIMS;
+  if (!mlra::aligned16(latent_new) || !mlra::aligned16(rope_new) || !mlra::aligned16(latent_cache) ||
+      !mlra::aligned16(rope_cache) || !mlra::aligned4(block_table) || !mlra::aligned4(seq_lens))
+    return MLRA_ERR_ALIGNMENT;
+  mlra::AppendParams a;
+  a.lat_new = latent_new;
+  a.rope_new = rope_new;
+  a.lat = latent_cache;
+  a.rope = rope_cache;
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.Q = r.Q;
+  a.NB = r.NB;
+  a.DC = r.DC;
+  a.DR = r.DR;
+  a.max_blocks = r.max_blocks;
+  a.num_blocks = r.num_blocks;
+  a.lsb = r.lsb;
+  a.lst = r.lst;
+  a.lsbr = r.lsbr;
+  a.rsb = r.rsb;
+  a.rst = r.rst;
+  a.latent_scale = latent_scale;
+  for (int i = 0; i < 64; ++i)
+    a.theta[i] = i < r.DR / 2 ? std::pow((double)rope_base, -2.0 * i / r.DR) : 0.0;
+  a.S = r.S;
+  const int ch = r.dtype == MLRA_BF16 ? 8 : 4;
+  const int64_t threads = (int64_t)r.S * r.Q * (r.NB * r.DC / ch + r.DR / 2);
+  const dim3 grid((uint32_t)((threads + 255) / 256));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (r.dtype == MLRA_BF16)
+    hipLaunchKernelGGL(mlra::mlra_append<__bf16>, grid, dim3(256), 0, hs, a);
+  else
+    hipLaunchKernelGGL(mlra::mlra_append<float>, grid, dim3(256), 0, hs, a);
+  return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
 }

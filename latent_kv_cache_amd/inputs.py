@@ -132,6 +132,18 @@ def make_inputs(cfg: DecodeConfig, seed: int | None = None) -> DecodeInputs:
                         q_rope=q_rope, poison_block=poison_block)
 
 
+def make_append_inputs(cfg: DecodeConfig, seed: int | None = None):
+    """New tokens for a cache append: projected branch latents [S][Q][NB][DC]
+    and position keys [S][Q][DR], N(0, 1) float32 (the projection's output,
+    not rounded), from their own stream (seed + 1000003), so the decode inputs
+    of the same config are unchanged."""
+    rng = np.random.default_rng((cfg.seed if seed is None else seed) + 1_000_003)
+    S, Q = cfg.num_seqs, cfg.q_len
+    lat = rng.standard_normal((S, Q, cfg.n_branch, cfg.d_latent), dtype=np.float32)
+    rope = rng.standard_normal((S, Q, cfg.d_rope), dtype=np.float32)
+    return lat, rope
+
+
 def to_device(inp: DecodeInputs, device="cuda") -> Dict[str, "object"]:
     """Copy the inputs to the device as torch tensors of the workload dtype."""
     import torch

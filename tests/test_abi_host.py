@@ -189,3 +189,24 @@ def test_two_phase_entry_points_check_only_their_own_pointers(lib):
     a = list(comb)
     a[3] = ctypes.c_void_p(4096 + 4)      # out must be 16-byte aligned
     assert lib.mlra_decode_combine(*a) == 5
+
+
+def test_cache_append_validates_before_touching_memory(lib):
+    # statuses come from host checks alone: no pointer is dereferenced
+    d = _dims(configs.MLRA4_FUSED)
+    fake = [256 * (i + 1) for i in range(6)]   # aligned, never read
+    ok_args = lambda: fake + [4, 0.5, 10000.0, ctypes.byref(d), None]
+    args = ok_args()
+    args[0] = None
+    assert lib.mlra_cache_append(*args) == 1                     # NULL latent_new
+    for k, v in ((7, float("nan")), (8, 0.0), (8, -1.0), (8, float("inf"))):
+        args = ok_args()
+        args[k] = v
+        assert lib.mlra_cache_append(*args) == 2, (k, v)         # bad scale / base
+    args = ok_args()
+    args[2] = 256 + 8
+    assert lib.mlra_cache_append(*args) == 5                     # misaligned cache
+    args = ok_args()
+    args[6] = 3
+    assert lib.mlra_cache_append(*args) == 3                     # unsupported n_branch
+
