@@ -16,12 +16,16 @@ combine kernel), bracketed by events: roofline.achieved is the split kernel's
 algorithmic bytes (everything above but the outputs) over its average
 per-launch time.
 
+With --outproj it measures the output side (mlra_out_projection: the decode
+call's concatenated output times the absorbed W_O . W_UV weight, model width
+4096) for the workload's rows, next to torch.matmul on the same operands.
 With --append the line instead measures the cache append (mlra_cache_append:
 the new tokens' calibrated latents and rotated position keys written into the
 paged caches) on the workload's layout, default mlra4_append_b4096_q2.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
                        [--workload NAME] [--no-cpu-baseline] [--graph] [--append]
+                       [--outproj]
 """
 from __future__ import annotations
 
@@ -185,14 +189,90 @@ def bench_append(torch, args) -> int:
     return 0
 
 
+OUTPROJ_D = 4096  # model width: H * dv with dv = 128 (not on the pages)
+
+
+def bench_outproj(torch, args) -> int:
+    from latent_kv_cache_amd import api, configs
+    from latent_kv_cache_amd.inputs import make_out_proj_inputs
+
+    cfg = configs.BY_NAME[args.workload or DEFAULT_WORKLOAD]
+    M = cfg.num_seqs * cfg.q_len
+    K = cfg.num_heads * cfg.n_branch * cfg.d_latent
+    D = OUTPROJ_D
+    x, w = make_out_proj_inputs(M, K, D, seed=cfg.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wbytes = D * K * 2
+    nbytes = wbytes + M * K * 2 + M * D * 2
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / wbytes))
+    xd = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    w0 = torch.from_numpy(w).to(dev).to(torch.bfloat16)
+    wps = [api.pack_out_projection_weight(w0) for _ in range(copies)]   # packed once per weight
+    wts = [w0.clone() for _ in range(copies)]                            # for torch.matmul
+    y = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(50_000_000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms = timed(lambda i: api.mlra_out_projection(xd, wps[i % copies], out=y))
+    ms_lib = timed(lambda i: torch.matmul(xd, wts[i % copies].t()))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode output projection HBM GB/s (% of peak)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) decode output, N(0,1/K) absorbed weight)",
+        "config": {"workload": cfg.name, "rows": M, "k": K, "d_model": D, "weight_copies": copies},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "algorithmic_bytes_per_step": nbytes,
+        "torch_matmul_us": round(ms_lib * 1e3, 3),
+        "roofline": {"bound": "hbm", "kernel": "mlra_outproj", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("mlra_outproj", cfg.name)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import out_projection
+        x3 = x.astype(np.float64)[:, None, None, None, :]
+        reps, t_total = 0, 0.0
+        while t_total < 10.0 and reps < 200:
+            t0 = time.perf_counter()
+            out_projection(x3, w)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        per = t_total / reps
+        res["cpu_baseline"] = {
+            "value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} passes of the float64 oracle (NumPy matmul, float64 copy of the "
+                      f"weight included) over the same operands, {per * 1e3:.1f} ms per pass"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([t.get("num_threads", 1) for t in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     """Time the float64 oracle on the host over repeated passes of the batch."""
     from oracle import mlra_decode
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = _blas_threads()
     c = inp.cfg
     nbytes = algorithmic_bytes(inp)["total"]
     reps, t_total = 0, 0.0
@@ -244,6 +324,8 @@ def main() -> int:
                          "mlra4_append_b4096_q2)")
     ap.add_argument("--append", action="store_true",
                     help="measure the cache append instead of decode attention")
+    ap.add_argument("--outproj", action="store_true",
+                    help="measure the output projection instead of decode attention")
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0: enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
@@ -263,6 +345,8 @@ def main() -> int:
         return copy_calibration(torch, args.copy_calibration, args.steps, args.warmup)
     if args.append:
         return bench_append(torch, args)
+    if args.outproj:
+        return bench_outproj(torch, args)
     from latent_kv_cache_amd import api, configs
     from latent_kv_cache_amd.inputs import make_inputs, to_device
 

@@ -248,6 +248,39 @@ mlra_status mlra_cache_append(const float* latent_new, const float* rope_new,
                               int32_t n_branch, float latent_scale, float rope_base,
                               const mlra_decode_dims* dims, void* stream);
 
+/*
+ * The output side of decode as one contraction, in bf16 with float32
+ * accumulation:  y[M][D] = x[M][K] . W^T.
+ * Following the wispaper.ai blog "MLRA: Breaking the Sharding Bottleneck in
+ * Latent Attention", "The Core Insight" (branch outputs are combined after
+ * attention), with one value up-projection W_UV[h][b] (dv x DC) per branch
+ * and the output projection W_O (D x H*dv):
+ *  x  [M][K] bf16, dense: the CONCAT output of mlra_decode_attention viewed
+ *     as [S*Q][H*n_branch*DC] (M = S*Q, K = H*n_branch*DC; it already carries
+ *     out_rescale)
+ *  W  [D][K] bf16: the absorbed weight
+ *     W[n][(h*n_branch + b)*DC + c] = sum_d W_O[n][h*dv + d] * W_UV[h][b][d][c]
+ *  y  [M][D] bf16, dense (nearest, ties to even)
+ * W is a fixed weight: mlra_out_projection_pack rewrites it once, on the
+ * stream, into the order the kernel loads (D*K*2 bytes, caller-owned):
+ *     packed[t][kb][q][l][e] = W[16t + l%16][64kb + 32q + 8(l/16) + e]
+ * for t < D/16, kb < K/64, q < 2, l < 64, e < 8; mlra_out_projection takes
+ * the packed weight. Sizes: 1 <= M <= 128 (decode rows; larger M is an
+ * ordinary GEMM), K a multiple of 512, D a multiple of 128; otherwise
+ * MLRA_ERR_UNSUPPORTED. workspace: at least
+ * mlra_out_projection_workspace_size bytes (0 for some sizes, then it may be
+ * NULL), 16-byte aligned, no initialisation needed. Pointers 16-byte
+ * aligned. Both calls are asynchronous on stream.
+ */
+mlra_status mlra_out_projection_pack(const void* w, void* w_packed, int32_t k, int32_t d,
+                                     void* stream);
+
+mlra_status mlra_out_projection_workspace_size(int32_t m, int32_t k, int32_t d, size_t* bytes);
+
+mlra_status mlra_out_projection(const void* x, const void* w_packed, void* y, int32_t m,
+                                int32_t k, int32_t d, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* mlra_status_string(mlra_status status);
 

@@ -22,7 +22,9 @@ STATUS_NAMES = {0: "MLRA_OK", 1: "MLRA_ERR_NULL_PTR", 2: "MLRA_ERR_BAD_DIMS",
 # Functions include/mlra.h declares (checked against the header by the tests).
 EXPORTS = ("mlra_decode_make_plan", "mlra_decode_workspace_size", "mlra_decode_attention",
            "mla_decode_attention", "mlra_decode_partials", "mlra_decode_combine",
-           "mlra_cache_append", "mlra_status_string", "mlra_version")
+           "mlra_cache_append", "mlra_out_projection_pack", "mlra_out_projection_workspace_size",
+           "mlra_out_projection",
+           "mlra_status_string", "mlra_version")
 
 
 class DecodeDims(ctypes.Structure):
@@ -92,6 +94,12 @@ def load() -> ctypes.CDLL:
         lib.mlra_decode_combine.restype = i32
         lib.mlra_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, f32, f32, dims_p, vp]
         lib.mlra_cache_append.restype = i32
+        lib.mlra_out_projection_pack.argtypes = [vp, vp, i32, i32, vp]
+        lib.mlra_out_projection_pack.restype = i32
+        lib.mlra_out_projection_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        lib.mlra_out_projection_workspace_size.restype = i32
+        lib.mlra_out_projection.argtypes = [vp, vp, vp, i32, i32, i32, vp, sz, vp]
+        lib.mlra_out_projection.restype = i32
         lib.mlra_status_string.argtypes = [i32]
         lib.mlra_status_string.restype = ctypes.c_char_p
         lib.mlra_version.argtypes = []

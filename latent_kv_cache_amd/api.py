@@ -21,6 +21,8 @@ from __future__ import annotations
 
 from typing import Optional, Tuple
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -186,6 +188,64 @@ def mlra_cache_append(latent_new: torch.Tensor, rope_new: torch.Tensor,
                                    block_table.data_ptr(), seq_lens.data_ptr(), int(NB),
                                    float(latent_scale), float(rope_base), dims, stream)
     _lib.check(status, "mlra_cache_append")
+
+
+def pack_out_projection_weight(w: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """Rewrite the absorbed weight w [D][K] (bf16) into the order
+    mlra_out_projection loads (include/mlra.h). Done once per weight."""
+    lib = _lib.load()
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_contiguous() or w.device.type != "cuda":
+        raise ValueError("w must be a contiguous bf16 [D][K] tensor on the GPU")
+    packed = torch.empty_like(w)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device).cuda_stream
+    _lib.check(lib.mlra_out_projection_pack(w.data_ptr(), packed.data_ptr(), w.shape[1],
+                                            w.shape[0], stream), "mlra_out_projection_pack")
+    return packed
+
+
+def out_projection_workspace_bytes(m: int, k: int, d: int) -> int:
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.mlra_out_projection_workspace_size(int(m), int(k), int(d), ctypes.byref(n)),
+               "mlra_out_projection_workspace_size")
+    return int(n.value)
+
+
+def mlra_out_projection(x: torch.Tensor, w_packed: torch.Tensor, *,
+                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """y = x . W^T in bf16 (float32 accumulation): x is the decode call's CONCAT
+    output [S][Q][H][NB][DC] (or already [M][K]); w_packed the absorbed weight
+    [D][K] after pack_out_projection_weight. Returns y [M][D] (or [S][Q][D]
+    for a 5-D x)."""
+    lib = _lib.load()
+    if x.dtype != torch.bfloat16 or w_packed.dtype != torch.bfloat16:
+        raise TypeError("x and w_packed must be bfloat16")
+    if not x.is_contiguous() or not w_packed.is_contiguous():
+        raise ValueError("x and w_packed must be contiguous")
+    lead = tuple(x.shape[:2]) if x.dim() == 5 else None
+    x2 = x.reshape(-1, x.shape[2] * x.shape[3] * x.shape[4]) if x.dim() == 5 else x
+    if x2.dim() != 2 or w_packed.dim() != 2 or w_packed.shape[1] != x2.shape[1]:
+        raise ValueError("x must be [M][K] (or [S][Q][H][NB][DC]) and w_packed [D][K]")
+    if x.device != w_packed.device or x.device.type != "cuda":
+        raise ValueError("x and w_packed must be on the same GPU")
+    M, K = x2.shape
+    D = w_packed.shape[0]
+    if out is None:
+        out = torch.empty((M, D), dtype=torch.bfloat16, device=x.device)
+    if out.numel() != M * D or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bf16 tensor of {M}x{D} elements")
+    need = out_projection_workspace_bytes(M, K, D)
+    if workspace is None and need > 0:
+        workspace = _workspace(x.device, need)
+    wsp = workspace.data_ptr() if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    _lib.check(lib.mlra_out_projection(x2.data_ptr(), w_packed.data_ptr(), out.data_ptr(), M, K, D,
+                                       wsp, wsb, stream), "mlra_out_projection")
+    return out.view(lead + (D,)) if lead else out.view(M, D)
 
 
 def mlra_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,

@@ -1467,6 +1467,183 @@ __global__ void __launch_bounds__(256) mlra_append(AppendParams a) {
 }
 
 // ---------------------------------------------------------------------------
+// output side: value up-projections of every branch and the output
+// projection as one contraction, y[M][D] = x[M][K] . W^T
+// ---------------------------------------------------------------------------
+// x is the decode call's CONCAT output viewed as [S*Q][H*NB*DC] (the wispaper.ai
+// blog "MLRA: Breaking the Sharding Bottleneck in Latent Attention", "The Core
+// Insight": branch outputs are combined after attention; with one value
+// up-projection per branch the head output is the sum of the branches'
+// up-projections), W [D][K] the absorbed weight W_O . W_UV. At decode M is a
+// few dozen rows, so the contraction streams W once from HBM: the bytes of W
+// set the time.
+//
+// W rows are the A operand of v_mfma_f32_16x16x32_bf16 and x rows the B
+// operand. Read straight from a row-major W, the 64 lanes of one load would
+// touch 16 rows in 64 pieces; so W is packed once (it is a fixed weight) into
+// operand order, and every load is one contiguous kilobyte:
+//   packed[t][kb][q][lane][e] = W[16t + lane%16][64kb + 32q + 8(lane/16) + e]
+// (tile t of 16 features, 64-column block kb, MFMA step q < 2, element e < 8).
+// Workgroup (g, c): 128 features (8 tiles, one per wave) over K-chunk c, so
+// that the grid covers every CU (one CU alone draws only some 25 GB/s). The
+// x it needs is staged in LDS with coalesced loads and read by every wave in
+// the same k order as the packed W, so the contraction is unchanged and x
+// crosses the L2 D/128 times instead of D/16. Each wave keeps PF column
+// blocks of its W tile in flight. x is staged for the whole chunk at once
+// when it fits in kOpXBytes of LDS (decode-sized M), else in sub-chunks;
+// staging waits for the wave's earlier loads (loads complete in order), so
+// every sub-chunk boundary drains the W pipeline once. With more than one
+// K-chunk each writes an fp32 partial that mlra_outproj_reduce sums into bf16.
+constexpr int kOpMaxM = 128;
+constexpr int kOpXBytes = 128 * 1024;
+struct OutProjParams {
+  const __bf16* x;   // [M][K]
+  const __bf16* wp;  // packed W
+  __bf16* y;         // [M][D]
+  float* part;       // [KC][M][D] when KC > 1
+  int32_t M, K, D, KC, SB;  // SB: 64-column blocks per staged x sub-chunk
+};
+
+__global__ void __launch_bounds__(256) mlra_outproj_pack(const __bf16* w, __bf16* wp, int32_t K,
+                                                         int32_t D) {
+  // one thread per 16-byte piece of the packed array
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t pieces = (int64_t)D * K / 8;
+  if (i >= pieces) return;
+  const int lane = (int)(i % 64);
+  const int64_t r = i / 64;  // = (t * (K/64) + kb) * 2 + q
+  const int q = (int)(r % 2);
+  const int64_t kb = (r / 2) % (K / 64), t = (r / 2) / (K / 64);
+  const __bf16* src = w + (t * 16 + lane % 16) * (int64_t)K + kb * 64 + 32 * q + 8 * (lane / 16);
+  *reinterpret_cast<u32x4*>(wp + i * 8) = *reinterpret_cast<const u32x4*>(src);
+}
+
+template <int MT>  // 16-row tiles of x
+__global__ void __launch_bounds__(512) mlra_outproj(OutProjParams p) {
+  constexpr int PF = MT <= 2 ? 8 : 4;  // column blocks in flight per wave
+  extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
+  const int pitch = p.SB * 128 + 16;  // LDS bytes per staged x row (16 spare)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, kg = lane >> 4;
+  const int t = blockIdx.x * 8 + wave;  // this wave's 16-feature tile
+  const int kc = blockIdx.y;
+  const int nkb = p.K / 64, nblk = nkb / p.KC;  // column blocks in this K-chunk
+  const int kb0 = kc * nblk;
+  const char* wbase = reinterpret_cast<const char*>(p.wp) + ((int64_t)t * nkb + kb0) * 2048 + lane * 16;
+  bf16x8 a[PF][2];
+  auto load = [&](int blk, int slot) {  // unconditional: past the end it re-reads the last block
+    const int bb = min(blk, nblk - 1);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) a[slot][q] = __builtin_bit_cast(bf16x8, ld16(wbase + bb * 2048 + q * 1024));
+  };
+  auto stage = [&](int b, int n) {  // x rows [0, MT*16) x blocks [b, b + n) of this chunk
+    const int cpr = n * 8;           // 16-byte chunks per row
+    for (int i = threadIdx.x; i < MT * 16 * cpr; i += blockDim.x) {
+      const int row = i / cpr, ch = i - row * cpr;
+      const u32x4 v = ld16(p.x + (int64_t)min(row, p.M - 1) * p.K + (kb0 + b) * 64 + ch * 8);
+      *reinterpret_cast<u32x4*>(xs + row * pitch + ch * 16) = row < p.M ? v : u32x4{};
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < PF; ++i) load(i, i);
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{};
+  const unsigned char* xl = xs + r * pitch + 16 * kg;
+  for (int b0 = 0; b0 < nblk; b0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int b = b0 + i;  // block; its W sits in slot i
+      if (b < nblk) {        // uniform
+        const int sb = b % p.SB;
+        if (sb == 0) {  // next x sub-chunk
+          __syncthreads();
+          stage(b, min(p.SB, nblk - b));
+          __syncthreads();
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const bf16x8 bv = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(xl + mt * 16 * pitch + sb * 128 + q * 64));
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][q], bv, acc[mt], 0, 0, 0);
+          }
+      }
+      load(b + PF, i);
+    }
+  }
+  // acc[mt][e] is y[mt*16 + lane%16][16t + 4(lane/16) + e] over this K-chunk
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + r;
+    if (m >= p.M) continue;
+    const int64_t col = 16 * t + 4 * kg;
+    if (p.KC == 1) {
+      __bf16 o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[mt][e];
+      *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.D + col) = __builtin_bit_cast(uint2, o);
+    } else {
+      *reinterpret_cast<f32x4*>(p.part + ((int64_t)kc * p.M + m) * p.D + col) = acc[mt];
+    }
+  }
+}
+
+// y[m][n] = bf16(sum over K-chunks of the partials, in chunk order), four
+// outputs per thread, every chunk's load in flight together (KC <= KMAX).
+template <int KMAX>
+__global__ void __launch_bounds__(256) mlra_outproj_reduce(OutProjParams p) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int64_t total = (int64_t)p.M * p.D;
+  if (i >= total) return;
+  f32x4 v[KMAX];
+#pragma unroll
+  for (int c = 0; c < KMAX; ++c)
+    v[c] = *reinterpret_cast<const f32x4*>(p.part + (int64_t)min(c, p.KC - 1) * total + i);
+  f32x4 sum = v[0];
+#pragma unroll
+  for (int c = 1; c < KMAX; ++c) sum = c < p.KC ? sum + v[c] : sum;
+  __bf16 o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (__bf16)sum[e];
+  *reinterpret_cast<uint2*>(p.y + i) = __builtin_bit_cast(uint2, o);
+}
+
+// K-chunks: the fewest that give about 256 workgroups (one per CU), each
+// chunk a whole number of 64-column blocks.
+static int outproj_kc(int K, int D) {
+  const int groups = D / 128;
+  for (int kc = 1; kc <= 32 && kc <= K / 64; ++kc)
+    if (K % (kc * 64) == 0 && groups * kc >= 256) return kc;
+  for (int kc = 32; kc >= 1; --kc)  // at most 32 chunks (the reduce keeps them in flight)
+    if (K % (kc * 64) == 0) return kc;
+  return 1;
+}
+// 64-column blocks of x staged at a time: the whole chunk when it fits.
+static int outproj_sb(int M, int K, int KC) {
+  const int rows = (M + 15) / 16 * 16, nblk = K / 64 / KC;
+  int sb = nblk;
+  while (sb > 1 && rows * (sb * 128 + 16) > kOpXBytes) --sb;
+  return sb;
+}
+template <int MT>
+static hipError_t outproj_launch(dim3 grid, const OutProjParams& p, hipStream_t st) {
+  static bool attr_set = false;  // per instance; the call is idempotent
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mlra_outproj<MT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             kOpXBytes + 16 * kOpMaxM);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const size_t lds = (size_t)MT * 16 * (p.SB * 128 + 16);
+  hipLaunchKernelGGL(mlra_outproj<MT>, grid, dim3(512), lds, st, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <int NB, int DC, int DR, int NT>
@@ -1843,5 +2020,68 @@ extern "C" mlra_status mlra_cache_append(const float* latent_new, const float* r
     hipLaunchKernelGGL(mlra::mlra_append<__bf16>, grid, dim3(256), 0, hs, a);
   else
     hipLaunchKernelGGL(mlra::mlra_append<float>, grid, dim3(256), 0, hs, a);
+  return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
+}
+
+extern "C" mlra_status mlra_out_projection_pack(const void* w, void* w_packed, int32_t k, int32_t d,
+                                                void* stream) {
+  if (!w || !w_packed) return MLRA_ERR_NULL_PTR;
+  if (k < 1 || d < 1) return MLRA_ERR_BAD_DIMS;
+  if (k % 512 || d % 128) return MLRA_ERR_UNSUPPORTED;
+  if (!mlra::aligned16(w) || !mlra::aligned16(w_packed)) return MLRA_ERR_ALIGNMENT;
+  const int64_t pieces = (int64_t)k * d / 8;
+  hipLaunchKernelGGL(mlra::mlra_outproj_pack, dim3((uint32_t)((pieces + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const __bf16*>(w),
+                     static_cast<__bf16*>(w_packed), k, d);
+  return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
+}
+
+extern "C" mlra_status mlra_out_projection_workspace_size(int32_t m, int32_t k, int32_t d,
+                                                          size_t* bytes) {
+  if (!bytes) return MLRA_ERR_NULL_PTR;
+  if (m < 1 || k < 1 || d < 1) return MLRA_ERR_BAD_DIMS;
+  if (m > mlra::kOpMaxM || k % 512 || d % 128) return MLRA_ERR_UNSUPPORTED;
+  const int kc = mlra::outproj_kc(k, d);
+  *bytes = kc > 1 ? (size_t)kc * m * d * 4 : 0;
+  return MLRA_OK;
+}
+
+extern "C" mlra_status mlra_out_projection(const void* x, const void* w_packed, void* y, int32_t m,
+                                           int32_t k, int32_t d, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  const mlra_status st = mlra_out_projection_workspace_size(m, k, d, &need);
+  if (st != MLRA_OK) return st;
+  if (!x || !w_packed || !y || (need > 0 && !workspace)) return MLRA_ERR_NULL_PTR;
+  if (workspace_bytes < need) return MLRA_ERR_WORKSPACE;
+  if (!mlra::aligned16(x) || !mlra::aligned16(w_packed) || !mlra::aligned16(y) ||
+      (need > 0 && !mlra::aligned16(workspace)))
+    return MLRA_ERR_ALIGNMENT;
+  mlra::OutProjParams p;
+  p.x = static_cast<const __bf16*>(x);
+  p.wp = static_cast<const __bf16*>(w_packed);
+  p.y = static_cast<__bf16*>(y);
+  p.part = static_cast<float*>(workspace);
+  p.M = m;
+  p.K = k;
+  p.D = d;
+  p.KC = mlra::outproj_kc(k, d);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const dim3 grid((uint32_t)(d / 128), (uint32_t)p.KC);
+  p.SB = mlra::outproj_sb(m, k, p.KC);
+  const int mt = (m + 15) / 16;
+  hipError_t e;
+  if (mt <= 1) e = mlra::outproj_launch<1>(grid, p, hs);
+  else if (mt <= 2) e = mlra::outproj_launch<2>(grid, p, hs);
+  else if (mt <= 4) e = mlra::outproj_launch<4>(grid, p, hs);
+  else e = mlra::outproj_launch<8>(grid, p, hs);
+  if (e != hipSuccess) return MLRA_ERR_HIP;
+  if (p.KC > 1) {
+    const int64_t threads = ((int64_t)m * d + 3) / 4;
+    const dim3 rg((uint32_t)((threads + 255) / 256));
+    if (p.KC <= 8) hipLaunchKernelGGL(mlra::mlra_outproj_reduce<8>, rg, dim3(256), 0, hs, p);
+    else if (p.KC <= 16) hipLaunchKernelGGL(mlra::mlra_outproj_reduce<16>, rg, dim3(256), 0, hs, p);
+    else hipLaunchKernelGGL(mlra::mlra_outproj_reduce<32>, rg, dim3(256), 0, hs, p);
+  }
   return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
 }

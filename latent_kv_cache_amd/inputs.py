@@ -144,6 +144,16 @@ def make_append_inputs(cfg: DecodeConfig, seed: int | None = None):
     return lat, rope
 
 
+def make_out_proj_inputs(m: int, k: int, d: int, seed: int):
+    """Operands of the output projection: x [m][k] N(0, 1) and an absorbed
+    weight w [d][k] N(0, 1/k), both rounded to bf16 (float32 arrays holding
+    bf16-exact values)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    w = rng.standard_normal((d, k), dtype=np.float32) * np.float32(1.0 / np.sqrt(k))
+    return round_to_bf16(x), round_to_bf16(w)
+
+
 def to_device(inp: DecodeInputs, device="cuda") -> Dict[str, "object"]:
     """Copy the inputs to the device as torch tensors of the workload dtype."""
     import torch

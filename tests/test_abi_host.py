@@ -210,3 +210,18 @@ def test_cache_append_validates_before_touching_memory(lib):
     args[6] = 3
     assert lib.mlra_cache_append(*args) == 3                     # unsupported n_branch
 
+
+def test_out_projection_validation(lib):
+    n = ctypes.c_size_t(123)
+    assert lib.mlra_out_projection_workspace_size(16, 4096, 4096, ctypes.byref(n)) == 0
+    assert n.value == 8 * 16 * 4096 * 4          # eight K-chunks of float32 partials
+    assert lib.mlra_out_projection_workspace_size(0, 512, 128, ctypes.byref(n)) == 2
+    for m, k, d in ((129, 512, 128), (16, 768, 128), (16, 512, 96)):  # M, K or D off the grid
+        assert lib.mlra_out_projection_workspace_size(m, k, d, ctypes.byref(n)) == 3
+    fake = 4096
+    assert lib.mlra_out_projection(None, fake, fake, 16, 4096, 4096, fake, 1 << 22, None) == 1
+    assert lib.mlra_out_projection(fake, fake, fake, 16, 4096, 4096, fake, 16, None) == 4
+    assert lib.mlra_out_projection(fake + 2, fake, fake, 16, 4096, 4096, fake, 1 << 22, None) == 5
+    assert lib.mlra_out_projection_pack(fake, None, 4096, 4096, None) == 1
+    assert lib.mlra_out_projection_pack(fake, fake, 100, 4096, None) == 3
+    assert lib.mlra_out_projection_pack(fake, fake + 8, 4096, 4096, None) == 5
