@@ -60,11 +60,19 @@ def algorithmic_bytes(inp) -> dict:
     return dict(total=total, cache=cache, out=out, lse=lse, kv_tokens=int(L.sum()))
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the kernel sources, to tell whether a stored counter
-    measurement still describes the kernel that runs."""
+KERNEL_SOURCES = {
+    "decode": ("mlra_kernels.hip", "mlra_internal.h", "mlra_device.h"),
+    "step": ("mlra_step_kernels.hip", "mlra_internal.h", "mlra_device.h"),
+}
+
+
+def kernel_source_digest(kernel: str = "mlra_split_pc") -> str:
+    """sha256 over the sources that define a kernel (the decode kernels, or
+    the append and output-projection kernels), to tell whether a stored
+    counter measurement still describes the kernel that runs."""
+    family = "step" if kernel.startswith(("mlra_append", "mlra_outproj")) else "decode"
     h = hashlib.sha256()
-    for name in ("mlra_kernels.hip", "mlra_internal.h"):
+    for name in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "latent_kv_cache_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -87,7 +95,7 @@ def measured_traffic(kernel: str, workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_digest():
+    if fields.get("kernel_source_sha256") != kernel_source_digest(kernel):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])

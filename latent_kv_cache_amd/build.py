@@ -22,6 +22,8 @@ HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC"
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+# HIP translation units: the decode kernels, and the kernels of the steps around them.
+HIP_SOURCES = ("mlra_kernels.hip", "mlra_step_kernels.hip")
 
 
 def hipcc() -> str:
@@ -48,14 +50,15 @@ def build(verbose: bool = False, save_temps: str | None = None) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory() as tmp:
         host_o = os.path.join(tmp, "mlra_host.o")
-        kern_o = os.path.join(tmp, "mlra_kernels.o")
         _run([cc, *HOST_FLAGS, "-c", os.path.join(CSRC, "mlra_host.cpp"), "-o", host_o], verbose)
         extra = [f"-save-temps={save_temps}"] if save_temps else []
-        _run([cc, *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, "mlra_kernels.hip"),
-              "-o", kern_o], verbose)
+        objs = [host_o]
+        for src in HIP_SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            _run([cc, *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
         tmp_lib = LIB + ".tmp"
-        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", host_o, kern_o, "-o", tmp_lib],
-             verbose)
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
         os.replace(tmp_lib, LIB)
     return LIB
 

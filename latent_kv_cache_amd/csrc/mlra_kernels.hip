@@ -31,14 +31,10 @@
 #include <algorithm>
 #include <cmath>
 
+#include "mlra_device.h"
 #include "mlra_internal.h"
 
 namespace mlra {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -100,15 +96,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ u32x4 ld16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
 // ---------------------------------------------------------------------------
 // bf16 split kernel (MFMA)
 // ---------------------------------------------------------------------------
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
 // LDS transpose read (gfx950 ds_read_b64_tr_b16): within each 16-lane group,
 // lane j supplies the address of 4 bf16 at row j/4, column 4*(j%4) of a 4x16
 // block; lane i receives column i, rows 0..3 of that block.
@@ -1377,273 +1367,6 @@ __global__ void __launch_bounds__(256) mlra_combine_cols(CombineParams c) {
 }
 
 // ---------------------------------------------------------------------------
-// cache append: the new tokens' latents and rotated position keys
-// ---------------------------------------------------------------------------
-// What a token holds in the cache follows the wispaper.ai blog "MLRA: Breaking
-// the Sharding Bottleneck in Latent Attention", "The Core Insight" (one latent
-// per branch plus one decoupled position key shared by the branches) and
-// "Mathematical Calibration" (latents multiplied by a calibration factor).
-// The key is rotated by the rotary position embedding (adjacent pairs
-// (2i, 2i+1) turned by p * base^(-2i/DR)). Threads are numbered over (token,
-// piece), so every lane of a wave has work: a latent piece is one 16-byte
-// chunk, a key piece one pair (its double-precision sine and cosine are the
-// long pole, so each thread takes one). The new values and the sequence
-// length are loaded before the block id, which depends on the length. Values
-// are formed in double (the latent product of two floats is exact there;
-// angles keep full precision at positions in the millions) and rounded once
-// to the cache type.
-struct AppendParams {
-  const float* lat_new;   // [S][Q][NB][DC]
-  const float* rope_new;  // [S][Q][DR]
-  void* lat;
-  void* rope;
-  const int32_t* table;
-  const int32_t* seq_lens;
-  int32_t S, Q, NB, DC, DR, max_blocks, num_blocks;
-  int64_t lsb, lst, lsbr, rsb, rst;
-  double latent_scale;
-  double theta[64];  // rope_base^(-2i/DR) for pair i < DR/2, computed on the host
-};
-
-// Nearest bf16 of a double, ties to even, in one rounding: round the double
-// to 8 significant bits in place, after which narrowing to float and to bf16
-// is exact (finite values in float's normal range).
-__device__ __forceinline__ __bf16 bf16_from_double(double x) {
-  uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
-  u += ((u >> 45) & 1) + ((uint64_t(1) << 44) - 1);
-  u &= ~((uint64_t(1) << 45) - 1);
-  return (__bf16)(float)__longlong_as_double(static_cast<long long>(u));
-}
-__device__ __forceinline__ void cvt_from_double(__bf16& d, double x) { d = bf16_from_double(x); }
-__device__ __forceinline__ void cvt_from_double(float& d, double x) { d = (float)x; }
-
-template <typename T>
-__global__ void __launch_bounds__(256) mlra_append(AppendParams a) {
-  constexpr int CH = 16 / sizeof(T);  // latent elements per 16-byte store
-  const int lch = a.DC / CH, nl = a.NB * lch, per_tok = nl + a.DR / 2;
-  const int x = blockIdx.x * blockDim.x + threadIdx.x;
-  if (x >= a.S * a.Q * per_tok) return;
-  const int tok = x / per_tok;  // = s * Q + j
-  const int c = x - tok * per_tok;
-  const int s = tok / a.Q, j = tok - s * a.Q;
-  const bool is_lat = c < nl;
-  const int b = is_lat ? c / lch : 0;
-  const int c0 = is_lat ? (c - b * lch) * CH : 2 * (c - nl);
-  float in[CH];
-  if (is_lat) {
-    const float* src = a.lat_new + ((int64_t)tok * a.NB + b) * a.DC + c0;
-#pragma unroll
-    for (int q = 0; q < CH / 4; ++q) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) in[4 * q + e] = v[e];
-    }
-  } else {
-    const float2 v = *reinterpret_cast<const float2*>(a.rope_new + (int64_t)tok * a.DR + c0);
-    in[0] = v.x;
-    in[1] = v.y;
-  }
-  const int64_t p = (int64_t)a.seq_lens[s] - a.Q + j;  // position of new token j
-  if (p < 0 || p >= (int64_t)a.max_blocks * kBlock) return;
-  const int blk = a.table[(int64_t)s * a.max_blocks + p / kBlock];
-  if (blk < 0 || blk >= a.num_blocks) return;  // never write outside the cache
-  const int slot = (int)(p % kBlock);
-  if (is_lat) {
-    T outv[CH];
-#pragma unroll
-    for (int e = 0; e < CH; ++e) cvt_from_double(outv[e], (double)in[e] * a.latent_scale);
-    T* dst = static_cast<T*>(a.lat) + blk * a.lsb + slot * a.lst + b * a.lsbr + c0;
-    *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, outv);
-  } else {
-    double sn, cs;
-    sincos((double)p * a.theta[c0 / 2], &sn, &cs);
-    T o2[2];
-    cvt_from_double(o2[0], (double)in[0] * cs - (double)in[1] * sn);
-    cvt_from_double(o2[1], (double)in[0] * sn + (double)in[1] * cs);
-    T* dst = static_cast<T*>(a.rope) + blk * a.rsb + slot * a.rst + c0;
-    dst[0] = o2[0];
-    dst[1] = o2[1];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// output side: value up-projections of every branch and the output
-// projection as one contraction, y[M][D] = x[M][K] . W^T
-// ---------------------------------------------------------------------------
-// x is the decode call's CONCAT output viewed as [S*Q][H*NB*DC] (the wispaper.ai
-// blog "MLRA: Breaking the Sharding Bottleneck in Latent Attention", "The Core
-// Insight": branch outputs are combined after attention; with one value
-// up-projection per branch the head output is the sum of the branches'
-// up-projections), W [D][K] the absorbed weight W_O . W_UV. At decode M is a
-// few dozen rows, so the contraction streams W once from HBM: the bytes of W
-// set the time.
-//
-// W rows are the A operand of v_mfma_f32_16x16x32_bf16 and x rows the B
-// operand. Read straight from a row-major W, the 64 lanes of one load would
-// touch 16 rows in 64 pieces; so W is packed once (it is a fixed weight) into
-// operand order, and every load is one contiguous kilobyte:
-//   packed[t][kb][q][lane][e] = W[16t + lane%16][64kb + 32q + 8(lane/16) + e]
-// (tile t of 16 features, 64-column block kb, MFMA step q < 2, element e < 8).
-// Workgroup (g, c): 128 features (8 tiles, one per wave) over K-chunk c, so
-// that the grid covers every CU (one CU alone draws only some 25 GB/s). The
-// x it needs is staged in LDS with coalesced loads and read by every wave in
-// the same k order as the packed W, so the contraction is unchanged and x
-// crosses the L2 D/128 times instead of D/16. Each wave keeps PF column
-// blocks of its W tile in flight. x is staged for the whole chunk at once
-// when it fits in kOpXBytes of LDS (decode-sized M), else in sub-chunks;
-// staging waits for the wave's earlier loads (loads complete in order), so
-// every sub-chunk boundary drains the W pipeline once. With more than one
-// K-chunk each writes an fp32 partial that mlra_outproj_reduce sums into bf16.
-constexpr int kOpMaxM = 128;
-constexpr int kOpXBytes = 128 * 1024;
-struct OutProjParams {
-  const __bf16* x;   // [M][K]
-  const __bf16* wp;  // packed W
-  __bf16* y;         // [M][D]
-  float* part;       // [KC][M][D] when KC > 1
-  int32_t M, K, D, KC, SB;  // SB: 64-column blocks per staged x sub-chunk
-};
-
-__global__ void __launch_bounds__(256) mlra_outproj_pack(const __bf16* w, __bf16* wp, int32_t K,
-                                                         int32_t D) {
-  // one thread per 16-byte piece of the packed array
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t pieces = (int64_t)D * K / 8;
-  if (i >= pieces) return;
-  const int lane = (int)(i % 64);
-  const int64_t r = i / 64;  // = (t * (K/64) + kb) * 2 + q
-  const int q = (int)(r % 2);
-  const int64_t kb = (r / 2) % (K / 64), t = (r / 2) / (K / 64);
-  const __bf16* src = w + (t * 16 + lane % 16) * (int64_t)K + kb * 64 + 32 * q + 8 * (lane / 16);
-  *reinterpret_cast<u32x4*>(wp + i * 8) = *reinterpret_cast<const u32x4*>(src);
-}
-
-template <int MT>  // 16-row tiles of x
-__global__ void __launch_bounds__(512) mlra_outproj(OutProjParams p) {
-  constexpr int PF = MT <= 2 ? 8 : 4;  // column blocks in flight per wave
-  extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
-  const int pitch = p.SB * 128 + 16;  // LDS bytes per staged x row (16 spare)
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, kg = lane >> 4;
-  const int t = blockIdx.x * 8 + wave;  // this wave's 16-feature tile
-  const int kc = blockIdx.y;
-  const int nkb = p.K / 64, nblk = nkb / p.KC;  // column blocks in this K-chunk
-  const int kb0 = kc * nblk;
-  const char* wbase = reinterpret_cast<const char*>(p.wp) + ((int64_t)t * nkb + kb0) * 2048 + lane * 16;
-  bf16x8 a[PF][2];
-  auto load = [&](int blk, int slot) {  // unconditional: past the end it re-reads the last block
-    const int bb = min(blk, nblk - 1);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) a[slot][q] = __builtin_bit_cast(bf16x8, ld16(wbase + bb * 2048 + q * 1024));
-  };
-  auto stage = [&](int b, int n) {  // x rows [0, MT*16) x blocks [b, b + n) of this chunk
-    const int cpr = n * 8;           // 16-byte chunks per row
-    for (int i = threadIdx.x; i < MT * 16 * cpr; i += blockDim.x) {
-      const int row = i / cpr, ch = i - row * cpr;
-      const u32x4 v = ld16(p.x + (int64_t)min(row, p.M - 1) * p.K + (kb0 + b) * 64 + ch * 8);
-      *reinterpret_cast<u32x4*>(xs + row * pitch + ch * 16) = row < p.M ? v : u32x4{};
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < PF; ++i) load(i, i);
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{};
-  const unsigned char* xl = xs + r * pitch + 16 * kg;
-  for (int b0 = 0; b0 < nblk; b0 += PF) {
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int b = b0 + i;  // block; its W sits in slot i
-      if (b < nblk) {        // uniform
-        const int sb = b % p.SB;
-        if (sb == 0) {  // next x sub-chunk
-          __syncthreads();
-          stage(b, min(p.SB, nblk - b));
-          __syncthreads();
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const bf16x8 bv = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(xl + mt * 16 * pitch + sb * 128 + q * 64));
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][q], bv, acc[mt], 0, 0, 0);
-          }
-      }
-      load(b + PF, i);
-    }
-  }
-  // acc[mt][e] is y[mt*16 + lane%16][16t + 4(lane/16) + e] over this K-chunk
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + r;
-    if (m >= p.M) continue;
-    const int64_t col = 16 * t + 4 * kg;
-    if (p.KC == 1) {
-      __bf16 o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[mt][e];
-      *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.D + col) = __builtin_bit_cast(uint2, o);
-    } else {
-      *reinterpret_cast<f32x4*>(p.part + ((int64_t)kc * p.M + m) * p.D + col) = acc[mt];
-    }
-  }
-}
-
-// y[m][n] = bf16(sum over K-chunks of the partials, in chunk order), four
-// outputs per thread, every chunk's load in flight together (KC <= KMAX).
-template <int KMAX>
-__global__ void __launch_bounds__(256) mlra_outproj_reduce(OutProjParams p) {
-  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  const int64_t total = (int64_t)p.M * p.D;
-  if (i >= total) return;
-  f32x4 v[KMAX];
-#pragma unroll
-  for (int c = 0; c < KMAX; ++c)
-    v[c] = *reinterpret_cast<const f32x4*>(p.part + (int64_t)min(c, p.KC - 1) * total + i);
-  f32x4 sum = v[0];
-#pragma unroll
-  for (int c = 1; c < KMAX; ++c) sum = c < p.KC ? sum + v[c] : sum;
-  __bf16 o[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = (__bf16)sum[e];
-  *reinterpret_cast<uint2*>(p.y + i) = __builtin_bit_cast(uint2, o);
-}
-
-// K-chunks: the fewest that give about 256 workgroups (one per CU), each
-// chunk a whole number of 64-column blocks.
-static int outproj_kc(int K, int D) {
-  const int groups = D / 128;
-  for (int kc = 1; kc <= 32 && kc <= K / 64; ++kc)
-    if (K % (kc * 64) == 0 && groups * kc >= 256) return kc;
-  for (int kc = 32; kc >= 1; --kc)  // at most 32 chunks (the reduce keeps them in flight)
-    if (K % (kc * 64) == 0) return kc;
-  return 1;
-}
-// 64-column blocks of x staged at a time: the whole chunk when it fits.
-static int outproj_sb(int M, int K, int KC) {
-  const int rows = (M + 15) / 16 * 16, nblk = K / 64 / KC;
-  int sb = nblk;
-  while (sb > 1 && rows * (sb * 128 + 16) > kOpXBytes) --sb;
-  return sb;
-}
-template <int MT>
-static hipError_t outproj_launch(dim3 grid, const OutProjParams& p, hipStream_t st) {
-  static bool attr_set = false;  // per instance; the call is idempotent
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mlra_outproj<MT>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             kOpXBytes + 16 * kOpMaxM);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const size_t lds = (size_t)MT * 16 * (p.SB * 128 + 16);
-  hipLaunchKernelGGL(mlra_outproj<MT>, grid, dim3(512), lds, st, p);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <int NB, int DC, int DR, int NT>
@@ -1787,13 +1510,11 @@ static int device_cus(int* out) {
   return 0;
 }
 
-static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Which kernels one call enqueues: the split kernel (partial results of
 // every split into the workspace), the combine kernel, or both.
 enum Phase { kPartials = 1, kCombine = 2, kBoth = 3 };
 
-static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
 static mlra_status decode(int phases, const void* q_latent, const void* q_rope,
                           const void* latent_cache, const void* rope_cache,
@@ -1973,115 +1694,4 @@ extern "C" mlra_status mlra_decode_combine(const int32_t* seq_lens, int32_t n_br
   return mlra::decode(mlra::kCombine, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens,
                       n_branch, 1.0f, out_rescale, out, lse, dims, const_cast<void*>(workspace),
                       workspace_bytes, stream);
-}
-
-extern "C" mlra_status mlra_cache_append(const float* latent_new, const float* rope_new,
-                                         void* latent_cache, void* rope_cache,
-                                         const int32_t* block_table, const int32_t* seq_lens,
-                                         int32_t n_branch, float latent_scale, float rope_base,
-                                         const mlra_decode_dims* dims, void* stream) {
-  mlra::Resolved r;
-  const mlra_status st = mlra::resolve_dims(dims, n_branch, &r);
-  if (st != MLRA_OK) return st;
-  if (!latent_new || !rope_new || !latent_cache || !rope_cache || !block_table || !seq_lens)
-    return MLRA_ERR_NULL_PTR;
-  if (!std::isfinite(latent_scale) || !std::isfinite(rope_base) || !(rope_base > 0.f))
-    return MLRA_ERR_BAD_DIMS;
-  if (!mlra::aligned16(latent_new) || !mlra::aligned16(rope_new) || !mlra::aligned16(latent_cache) ||
-      !mlra::aligned16(rope_cache) || !mlra::aligned4(block_table) || !mlra::aligned4(seq_lens))
-    return MLRA_ERR_ALIGNMENT;
-  mlra::AppendParams a;
-  a.lat_new = latent_new;
-  a.rope_new = rope_new;
-  a.lat = latent_cache;
-  a.rope = rope_cache;
-  a.table = block_table;
-  a.seq_lens = seq_lens;
-  a.Q = r.Q;
-  a.NB = r.NB;
-  a.DC = r.DC;
-  a.DR = r.DR;
-  a.max_blocks = r.max_blocks;
-  a.num_blocks = r.num_blocks;
-  a.lsb = r.lsb;
-  a.lst = r.lst;
-  a.lsbr = r.lsbr;
-  a.rsb = r.rsb;
-  a.rst = r.rst;
-  a.latent_scale = latent_scale;
-  for (int i = 0; i < 64; ++i)
-    a.theta[i] = i < r.DR / 2 ? std::pow((double)rope_base, -2.0 * i / r.DR) : 0.0;
-  a.S = r.S;
-  const int ch = r.dtype == MLRA_BF16 ? 8 : 4;
-  const int64_t threads = (int64_t)r.S * r.Q * (r.NB * r.DC / ch + r.DR / 2);
-  const dim3 grid((uint32_t)((threads + 255) / 256));
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (r.dtype == MLRA_BF16)
-    hipLaunchKernelGGL(mlra::mlra_append<__bf16>, grid, dim3(256), 0, hs, a);
-  else
-    hipLaunchKernelGGL(mlra::mlra_append<float>, grid, dim3(256), 0, hs, a);
-  return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
-}
-
-extern "C" mlra_status mlra_out_projection_pack(const void* w, void* w_packed, int32_t k, int32_t d,
-                                                void* stream) {
-  if (!w || !w_packed) return MLRA_ERR_NULL_PTR;
-  if (k < 1 || d < 1) return MLRA_ERR_BAD_DIMS;
-  if (k % 512 || d % 128) return MLRA_ERR_UNSUPPORTED;
-  if (!mlra::aligned16(w) || !mlra::aligned16(w_packed)) return MLRA_ERR_ALIGNMENT;
-  const int64_t pieces = (int64_t)k * d / 8;
-  hipLaunchKernelGGL(mlra::mlra_outproj_pack, dim3((uint32_t)((pieces + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const __bf16*>(w),
-                     static_cast<__bf16*>(w_packed), k, d);
-  return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
-}
-
-extern "C" mlra_status mlra_out_projection_workspace_size(int32_t m, int32_t k, int32_t d,
-                                                          size_t* bytes) {
-  if (!bytes) return MLRA_ERR_NULL_PTR;
-  if (m < 1 || k < 1 || d < 1) return MLRA_ERR_BAD_DIMS;
-  if (m > mlra::kOpMaxM || k % 512 || d % 128) return MLRA_ERR_UNSUPPORTED;
-  const int kc = mlra::outproj_kc(k, d);
-  *bytes = kc > 1 ? (size_t)kc * m * d * 4 : 0;
-  return MLRA_OK;
-}
-
-extern "C" mlra_status mlra_out_projection(const void* x, const void* w_packed, void* y, int32_t m,
-                                           int32_t k, int32_t d, void* workspace,
-                                           size_t workspace_bytes, void* stream) {
-  size_t need = 0;
-  const mlra_status st = mlra_out_projection_workspace_size(m, k, d, &need);
-  if (st != MLRA_OK) return st;
-  if (!x || !w_packed || !y || (need > 0 && !workspace)) return MLRA_ERR_NULL_PTR;
-  if (workspace_bytes < need) return MLRA_ERR_WORKSPACE;
-  if (!mlra::aligned16(x) || !mlra::aligned16(w_packed) || !mlra::aligned16(y) ||
-      (need > 0 && !mlra::aligned16(workspace)))
-    return MLRA_ERR_ALIGNMENT;
-  mlra::OutProjParams p;
-  p.x = static_cast<const __bf16*>(x);
-  p.wp = static_cast<const __bf16*>(w_packed);
-  p.y = static_cast<__bf16*>(y);
-  p.part = static_cast<float*>(workspace);
-  p.M = m;
-  p.K = k;
-  p.D = d;
-  p.KC = mlra::outproj_kc(k, d);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  const dim3 grid((uint32_t)(d / 128), (uint32_t)p.KC);
-  p.SB = mlra::outproj_sb(m, k, p.KC);
-  const int mt = (m + 15) / 16;
-  hipError_t e;
-  if (mt <= 1) e = mlra::outproj_launch<1>(grid, p, hs);
-  else if (mt <= 2) e = mlra::outproj_launch<2>(grid, p, hs);
-  else if (mt <= 4) e = mlra::outproj_launch<4>(grid, p, hs);
-  else e = mlra::outproj_launch<8>(grid, p, hs);
-  if (e != hipSuccess) return MLRA_ERR_HIP;
-  if (p.KC > 1) {
-    const int64_t threads = ((int64_t)m * d + 3) / 4;
-    const dim3 rg((uint32_t)((threads + 255) / 256));
-    if (p.KC <= 8) hipLaunchKernelGGL(mlra::mlra_outproj_reduce<8>, rg, dim3(256), 0, hs, p);
-    else if (p.KC <= 16) hipLaunchKernelGGL(mlra::mlra_outproj_reduce<16>, rg, dim3(256), 0, hs, p);
-    else hipLaunchKernelGGL(mlra::mlra_outproj_reduce<32>, rg, dim3(256), 0, hs, p);
-  }
-  return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
 }

@@ -22,12 +22,14 @@ pytestmark = pytest.mark.skipif(shutil.which(build.hipcc()) is None and not os.p
 
 @pytest.fixture(scope="module")
 def remarks():
+    text = ""
     with tempfile.TemporaryDirectory() as tmp:
-        cmd = [build.hipcc(), *build.HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
-               os.path.join(build.CSRC, "mlra_kernels.hip"), "-o", os.path.join(tmp, "k.o")]
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        assert res.returncode == 0, res.stderr[-2000:]
-        text = res.stdout + res.stderr
+        for src in build.HIP_SOURCES:
+            cmd = [build.hipcc(), *build.HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+                   os.path.join(build.CSRC, src), "-o", os.path.join(tmp, src + ".o")]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            assert res.returncode == 0, res.stderr[-2000:]
+            text += res.stdout + res.stderr
     kernels = {}
     name = None
     for line in text.splitlines():
@@ -44,7 +46,8 @@ def remarks():
 
 def test_every_kernel_is_reported(remarks):
     names = " ".join(remarks)
-    for kern in ("mlra_split_pc", "mlra_split_mfma", "mlra_split_valu", "mlra_combine"):
+    for kern in ("mlra_split_pc", "mlra_split_mfma", "mlra_split_valu", "mlra_combine",
+                 "mlra_append", "mlra_outproj_pack", "mlra_outproj", "mlra_outproj_reduce"):
         assert kern in names
 
 
