@@ -42,6 +42,13 @@ Parity pins (tests/test_oracle.py), per function:
                              sum of single-branch shares; negative control vs
                              MLA-style sum-before-softmax; Gaussian-tilting
                              statistics at full workload size.
+                             Prefill regime (tests/test_oracle_prefill.py,
+                             many causal query tokens): torch SDPA with its
+                             own causal flag (whole-sequence prefill) and with
+                             a position mask (a chunk after cached context);
+                             chunked prefill == whole prefill; the first
+                             token sees only itself; planted visibility
+                             mistakes caught.
   mlra_decode_bruteforce  -- hand-derived golden example; closed forms.
   mlra_expanded           -- torch.nn.functional.scaled_dot_product_attention.
   mla_expanded            -- torch SDPA (one softmax over a single latent).
