@@ -63,6 +63,7 @@ def algorithmic_bytes(inp) -> dict:
 KERNEL_SOURCES = {
     "decode": ("mlra_kernels.hip", "mlra_internal.h", "mlra_device.h"),
     "step": ("mlra_step_kernels.hip", "mlra_internal.h", "mlra_device.h"),
+    "prefill": ("mlra_prefill_kernels.hip", "mlra_internal.h", "mlra_device.h"),
 }
 
 
@@ -70,7 +71,8 @@ def kernel_source_digest(kernel: str = "mlra_split_pc") -> str:
     """sha256 over the sources that define a kernel (the decode kernels, or
     the append and output-projection kernels), to tell whether a stored
     counter measurement still describes the kernel that runs."""
-    family = "step" if kernel.startswith(("mlra_append", "mlra_outproj")) else "decode"
+    family = ("step" if kernel.startswith(("mlra_append", "mlra_outproj"))
+              else "prefill" if kernel.startswith("mlra_prefill") else "decode")
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "latent_kv_cache_amd", "csrc", name), "rb") as f:
@@ -269,6 +271,141 @@ def bench_outproj(torch, args) -> int:
     return 0
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def prefill_visible_tokens(inp) -> int:
+    """Sum over query tokens of the tokens each one sees (causal chunk rule)."""
+    c = inp.cfg
+    L = inp.seq_lens.astype(np.int64)[:, None]
+    j = np.arange(c.q_len, dtype=np.int64)[None, :]
+    V = L - (c.q_len - 1 - j) if c.causal else np.broadcast_to(L, (len(L), c.q_len))
+    return int(np.clip(V, 0, None).sum())
+
+
+def prefill_flops(inp) -> int:
+    """Algorithmic flops of one prefill call: per query row, branch and visible
+    token, 2*(DC + DR) for the score and 2*DC for the output."""
+    c = inp.cfg
+    per = 2 * (c.d_latent + c.d_rope) + 2 * c.d_latent
+    return prefill_visible_tokens(inp) * c.num_heads * c.n_branch * per
+
+
+def _sdpa_whole_prefill_ms(torch, inp, d, timed):
+    """torch's scaled_dot_product_attention (its own causal flag) on the same
+    whole-sequence prefill with keys and values materialised per branch, or
+    None when the shape has cached context before the chunk or SDPA fails."""
+    c = inp.cfg
+    if not c.causal or any(int(L) != c.q_len for L in inp.seq_lens):
+        return None
+    try:
+        S, Q, H, NB, DC = c.num_seqs, c.q_len, c.num_heads, c.n_branch, c.d_latent
+        nblk = -(-Q // c.block_size)
+        tab = d["block_table"][:, :nblk].long()
+        lat = d["latent_cache"][tab].reshape(S, nblk * c.block_size, NB, DC)[:, :Q]
+        kr = d["rope_cache"][tab].reshape(S, nblk * c.block_size, -1)[:, :Q]
+        qs, ks, vs = [], [], []
+        for b in range(NB):
+            qs.append(torch.cat([d["q_latent"][:, :, :, b], d["q_rope"]], -1).transpose(1, 2)
+                      .contiguous())
+            ks.append(torch.cat([lat[:, :, b], kr], -1)[:, None].expand(S, H, Q, -1).contiguous())
+            v = torch.nn.functional.pad(lat[:, :, b], (0, c.d_rope))  # v padded to the qk width
+            vs.append(v[:, None].expand(S, H, Q, -1).contiguous())
+        f = torch.nn.functional.scaled_dot_product_attention
+
+        def run(i):
+            for b in range(NB):
+                f(qs[b], ks[b], vs[b], is_causal=True, scale=c.scale)
+        return timed(run)
+    except Exception:
+        return None
+
+
+def bench_prefill(torch, args) -> int:
+    from latent_kv_cache_amd import api, configs
+    from latent_kv_cache_amd.inputs import make_inputs, to_device
+
+    cfg = configs.BY_NAME[args.workload or "mlra4_tp_share_prefill_b4_c2048_t8192"]
+    inp = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = to_device(inp, dev)
+    S, Q, H, NB, DC = inp.q_latent.shape
+    out = torch.empty((S, Q, H, DC), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((S, Q, H, NB), dtype=torch.float32, device=dev)
+    dims = api.make_dims(d["q_latent"], d["q_rope"], d["latent_cache"], d["rope_cache"],
+                         d["block_table"], max_seq_len=inp.max_seq_len, causal=cfg.causal)
+    plan = api.make_prefill_plan(dims, NB)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    fl = prefill_flops(inp)
+
+    def step(i):
+        api.mlra_prefill_attention(d["q_latent"], d["q_rope"], d["latent_cache"],
+                                   d["rope_cache"], d["block_table"], d["seq_lens"], NB,
+                                   cfg.scale, cfg.out_rescale, max_seq_len=inp.max_seq_len,
+                                   causal=cfg.causal, out=out, lse=lse, workspace=ws)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms = timed(step)
+    tfs = fl / (ms * 1e-3) / 1e12
+    sdpa_ms = _sdpa_whole_prefill_ms(torch, inp, d, timed)
+    res = {
+        "metric": "chunked-prefill attention TFLOP/s (% of bf16 MFMA peak)",
+        "value": round(tfs, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 latents, keys and queries, shuffled paged blocks)",
+        "config": {"workload": cfg.name, "batch": S, "chunk_tokens": Q, "heads": H,
+                   "n_branch": NB, "d_latent": DC, "d_rope": cfg.d_rope,
+                   "context": int(inp.max_seq_len), "causal": bool(cfg.causal),
+                   "splits": plan.splits_per_seq, "workgroups": plan.target_groups},
+        "pct_of_mfma_peak": round(100 * tfs / MFMA_BF16_PEAK_TFLOPS, 2),
+        "algorithmic_flops_per_step": fl,
+        "query_tokens_per_s": round(S * Q / (ms * 1e-3), 1),
+        "torch_sdpa_ms": None if sdpa_ms is None else round(sdpa_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "mlra_prefill", "achieved": round(tfs, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("mlra_prefill", cfg.name)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import mlra_decode
+        # query tokens of sequence 0, from its last one backwards, one oracle
+        # call per token (its visible length as the sequence length)
+        per_tok = 2 * (DC + cfg.d_rope) + 2 * DC
+        L0 = int(inp.seq_lens[0])
+        done, t_total, ntok = 0, 0.0, 0
+        for j in range(Q - 1, -1, -1):
+            if t_total >= 10.0:
+                break
+            V = L0 - (Q - 1 - j) if cfg.causal else L0
+            t0 = time.perf_counter()
+            mlra_decode(inp.q_latent[:1, j:j + 1], inp.q_rope[:1, j:j + 1], inp.latent_cache,
+                        inp.rope_cache, inp.block_table[:1], np.array([V], dtype=np.int32),
+                        cfg.scale, cfg.out_rescale, "sum", False, cfg.block_size)
+            t_total += time.perf_counter() - t0
+            done += max(V, 0) * H * NB * per_tok
+            ntok += 1
+        res["cpu_baseline"] = {
+            "value": round(done / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{ntok} query tokens of sequence 0 (all {H} heads, the last ones of the "
+                      f"chunk) through the float64 NumPy oracle, {t_total:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -334,6 +471,9 @@ def main() -> int:
                     help="measure the cache append instead of decode attention")
     ap.add_argument("--outproj", action="store_true",
                     help="measure the output projection instead of decode attention")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure chunked-prefill attention (default workload "
+                         "mlra4_tp_share_prefill_b4_c2048_t8192) instead of decode attention")
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0: enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
@@ -355,6 +495,8 @@ def main() -> int:
         return bench_append(torch, args)
     if args.outproj:
         return bench_outproj(torch, args)
+    if args.prefill:
+        return bench_prefill(torch, args)
     from latent_kv_cache_amd import api, configs
     from latent_kv_cache_amd.inputs import make_inputs, to_device
 

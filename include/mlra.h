@@ -281,6 +281,45 @@ mlra_status mlra_out_projection(const void* x, const void* w_packed, void* y, in
                                 int32_t k, int32_t d, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/*
+ * Chunked-prefill MLRA attention: the decode formula at the top of this
+ * header for a chunk of many new query tokens per sequence. It is the
+ * regime where the FlashAttention-3 pages place prefill (many queries per
+ * key, bound by matrix throughput), over the same paged latent cache
+ * (wispaper.ai blog "MLRA: Breaking the Sharding Bottleneck in Latent
+ * Attention", "The Core Insight": every head scores the shared latent and
+ * RoPE key of each token, one softmax per branch, branch outputs combined
+ * after attention). Token j of the chunk sits at position L - Q + j; with
+ * causal set it sees every token up to its own position,
+ * t < L - (Q - 1 - j). The chunk's latents and keys must already be in the
+ * cache (mlra_cache_append), so a whole-sequence prefill is Q = L.
+ *
+ * Arguments, layouts, outputs, alignment and error rules as for
+ * mlra_decode_attention, except:
+ *  - q_len may be any value >= 1 (num_heads * q_len <= 2^26);
+ *  - bf16 only, d_latent in {64, 128}, d_rope in {32, 64}, n_branch in
+ *    {1, 2, 4}; other shapes (and fp32) give MLRA_ERR_UNSUPPORTED;
+ *  - num_splits: 0 lets the library split long contexts when the query rows
+ *    alone do not fill the GPU; > 0 asks for that many token splits;
+ *  - the workspace is needed only with more than one split, or with
+ *    MLRA_BRANCH_SUM over more than one branch: mlra_prefill_workspace_size
+ *    returns 0 otherwise, and workspace may then be NULL.
+ * mlra_prefill_make_plan fills the decode plan struct: row_groups counts
+ * 256-row workgroups per sequence and branch, kernel_variant is 8.
+ */
+mlra_status mlra_prefill_make_plan(const mlra_decode_dims* dims, int32_t n_branch,
+                                   int32_t num_cus, mlra_decode_plan* plan);
+
+mlra_status mlra_prefill_workspace_size(const mlra_decode_dims* dims, int32_t n_branch,
+                                        size_t* bytes);
+
+mlra_status mlra_prefill_attention(const void* q_latent, const void* q_rope,
+                                   const void* latent_cache, const void* rope_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   int32_t n_branch, float scale, float out_rescale,
+                                   void* out, float* lse, const mlra_decode_dims* dims,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* mlra_status_string(mlra_status status);
 

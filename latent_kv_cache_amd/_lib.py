@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "MLRA_OK", 1: "MLRA_ERR_NULL_PTR", 2: "MLRA_ERR_BAD_DIMS",
 EXPORTS = ("mlra_decode_make_plan", "mlra_decode_workspace_size", "mlra_decode_attention",
            "mla_decode_attention", "mlra_decode_partials", "mlra_decode_combine",
            "mlra_cache_append", "mlra_out_projection_pack", "mlra_out_projection_workspace_size",
-           "mlra_out_projection",
+           "mlra_out_projection", "mlra_prefill_make_plan", "mlra_prefill_workspace_size",
+           "mlra_prefill_attention",
            "mlra_status_string", "mlra_version")
 
 
@@ -100,6 +101,13 @@ def load() -> ctypes.CDLL:
         lib.mlra_out_projection_workspace_size.restype = i32
         lib.mlra_out_projection.argtypes = [vp, vp, vp, i32, i32, i32, vp, sz, vp]
         lib.mlra_out_projection.restype = i32
+        lib.mlra_prefill_make_plan.argtypes = [dims_p, i32, i32, ctypes.POINTER(DecodePlan)]
+        lib.mlra_prefill_make_plan.restype = i32
+        lib.mlra_prefill_workspace_size.argtypes = [dims_p, i32, ctypes.POINTER(sz)]
+        lib.mlra_prefill_workspace_size.restype = i32
+        lib.mlra_prefill_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, f32, f32, vp, vp,
+                                               dims_p, vp, sz, vp]
+        lib.mlra_prefill_attention.restype = i32
         lib.mlra_status_string.argtypes = [i32]
         lib.mlra_status_string.restype = ctypes.c_char_p
         lib.mlra_version.argtypes = []

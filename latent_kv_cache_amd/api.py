@@ -85,6 +85,13 @@ def make_plan(dims: _lib.DecodeDims, n_branch: int, num_cus: int = 0) -> _lib.De
     return plan
 
 
+def make_prefill_plan(dims: _lib.DecodeDims, n_branch: int, num_cus: int = 0) -> _lib.DecodePlan:
+    lib = _lib.load()
+    plan = _lib.DecodePlan()
+    _lib.check(lib.mlra_prefill_make_plan(dims, n_branch, num_cus, plan), "mlra_prefill_make_plan")
+    return plan
+
+
 def _call(entry: str, q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
           n_branch, scale, out_rescale, max_seq_len, reduce, causal, num_splits, sum_seq_lens,
           out, lse, workspace, stream):
@@ -119,7 +126,8 @@ def _call(entry: str, q_latent, q_rope, latent_cache, rope_cache, block_table, s
     if workspace is None:
         if entry == "combine":
             raise ValueError("mlra_decode_combine needs the workspace of its partials call")
-        workspace = _workspace(dev, make_plan(dims, NB).workspace_bytes)
+        plan = make_prefill_plan(dims, NB) if entry == "prefill" else make_plan(dims, NB)
+        workspace = _workspace(dev, plan.workspace_bytes)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     wsb = workspace.numel() * workspace.element_size()
@@ -134,6 +142,12 @@ def _call(entry: str, q_latent, q_rope, latent_cache, rope_cache, block_table, s
         status = lib.mlra_decode_combine(
             seq_lens.data_ptr(), int(n_branch), float(out_rescale), out.data_ptr(),
             lse.data_ptr(), dims, workspace.data_ptr(), wsb, stream)
+    elif entry == "prefill":
+        status = lib.mlra_prefill_attention(
+            q_latent.data_ptr(), q_rope.data_ptr(), latent_cache.data_ptr(),
+            rope_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), int(n_branch),
+            float(scale), float(out_rescale), out.data_ptr(), lse.data_ptr(), dims,
+            workspace.data_ptr(), wsb, stream)
     elif entry == "mla":
         status = lib.mla_decode_attention(
             q_latent.data_ptr(), q_rope.data_ptr(), latent_cache.data_ptr(),
@@ -145,7 +159,8 @@ def _call(entry: str, q_latent, q_rope, latent_cache, rope_cache, block_table, s
             rope_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), int(n_branch),
             float(scale), float(out_rescale), out.data_ptr(), lse.data_ptr(), dims,
             workspace.data_ptr(), wsb, stream)
-    _lib.check(status, "mlra_decode_combine" if entry == "combine" else f"{entry}_decode_attention")
+    _lib.check(status, {"combine": "mlra_decode_combine", "prefill": "mlra_prefill_attention"}
+               .get(entry, f"{entry}_decode_attention"))
     return out, lse
 
 
@@ -263,6 +278,24 @@ def mlra_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
     return _call("mlra", q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
                  n_branch, scale, out_rescale, max_seq_len, reduce, causal, num_splits,
                  sum_seq_lens, out, lse, workspace, stream)
+
+
+def mlra_prefill_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
+                           latent_cache: torch.Tensor, rope_cache: torch.Tensor,
+                           block_table: torch.Tensor, seq_lens: torch.Tensor, n_branch: int,
+                           scale: float, out_rescale: float, *, max_seq_len: int,
+                           reduce: str = "sum", causal: bool = True, num_splits: int = 0,
+                           out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           stream: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunked-prefill MLRA attention (many query tokens per sequence, bf16);
+    see include/mlra.h. Same tensors and results as mlra_decode_attention."""
+    if q_latent.dim() != 5 or q_latent.shape[3] != n_branch:
+        raise ValueError("q_latent must be [S][Q][H][n_branch][DC]")
+    return _call("prefill", q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
+                 n_branch, scale, out_rescale, max_seq_len, reduce, causal, num_splits, 0,
+                 out, lse, workspace, stream)
 
 
 def mla_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,

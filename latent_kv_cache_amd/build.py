@@ -22,8 +22,9 @@ HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC"
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
-# HIP translation units: the decode kernels, and the kernels of the steps around them.
-HIP_SOURCES = ("mlra_kernels.hip", "mlra_step_kernels.hip")
+# HIP translation units: the decode kernels, the kernels of the steps around
+# them, and chunked-prefill attention.
+HIP_SOURCES = ("mlra_kernels.hip", "mlra_step_kernels.hip", "mlra_prefill_kernels.hip")
 
 
 def hipcc() -> str:

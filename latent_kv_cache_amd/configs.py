@@ -115,7 +115,28 @@ APPEND_B4096_Q2 = DecodeConfig(
     d_latent=128, d_rope=64, dtype="bf16", context=64, seed=9,
     scale=_mlra_scale(128, 64), out_rescale=0.5)
 
+# Chunked prefill on one tensor-parallel rank's share: 4 sequences, each
+# adding a chunk of 2048 tokens after 6144 cached ones (8192 in all), causal.
+# 65536 query rows (2048 tokens x 32 heads) per sequence share each token's
+# latent and RoPE key.
+MLRA4_TP_PREFILL = DecodeConfig(
+    name="mlra4_tp_share_prefill_b4_c2048_t8192", num_seqs=4, q_len=2048, num_heads=32,
+    n_branch=1, d_latent=128, d_rope=64, dtype="bf16", context=8192, seed=10,
+    scale=_mlra_scale(128, 64), out_rescale=0.5)
+# A whole 16384-token sequence prefilled at once (the chunk is the sequence).
+MLRA4_TP_PREFILL_WHOLE = DecodeConfig(
+    name="mlra4_tp_share_prefill_b1_t16384", num_seqs=1, q_len=16384, num_heads=32,
+    n_branch=1, d_latent=128, d_rope=64, dtype="bf16", context=16384, seed=11,
+    scale=_mlra_scale(128, 64), out_rescale=0.5)
+# All four MLRA-4 branches, summed: chunks of 512 after ragged contexts.
+MLRA4_FUSED_PREFILL = DecodeConfig(
+    name="mlra4_fused_prefill_b4_c512", num_seqs=4, q_len=512, num_heads=32, n_branch=4,
+    d_latent=128, d_rope=64, dtype="bf16", context=None, context_range=(512, 4096), seed=12,
+    scale=_mlra_scale(128, 64), out_rescale=0.5)
+
 ALL = [TINY_MLRA4_FP32, MLRA4_TP_SHARE, MLRA4_FUSED, LONG_CONTEXT, RAGGED_Q2]
 # Variants and stress workloads beyond the five above.
 EXTRA = [MLRA2_FUSED, MLRA4_B1_T1M, MLRA4_B1_T2M, APPEND_B4096_Q2]
-BY_NAME = {c.name: c for c in ALL + [MLA_COMPARE] + EXTRA}
+# Chunked-prefill workloads (mlra_prefill_attention).
+PREFILL = [MLRA4_TP_PREFILL, MLRA4_TP_PREFILL_WHOLE, MLRA4_FUSED_PREFILL]
+BY_NAME = {c.name: c for c in ALL + [MLA_COMPARE] + EXTRA + PREFILL}

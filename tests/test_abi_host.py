@@ -225,3 +225,79 @@ def test_out_projection_validation(lib):
     assert lib.mlra_out_projection_pack(fake, None, 4096, 4096, None) == 1
     assert lib.mlra_out_projection_pack(fake, fake, 100, 4096, None) == 3
     assert lib.mlra_out_projection_pack(fake, fake + 8, 4096, 4096, None) == 5
+
+
+# --------------------------------------------------------------------------- prefill
+
+def _pplan(lib, d, nb, cus=256):
+    p = _lib.DecodePlan()
+    st = lib.mlra_prefill_make_plan(ctypes.byref(d), nb, cus, ctypes.byref(p))
+    return st, p
+
+
+@pytest.mark.parametrize("cfg", configs.PREFILL, ids=lambda c: c.name)
+def test_prefill_plan_covers_rows_and_tiles(lib, cfg):
+    d = _dims(cfg)
+    st, p = _pplan(lib, d, cfg.n_branch)
+    assert st == 0 and p.kernel_variant == 8 and p.waves_per_group == 8
+    rows = cfg.num_heads * cfg.q_len
+    assert p.row_groups == -(-rows // 256)
+    max_tiles = -(-d.max_seq_len // 64)
+    assert p.splits_per_seq * p.tiles_per_split >= max_tiles
+    assert (p.splits_per_seq - 1) * p.tiles_per_split < max_tiles
+    assert p.target_groups == p.row_groups * cfg.num_seqs * cfg.n_branch * p.splits_per_seq
+    assert p.lds_bytes <= 64 * 1024
+    direct = p.splits_per_seq == 1 and cfg.n_branch == 1
+    if direct:
+        assert p.workspace_bytes == 0
+    else:
+        slots = cfg.num_seqs * p.splits_per_seq * cfg.n_branch * rows
+        assert p.workspace_bytes >= slots * (cfg.d_latent + 1) * 4
+
+
+def test_prefill_plan_splits_only_when_rows_leave_cus_idle(lib):
+    cfg = configs.MLRA4_TP_PREFILL
+    st, p = _pplan(lib, _dims(cfg), 1)
+    assert st == 0 and p.splits_per_seq == 1 and p.target_groups >= 256
+    # a 16-token chunk: 2 row groups per sequence, so the context is split
+    small = cfg.with_(q_len=16)
+    st, p = _pplan(lib, _dims(small), 1)
+    assert st == 0 and p.splits_per_seq > 1 and p.tiles_per_split >= 2
+    assert p.target_groups >= 128
+    d = _dims(small, num_splits=3)
+    st, p = _pplan(lib, d, 1)
+    assert st == 0 and p.splits_per_seq == 3
+    # CONCAT with one split needs no workspace even with four branches
+    d = _dims(cfg.with_(n_branch=4), reduce=_lib.MLRA_BRANCH_CONCAT)
+    st, p = _pplan(lib, d, 4)
+    assert st == 0 and p.splits_per_seq == 1 and p.workspace_bytes == 0
+    size = ctypes.c_size_t(7)
+    assert lib.mlra_prefill_workspace_size(ctypes.byref(_dims(cfg)), 1, ctypes.byref(size)) in (0, 6)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q_len", 0, 2), ("num_heads", 0, 2), ("dtype", _lib.MLRA_FP32, 3), ("d_latent", 256, 3),
+    ("d_latent", 96, 3), ("d_rope", 48, 3), ("block_size", 32, 3), ("num_seqs", 0, 2),
+    ("max_seq_len", -1, 2), ("reserved", 1, 2),
+])
+def test_prefill_rejects_bad_dims(lib, field, value, status):
+    d = _dims(configs.MLRA4_TP_PREFILL, **{field: value})
+    st, _ = _pplan(lib, d, 1)
+    assert st == status, (field, value, st)
+
+
+def test_prefill_rejects_too_many_rows_and_bad_pointers(lib):
+    d = _dims(configs.MLRA4_TP_PREFILL, num_heads=1 << 13, q_len=1 << 14)
+    st, _ = _pplan(lib, d, 1)
+    assert st == 3
+    d = _dims(configs.MLRA4_TP_PREFILL)
+    # pointer checks come before any device query
+    st = lib.mlra_prefill_attention(None, None, None, None, None, None, 1, 0.1, 0.5, None,
+                                    None, ctypes.byref(d), None, 0, None)
+    assert st == 1
+    st = lib.mlra_prefill_attention(16, 16, 16, 16, 16, 16, 1, float("nan"), 0.5, 16, 16,
+                                    ctypes.byref(d), None, 0, None)
+    assert st == 2
+    st = lib.mlra_prefill_attention(16, 16, 16, 16, 16, 16, 1, 0.1, 0.5, 24, 16,
+                                    ctypes.byref(d), None, 0, None)
+    assert st == 5

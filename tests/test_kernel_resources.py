@@ -47,7 +47,8 @@ def remarks():
 def test_every_kernel_is_reported(remarks):
     names = " ".join(remarks)
     for kern in ("mlra_split_pc", "mlra_split_mfma", "mlra_split_valu", "mlra_combine",
-                 "mlra_append", "mlra_outproj_pack", "mlra_outproj", "mlra_outproj_reduce"):
+                 "mlra_append", "mlra_outproj_pack", "mlra_outproj", "mlra_outproj_reduce",
+                 "mlra_prefill", "mlra_prefill_merge"):
         assert kern in names
 
 
@@ -60,4 +61,11 @@ def test_loader_compute_kernel_runs_two_waves_per_simd(remarks):
     pc = {k: v for k, v in remarks.items() if "mlra_split_pc" in k}
     assert pc
     for k, v in pc.items():
+        assert v["VGPRs"] + v.get("AGPRs", 0) <= 256, (k, v)
+
+
+def test_prefill_kernel_runs_two_waves_per_simd(remarks):
+    pf = {k: v for k, v in remarks.items() if "mlra_prefill" in k and "merge" not in k}
+    assert len(pf) == 4  # latent 64/128 x RoPE 32/64
+    for k, v in pf.items():
         assert v["VGPRs"] + v.get("AGPRs", 0) <= 256, (k, v)
