@@ -15,14 +15,17 @@
 // latent and RoPE key (absorbed form), so a workgroup's rows -- 8 query
 // tokens x 32 heads at H = 32 -- share one stream of cache tiles. Each
 // 64-token tile is read from HBM (or L2) once per workgroup, staged in LDS,
-// and used by all 8 waves; one wave holds 32 query rows in registers.
+// and used by all 4 waves (one per SIMD); a wave holds two 32-row tiles of
+// queries in registers, so every operand it reads from LDS feeds both.
 //
-// Per wave and 32-token sub-tile (the loop body of the decode kernels):
+// Per wave and 32-token sub-tile:
 //   S^T = [c ; k_r] [q_lat ; q_rope]^T        32x32x16 bf16 MFMA, K = DC + DR
 //   online softmax per row (column of S^T), lazily rescaled
 //   O^T += c^T P^T                            32x32x16 bf16 MFMA, transposed LDS reads
-// Rows of one wave share a query token when H is a multiple of 32, so the
-// causal edge is wave-uniform there; elsewhere each lane masks its own row.
+// software-pipelined by one sub-tile: the score MFMAs of sub-tile j are
+// issued between the vector instructions that turn the scores of sub-tile
+// j-1 into probabilities (the FlashAttention-3 pages' overlap of softmax
+// with the matrix products, here inside one wave's instruction stream).
 //
 // Outputs: with one split and no branch sum (one branch, or CONCAT) the
 // kernel writes out and lse directly; otherwise it writes the decode
@@ -31,6 +34,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "mlra_device.h"
 #include "mlra_internal.h"
@@ -42,9 +46,9 @@ constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfLn2 = 0.69314718055994531f;
 // Lazy softmax reference: probabilities exp2(score - m_ref) stay below 2^8.
 constexpr float kPfLazyLog2 = 8.0f;
-constexpr int kPfWaves = 8;               // two per SIMD
+constexpr int kPfWaves = 4;               // one per SIMD
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfRows = 32 * kPfWaves;    // query rows per workgroup
+constexpr int kPfRows = 64 * kPfWaves;    // query rows per workgroup (two 32-row tiles per wave)
 constexpr int kPfTile = kBlock;           // tokens per staged tile = one cache block
 constexpr int32_t kVariantPrefillBf16 = 8;  // mlra_decode_plan.kernel_variant of prefill
 
@@ -119,30 +123,32 @@ __device__ __forceinline__ bf16x8 pf_rd16(const unsigned char* a) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
 }
 
-// Staged tile in LDS: latent rows [64][LP] then RoPE rows [64][RP], in
-// 16-byte chunks. Latent rows carry 2 spare chunks and RoPE rows 1, the
-// pitches under which the decode kernels' row reads (8 lanes, one chunk of
-// 8 consecutive rows) and 16-lane transpose reads (4 rows x 32 bytes) land
-// on distinct banks.
+// Staged tiles in LDS: a ring of three buffers, each latent rows [64][LP]
+// then RoPE rows [64][RP] in 16-byte chunks. Latent rows carry 2 spare
+// chunks and RoPE rows 1 (the pitches of the decode kernels' row reads and
+// 16-lane transpose reads). Three buffers let a wave read the value rows of
+// the previous sub-tile after the barrier that publishes the next tile.
 template <int DC, int DR>
 struct PfLayout {
   static constexpr int LP = DC / 8 + 2, RP = DR / 8 + 1;
   static constexpr int LAT = kPfTile * LP * 16;
   static constexpr int BUF = LAT + kPfTile * RP * 16;
-  static constexpr int LDS = 2 * BUF;  // double buffered
+  static constexpr int NBUF = 3;
+  static constexpr int LDS = NBUF * BUF;
 };
 
 template <int DC, int DR>
-__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mlra_prefill(PrefillParams p) {
   constexpr int NL = DC / 16, NR = DR / 16, NDT = DC / 32;
   constexpr int LCH = DC / 8, RCH = DR / 8;
   using Lay = PfLayout<DC, DR>;
   constexpr int LP = Lay::LP, RP = Lay::RP, LAT = Lay::LAT, BUF = Lay::BUF;
-  constexpr int NCH = kPfTile * (LCH + RCH);              // 16-byte chunks per tile
-  constexpr int CPT = (NCH + kPfThreads - 1) / kPfThreads;  // per thread
-  static_assert((kPfTile * LCH) % kPfThreads == 0, "latent/RoPE split is uniform per load");
-  static_assert(Lay::LDS <= 64 * 1024, "LDS");
+  constexpr int CPT = kPfTile * (LCH + RCH) / kPfThreads;  // 16-byte chunks per thread and tile
+  constexpr int CPT_L = kPfTile * LCH / kPfThreads;        // the first CPT_L are latent
+  static_assert((kPfTile * LCH) % kPfThreads == 0 && (kPfTile * RCH) % kPfThreads == 0,
+                "every thread moves whole latent and RoPE chunks");
+  static_assert(Lay::LDS <= 160 * 1024, "LDS");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   // workgroup -> (split, branch, sequence, row tile); the last row tiles,
@@ -161,53 +167,52 @@ mlra_prefill(PrefillParams p) {
   int L = p.seq_lens[s];
   L = L < 0 ? 0 : (L > p.lcap ? p.lcap : L);
   const int r0 = rt * kPfRows;
-  const int vmax = max(0, pf_visible(L, p.Q, p.H, min(r0 + kPfRows, p.rows) - 1, p.causal));
+  const int r_last = min(r0 + kPfRows, p.rows) - 1;
+  const int vmax = max(0, pf_visible(L, p.Q, p.H, r_last, p.causal));
+  // rows past the end see nothing, so a group holding some masks everywhere
+  const int vmin = r0 + kPfRows <= p.rows ? pf_visible(L, p.Q, p.H, r0, p.causal) : 0;
   const int t_lo = k * p.tps * kPfTile;
   const int t_hi = min(t_lo + p.tps * kPfTile, vmax);
-  const int ntile = t_hi > t_lo ? (t_hi - t_lo + kPfTile - 1) / kPfTile : 0;
-  if (ntile == 0 && !p.direct) return;  // no row of this group has a token in the split
+  const int nsub = t_hi > t_lo ? (t_hi - t_lo + 31) / 32 : 0;  // 32-token sub-tiles
+  const int ntile = (nsub + 1) / 2;
+  if (nsub == 0 && !p.direct) return;  // no row of this group has a token in the split
+  // sub-tiles from jm on hold some token that some row of the group may not see
+  const int jm = vmin - t_lo >= 32 ? (vmin - t_lo) / 32 : 0;
 
-  // this lane's row, its visible length, and the wave's extremes (rows past
-  // the end see nothing)
-  const int wr0 = r0 + 32 * wave;
-  const int row = wr0 + n;
-  const bool live = row < p.rows;
-  const int vis = live ? pf_visible(L, p.Q, p.H, row, p.causal) : 0;
-  const int wmin = wr0 + 31 < p.rows ? pf_visible(L, p.Q, p.H, wr0, p.causal) : 0;
-  const int wmax = wr0 < p.rows ? pf_visible(L, p.Q, p.H, min(wr0 + 31, p.rows - 1), p.causal) : 0;
+  // Two 32-row tiles per wave: A = rows wr0 + n, B = rows wr0 + 32 + n.
+  const int wr0 = r0 + 64 * wave;
+  const int rowA = wr0 + n, rowB = wr0 + 32 + n;
+  const bool liveA = rowA < p.rows, liveB = rowB < p.rows;
+  const int visA = liveA ? pf_visible(L, p.Q, p.H, rowA, p.causal) : 0;
+  const int visB = liveB ? pf_visible(L, p.Q, p.H, rowB, p.causal) : 0;
 
   // Query rows in registers as the B operand of S^T: k-step st takes
   // features 8st..8st+7 (g = 0) and DC/2 + 8st.. (g = 1), the order the
   // staged rows are read in.
-  const int64_t qrow = (int64_t)s * p.rows + (live ? row : 0);
-  const __bf16* ql = p.q_lat + (qrow * p.NB + b) * DC + g * (DC / 2);
-  const __bf16* qr = p.q_rope + qrow * DR + g * (DR / 2);
-  bf16x8 qL[NL], qR[NR];
+  bf16x8 qLA[NL], qRA[NR], qLB[NL], qRB[NR];
+  {
+    const int64_t qa = (int64_t)s * p.rows + (liveA ? rowA : 0);
+    const int64_t qb = (int64_t)s * p.rows + (liveB ? rowB : 0);
+    const __bf16* la = p.q_lat + (qa * p.NB + b) * DC + g * (DC / 2);
+    const __bf16* lb = p.q_lat + (qb * p.NB + b) * DC + g * (DC / 2);
+    const __bf16* ra = p.q_rope + qa * DR + g * (DR / 2);
+    const __bf16* rb = p.q_rope + qb * DR + g * (DR / 2);
 #pragma unroll
-  for (int st = 0; st < NL; ++st) qL[st] = __builtin_bit_cast(bf16x8, live ? ld16(ql + 8 * st) : u32x4{});
+    for (int st = 0; st < NL; ++st) {
+      qLA[st] = __builtin_bit_cast(bf16x8, liveA ? ld16(la + 8 * st) : u32x4{});
+      qLB[st] = __builtin_bit_cast(bf16x8, liveB ? ld16(lb + 8 * st) : u32x4{});
+    }
 #pragma unroll
-  for (int st = 0; st < NR; ++st) qR[st] = __builtin_bit_cast(bf16x8, live ? ld16(qr + 8 * st) : u32x4{});
-
-  // Tile loads: thread tid moves chunks tid, tid + 512, ... of a tile.
-  // Offsets inside a block, and the LDS destinations, are fixed per thread.
-  uint32_t goff[CPT], loff[CPT];
-  int gtok[CPT];
-  bool isl[CPT], has[CPT];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int x = c * kPfThreads + tid;
-    has[c] = x < NCH;
-    isl[c] = x < kPfTile * LCH;
-    const int y = x - kPfTile * LCH;
-    gtok[c] = isl[c] ? x / LCH : y / RCH;
-    goff[c] = isl[c] ? (uint32_t)(gtok[c] * p.lst * 2 + (x % LCH) * 16)
-                     : (uint32_t)(gtok[c] * p.rst * 2 + (y % RCH) * 16);
-    loff[c] = isl[c] ? (uint32_t)((gtok[c] * LP + x % LCH) * 16)
-                     : (uint32_t)(LAT + (gtok[c] * RP + y % RCH) * 16);
+    for (int st = 0; st < NR; ++st) {
+      qRA[st] = __builtin_bit_cast(bf16x8, liveA ? ld16(ra + 8 * st) : u32x4{});
+      qRB[st] = __builtin_bit_cast(bf16x8, liveB ? ld16(rb + 8 * st) : u32x4{});
+    }
   }
+
+  // Tile loads: chunk c of thread tid is latent chunk c*256 + tid (c <
+  // CPT_L) or RoPE chunk (c - CPT_L)*256 + tid of the tile.
   const int64_t tab_base = (int64_t)s * p.max_blocks;
   const int tile0 = t_lo / kPfTile;
-  // block ids of 64 consecutive tiles, one per lane, the next 64 in flight
   auto tab_load = [&](int i) { return p.table[tab_base + min(tile0 + i + lane, p.max_blocks - 1)]; };
   int tabA = 0, tabB = 0;
   if (ntile > 0) {
@@ -217,6 +222,9 @@ mlra_prefill(PrefillParams p) {
   const unsigned char* lat_b = reinterpret_cast<const unsigned char*>(p.lat) + (int64_t)b * p.lsbr * 2;
   const unsigned char* rope_b = reinterpret_cast<const unsigned char*>(p.rope);
   u32x4 buf[CPT];
+  auto chunk_tok = [&](int c) {
+    return c < CPT_L ? (c * kPfThreads + tid) / LCH : ((c - CPT_L) * kPfThreads + tid) / RCH;
+  };
   auto issue = [&](int i) {  // tile i of the split: global -> registers
     if (i > 0 && (i & 63) == 0) {
       tabA = tabB;
@@ -226,62 +234,60 @@ mlra_prefill(PrefillParams p) {
     const unsigned char* lb = lat_b + (int64_t)phys * p.lsb * 2;
     const unsigned char* rb = rope_b + (int64_t)phys * p.rsb * 2;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (has[c]) buf[c] = ld16((isl[c] ? lb : rb) + goff[c]);
+    for (int c = 0; c < CPT; ++c) {
+      const int t = chunk_tok(c);
+      if (c < CPT_L)
+        buf[c] = ld16(lb + (uint32_t)(t * p.lst * 2) + ((c * kPfThreads + tid) % LCH) * 16);
+      else
+        buf[c] = ld16(rb + (uint32_t)(t * p.rst * 2) + (((c - CPT_L) * kPfThreads + tid) % RCH) * 16);
+    }
   };
   auto stage = [&](int i, unsigned char* dst) {  // registers -> LDS, rows past vmax zeroed
     const int tok0 = (tile0 + i) * kPfTile;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (has[c]) *reinterpret_cast<u32x4*>(dst + loff[c]) = tok0 + gtok[c] < vmax ? buf[c] : u32x4{};
+    for (int c = 0; c < CPT; ++c) {
+      const int t = chunk_tok(c);
+      const int off = c < CPT_L ? (t * LP + (c * kPfThreads + tid) % LCH) * 16
+                                : LAT + (t * RP + ((c - CPT_L) * kPfThreads + tid) % RCH) * 16;
+      *reinterpret_cast<u32x4*>(dst + off) = tok0 + t < vmax ? buf[c] : u32x4{};
+    }
   };
 
-  f32x16 acc[NDT];
+  f32x16 accA[NDT], accB[NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int dt = 0; dt < NDT; ++dt) accA[dt] = accB[dt] = f32x16{};
+  float mA = -INFINITY, lA = 0.f, mB = -INFINITY, lB = 0.f;
 
   const int a_l = (n * LP + g * (LCH / 2)) * 16;  // S^T A operand: token row n
   const int a_r = (n * RP + g * (RCH / 2)) * 16;
   const int a_t = (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
-  // One 32-token sub-tile: latent rows at sl, RoPE rows at sr, first token tb.
-  auto sub_tile = [&](const unsigned char* sl, const unsigned char* sr, int tb) {
-    // LDS reads batched ahead of the MFMAs that use them (the score operands
-    // first, then the transposed value operands in two halves between the
-    // score MFMAs); at most 15 reads outstanding past any wait.
-    bf16x8 aR[NR], aL[NL], aT[2][NDT];
-    auto read_t = [&](int h2) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const i16x4 lo = pf_read_tr(sl + a_t + (16 * h2) * LP * 16 + dt * 64);
-        const i16x4 hi = pf_read_tr(sl + a_t + (16 * h2 + 8) * LP * 16 + dt * 64);
-        aT[h2][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
+  // S^T of both row tiles for the sub-tile with latent rows at sl, RoPE at sr.
+  auto scores = [&](const unsigned char* sl, const unsigned char* sr, f32x16& sa, f32x16& sb) {
+    bf16x8 aR[NR], aL[NL];
 #pragma unroll
     for (int st = 0; st < NR; ++st) aR[st] = pf_rd16(sr + a_r + st * 16);
 #pragma unroll
     for (int st = 0; st < NL; ++st) aL[st] = pf_rd16(sl + a_l + st * 16);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 sc = f32x16{}, sd = f32x16{};
+    sa = f32x16{};
+    sb = f32x16{};
 #pragma unroll
-    for (int st = 0; st < NR; ++st) sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qR[st], sd, 0, 0, 0);
-    read_t(0);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int st = 0; st < NR; ++st) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qRA[st], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qRB[st], sb, 0, 0, 0);
+    }
 #pragma unroll
     for (int st = 0; st < NL; ++st) {
-      if (st % 2 == 0)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[st], sc, 0, 0, 0);
-      else
-        sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[st], sd, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qLA[st], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qLB[st], sb, 0, 0, 0);
     }
-    read_t(1);
-    __builtin_amdgcn_sched_barrier(0);
-    sc += sd;
-    if (tb + 32 > wmin) {  // uniform: some row of the wave stops inside this sub-tile
-      // element r holds token tb + 4g + 8(r/4) + r%4
+  };
+  // Row maximum of a sub-tile (first token tb), in base-2 units; with MASK,
+  // tokens at or past the row's visible length become -inf first. Element r
+  // of lane (n, g) holds token tb + 4g + 8(r/4) + r%4.
+  auto row_max = [&](f32x16& sc, int vis, int tb, auto mask) {
+    if constexpr (decltype(mask)::value) {
       const int lim = vis - tb - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] = 8 * (r >> 2) + (r & 3) < lim ? sc[r] : -INFINITY;
@@ -289,20 +295,34 @@ mlra_prefill(PrefillParams p) {
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    mx = pf_max_halves(mx) * p.score_scale;
-    const bool first = m_run == -INFINITY;
-    const bool grow = first ? mx > -INFINITY : mx > m_run + kPfLazyLog2;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
-      m_run = grow ? mx : m_run;
-      l_run *= alpha;
-      if (__builtin_amdgcn_ballot_w64(grow && !first)) {
+    return pf_max_halves(mx) * p.score_scale;
+  };
+  // Lazily moved reference maximum: rescale only when a row maximum exceeds
+  // it by more than kPfLazyLog2 (log2 units).
+  auto settle = [&](float mxA, float mxB) {
+    const bool firstA = mA == -INFINITY, firstB = mB == -INFINITY;
+    const bool growA = firstA ? mxA > -INFINITY : mxA > mA + kPfLazyLog2;
+    const bool growB = firstB ? mxB > -INFINITY : mxB > mB + kPfLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(growA || growB)) {
+      const float alA = growA ? __builtin_amdgcn_exp2f(mA - mxA) : 1.f;
+      const float alB = growB ? __builtin_amdgcn_exp2f(mB - mxB) : 1.f;
+      mA = growA ? mxA : mA;
+      mB = growB ? mxB : mB;
+      lA *= alA;
+      lB *= alB;
+      if (__builtin_amdgcn_ballot_w64((growA && !firstA) || (growB && !firstB))) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        for (int dt = 0; dt < NDT; ++dt) {
+          accA[dt] *= alA;
+          accB[dt] *= alB;
+        }
       }
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    bf16x8 pB[2];
+  };
+  // Probabilities of a sub-tile against the reference, as the B operand of
+  // O^T += C^T P^T, and their sum.
+  auto probs = [&](const f32x16& sc, float m, float& l, bf16x8 (&pb)[2]) {
+    const float m_use = m == -INFINITY ? 0.f : m;
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -310,70 +330,109 @@ mlra_prefill(PrefillParams p) {
       for (int e = 0; e < 8; ++e) {
         const float pe = __builtin_amdgcn_exp2f(fmaf(sc[8 * h2 + e], p.score_scale, -m_use));
         ps[e & 3] += pe;
-        pB[h2][e] = (__bf16)pe;
+        pb[h2][e] = (__bf16)pe;
       }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  // O^T += C^T P^T for both row tiles; value rows (the sub-tile's latent) at vl.
+  auto values = [&](const unsigned char* vl, const bf16x8 (&pa)[2], const bf16x8 (&pb)[2]) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aT[h2][dt], pB[h2], acc[dt], 0, 0, 0);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const i16x4 lo = pf_read_tr(vl + a_t + (16 * h2) * LP * 16 + dt * 64);
+        const i16x4 hi = pf_read_tr(vl + a_t + (16 * h2 + 8) * LP * 16 + dt * 64);
+        const bf16x8 at = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        accA[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pa[h2], accA[dt], 0, 0, 0);
+        accB[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pb[h2], accB[dt], 0, 0, 0);
+      }
   };
 
-  if (ntile > 0) {
-    // Tile i+1 is in registers while tile i is computed from LDS; it is
-    // staged into the other buffer after the compute, and the barrier that
-    // follows both publishes it and frees the buffer just computed on.
+  if (nsub > 0) {
+    // Software pipeline over 32-token sub-tiles j: iteration j computes the
+    // scores of j while the probabilities of j-1 are formed and multiplied
+    // into the outputs, so the vector work of one sub-tile runs beside the
+    // matrix work of the next. Tile i (sub-tiles 2i, 2i+1) sits in buffer
+    // i % 3; it is staged from registers and published by a barrier at the
+    // start of iteration 2i, and the loads of tile i+1 leave right after.
+    // The buffer staged there last held tile i-3, whose last reads were in
+    // iteration 2i-4, before the barrier of iteration 2i-2.
     issue(0);
     stage(0, smem);
     if (ntile > 1) issue(1);
     pf_lds_barrier();
-    for (int i = 0; i < ntile; ++i) {
-      const unsigned char* tb_base = smem + (i & 1) * BUF;
-      const int t0 = (tile0 + i) * kPfTile;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (t0 + 32 * u >= wmax) break;  // uniform: the wave's rows see no further token
-        sub_tile(tb_base + u * 32 * LP * 16, tb_base + LAT + u * 32 * RP * 16, t0 + 32 * u);
+    f32x16 sA, sB;
+    scores(smem, smem + LAT, sA, sB);
+    if (jm == 0)
+      settle(row_max(sA, visA, t_lo, std::true_type{}), row_max(sB, visB, t_lo, std::true_type{}));
+    else
+      settle(row_max(sA, visA, t_lo, std::false_type{}), row_max(sB, visB, t_lo, std::false_type{}));
+    int cur = 0, prev = 0;  // buffers of sub-tiles j and j-1
+    auto step = [&](int j, auto mask) {
+      prev = cur;
+      if ((j & 1) == 0) {
+        cur = cur == 2 ? 0 : cur + 1;
+        stage(j >> 1, smem + cur * BUF);
+        pf_lds_barrier();
+        if ((j >> 1) + 1 < ntile) issue((j >> 1) + 1);
       }
-      if (i + 1 < ntile) {
-        stage(i + 1, smem + ((i + 1) & 1) * BUF);
-        if (i + 2 < ntile) issue(i + 2);
-      }
-      pf_lds_barrier();
-    }
+      const unsigned char* kb = smem + cur * BUF;
+      const unsigned char* vb = smem + prev * BUF + ((j - 1) & 1) * 32 * LP * 16;
+      f32x16 nA, nB;
+      scores(kb + (j & 1) * 32 * LP * 16, kb + LAT + (j & 1) * 32 * RP * 16, nA, nB);
+      bf16x8 pA[2], pB[2];
+      probs(sA, mA, lA, pA);
+      probs(sB, mB, lB, pB);
+      values(vb, pA, pB);
+      sA = nA;
+      sB = nB;
+      const int tb = t_lo + 32 * j;
+      settle(row_max(sA, visA, tb, mask), row_max(sB, visB, tb, mask));
+    };
+    const int j1 = min(max(jm, 1), nsub);
+    for (int j = 1; j < j1; ++j) step(j, std::false_type{});
+    for (int j = j1; j < nsub; ++j) step(j, std::true_type{});
+    bf16x8 pA[2], pB[2];
+    probs(sA, mA, lA, pA);
+    probs(sB, mB, lB, pB);
+    values(smem + cur * BUF + ((nsub - 1) & 1) * 32 * LP * 16, pA, pB);
   }
 
-  l_run = pf_sum_halves(l_run);
-  if (!live) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kPfLn2 : -INFINITY;
+  lA = pf_sum_halves(lA);
+  lB = pf_sum_halves(lB);
   // O^T element (dt, r) of lane (n, g) is feature dt*32 + 8(r/4) + 4g + r%4 of row n
-  if (p.direct) {
-    const float f = inv * p.out_rescale;
-    __bf16* o = p.out + ((int64_t)(s * (int64_t)p.rows + row) * (p.concat ? p.NB : 1) +
-                         (p.concat ? b : 0)) * DC;
+  auto write_row = [&](int row, bool live, const f32x16 (&acc)[NDT], float m, float l) {
+    if (!live) return;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lse_v = l > 0.f ? (m + __log2f(l)) * kPfLn2 : -INFINITY;
+    if (p.direct) {
+      const float f = inv * p.out_rescale;
+      __bf16* o = p.out + ((int64_t)(s * (int64_t)p.rows + row) * (p.concat ? p.NB : 1) +
+                           (p.concat ? b : 0)) * DC;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x4 v;
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[dt][4 * q + e] * f);
-        *reinterpret_cast<bf16x4*>(o + dt * 32 + 8 * q + 4 * g) = v;
-      }
-    if (g == 0) p.lse[((int64_t)s * p.rows + row) * p.NB + b] = lse_v;
-  } else {
-    const int64_t ri = (((int64_t)s * p.spl + k) * p.NB + b) * p.rows + row;
-    float* o = p.part_o + ri * DC;
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[dt][4 * q + e] * f);
+          *reinterpret_cast<bf16x4*>(o + dt * 32 + 8 * q + 4 * g) = v;
+        }
+      if (g == 0) p.lse[((int64_t)s * p.rows + row) * p.NB + b] = lse_v;
+    } else {
+      const int64_t ri = (((int64_t)s * p.spl + k) * p.NB + b) * p.rows + row;
+      float* o = p.part_o + ri * DC;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
-            f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} * inv;
-    if (g == 0) p.part_lse[ri] = lse_v;
-  }
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
+              f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} * inv;
+      if (g == 0) p.part_lse[ri] = lse_v;
+    }
+  };
+  write_row(rowA, liveA, accA, mA, lA);
+  write_row(rowB, liveB, accB, mB, lB);
 }
 
 // Merge of split partials: one thread per (sequence, row, 4 features). Row r
@@ -510,6 +569,11 @@ mlra_status prefill_plan(const Resolved& r, int32_t num_cus, int32_t num_splits,
 template <int DC, int DR>
 hipError_t launch_prefill(const PrefillParams& pp, int64_t groups, hipStream_t st) {
   constexpr uint32_t lds = PfLayout<DC, DR>::LDS;
+  // more than 64 KB of dynamic LDS must be allowed once per kernel instance
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&mlra_prefill<DC, DR>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((mlra_prefill<DC, DR>), dim3((uint32_t)groups), dim3(kPfThreads), lds, st, pp);
   return hipGetLastError();
 }
