@@ -51,6 +51,7 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRows = 64 * kPfWaves;    // query rows per workgroup (two 32-row tiles per wave)
 constexpr int kPfTile = kBlock;           // tokens per staged tile = one cache block
 constexpr int32_t kVariantPrefillBf16 = 8;  // mlra_decode_plan.kernel_variant of prefill
+constexpr int kPfMaxTiles = 1024;           // 64-token tiles per split (block ids staged in LDS)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -119,22 +120,50 @@ __device__ __forceinline__ i16x4 pf_read_tr(const unsigned char* p) {
       (__attribute__((address_space(3))) i16x4*)(const_cast<unsigned char*>(p)));
 }
 
+// 16 bytes per lane from global memory straight into LDS at lds_addr +
+// 16 * lane (lds_addr wave-uniform, in M0). No register receives data;
+// completion is counted by vmcnt, and the kernel waits for it explicitly
+// before the barrier that publishes the tile. Written as asm rather than
+// with the load-to-LDS builtin: with the builtin the compiler cannot tell
+// the ring's buffers apart and waits for every tile load in flight before
+// each LDS read, which serialises the prefetch.
+__device__ __forceinline__ void pf_load_lds16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x8 pf_rd16(const unsigned char* a) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
 }
 
-// Staged tiles in LDS: a ring of three buffers, each latent rows [64][LP]
-// then RoPE rows [64][RP] in 16-byte chunks. Latent rows carry 2 spare
-// chunks and RoPE rows 1 (the pitches of the decode kernels' row reads and
-// 16-lane transpose reads). Three buffers let a wave read the value rows of
-// the previous sub-tile after the barrier that publishes the next tile.
+// Staged tiles in LDS: a ring of four buffers, each latent rows [64][LP]
+// then RoPE rows [64][RP] in 16-byte chunks (unpadded, chunks swizzled as
+// above). Loads run two tiles ahead, and a wave still reads the previous
+// sub-tile's value rows after the barrier that publishes the next tile:
+// four buffers.
+// Chunk swizzles of the staged rows: chunk c of latent row r sits at chunk
+// c ^ lat_swz(r) of that row, chunk c of RoPE row r at c ^ rope_swz(r).
+// With 64 LDS banks (16 chunks), a 16-byte row read serves 16 lanes at a
+// time and an 8-byte transpose read 32 lanes; these swizzles put every
+// such group on distinct banks (16 consecutive rows, one chunk; or 4
+// consecutive rows, 4 consecutive chunks), which no single row padding
+// achieves for both. Both have period 16 in r.
+template <int LCH>
+__device__ __forceinline__ int lat_swz(int r) {
+  return LCH == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+template <int RCH>
+__device__ __forceinline__ int rope_swz(int r) {
+  return RCH == 8 ? (r >> 1) & 7 : (r >> 2) & 3;
+}
+
 template <int DC, int DR>
 struct PfLayout {
-  static constexpr int LP = DC / 8 + 2, RP = DR / 8 + 1;
+  static constexpr int LP = DC / 8, RP = DR / 8;  // unpadded rows, swizzled chunks
   static constexpr int LAT = kPfTile * LP * 16;
   static constexpr int BUF = LAT + kPfTile * RP * 16;
-  static constexpr int NBUF = 3;
-  static constexpr int LDS = NBUF * BUF;
+  static constexpr int NBUF = 4;
+  static constexpr int LDS = NBUF * BUF;                     // tile ring
+  static constexpr int TOTAL = LDS + kPfMaxTiles * 4;         // + block ids of a split
 };
 
 template <int DC, int DR>
@@ -144,11 +173,13 @@ mlra_prefill(PrefillParams p) {
   constexpr int LCH = DC / 8, RCH = DR / 8;
   using Lay = PfLayout<DC, DR>;
   constexpr int LP = Lay::LP, RP = Lay::RP, LAT = Lay::LAT, BUF = Lay::BUF;
-  constexpr int CPT = kPfTile * (LCH + RCH) / kPfThreads;  // 16-byte chunks per thread and tile
-  constexpr int CPT_L = kPfTile * LCH / kPfThreads;        // the first CPT_L are latent
-  static_assert((kPfTile * LCH) % kPfThreads == 0 && (kPfTile * RCH) % kPfThreads == 0,
-                "every thread moves whole latent and RoPE chunks");
-  static_assert(Lay::LDS <= 160 * 1024, "LDS");
+  // A tile buffer is filled by direct global->LDS loads of 64 lanes x 16
+  // bytes: load q covers buffer chunks 64q..64q+63; wave w issues loads
+  // w, w + 4, ... (NLW of the NLD).
+  constexpr int NLD = BUF / 1024;
+  constexpr int NLW = NLD / kPfWaves;
+  static_assert((BUF / 16) % (64 * kPfWaves) == 0, "every wave issues the same number of loads");
+  static_assert(Lay::TOTAL <= 160 * 1024, "LDS");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   // workgroup -> (split, branch, sequence, row tile); the last row tiles,
@@ -213,44 +244,50 @@ mlra_prefill(PrefillParams p) {
   // CPT_L) or RoPE chunk (c - CPT_L)*256 + tid of the tile.
   const int64_t tab_base = (int64_t)s * p.max_blocks;
   const int tile0 = t_lo / kPfTile;
-  auto tab_load = [&](int i) { return p.table[tab_base + min(tile0 + i + lane, p.max_blocks - 1)]; };
-  int tabA = 0, tabB = 0;
-  if (ntile > 0) {
-    tabA = tab_load(0);
-    tabB = ntile > 64 ? tab_load(64) : 0;
-  }
+  // The split's block ids, staged in LDS before any tile load: once tile
+  // loads are in flight a vector load of the table would make the compiler
+  // wait for all of them (it does not track them).
+  int* const tabl = reinterpret_cast<int*>(smem + Lay::LDS);
+  for (int i = tid; i < ntile; i += kPfThreads)
+    tabl[i] = pf_clamp_block(p.table[tab_base + min(tile0 + i, p.max_blocks - 1)], p.num_blocks);
+  auto block_of = [&](int i) { return __builtin_amdgcn_readfirstlane(tabl[i]); };
   const unsigned char* lat_b = reinterpret_cast<const unsigned char*>(p.lat) + (int64_t)b * p.lsbr * 2;
   const unsigned char* rope_b = reinterpret_cast<const unsigned char*>(p.rope);
-  u32x4 buf[CPT];
-  auto chunk_tok = [&](int c) {
-    return c < CPT_L ? (c * kPfThreads + tid) / LCH : ((c - CPT_L) * kPfThreads + tid) / RCH;
-  };
-  auto issue = [&](int i) {  // tile i of the split: global -> registers
-    if (i > 0 && (i & 63) == 0) {
-      tabA = tabB;
-      tabB = i + 64 < ntile ? tab_load(i + 64) : 0;
-    }
-    const int phys = pf_clamp_block(__builtin_amdgcn_readlane(tabA, i & 63), p.num_blocks);
+  // Source of this lane's chunk in each of its loads: row, chunk, latent or RoPE.
+  int lrow[NLW], lch[NLW];
+  bool llat[NLW];
+#pragma unroll
+  for (int i = 0; i < NLW; ++i) {
+    const int q = wave + kPfWaves * i;
+    const int pos = 64 * q + lane;  // 16-byte chunk of the buffer
+    llat[i] = pos < LAT / 16;
+    const int pr = llat[i] ? pos : pos - LAT / 16;
+    lrow[i] = llat[i] ? pr / LP : pr / RP;
+    lch[i] = llat[i] ? (pr % LP) ^ lat_swz<LCH>(lrow[i]) : (pr % RP) ^ rope_swz<RCH>(lrow[i]);
+  }
+  // Tile i of the split into buffer dst: rows at or past vmax (which may
+  // hold NaN) are loaded from the tile's last visible row instead; their
+  // probabilities are exactly 0.
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
+  auto issue = [&](int i, unsigned char* dst, int phys) {
     const unsigned char* lb = lat_b + (int64_t)phys * p.lsb * 2;
     const unsigned char* rb = rope_b + (int64_t)phys * p.rsb * 2;
+    const int last = vmax - 1 - (tile0 + i) * kPfTile;  // >= 0: the tile holds a visible token
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int t = chunk_tok(c);
-      if (c < CPT_L)
-        buf[c] = ld16(lb + (uint32_t)(t * p.lst * 2) + ((c * kPfThreads + tid) % LCH) * 16);
-      else
-        buf[c] = ld16(rb + (uint32_t)(t * p.rst * 2) + (((c - CPT_L) * kPfThreads + tid) % RCH) * 16);
+    for (int l = 0; l < NLW; ++l) {
+      const int q = wave + kPfWaves * l;
+      const int r = min(lrow[l], last);
+      const unsigned char* src = llat[l] ? lb + (int64_t)r * p.lst * 2 + lch[l] * 16
+                                         : rb + (int64_t)r * p.rst * 2 + lch[l] * 16;
+      pf_load_lds16(src, lds_base + (uint32_t)(dst - smem) + 1024 * q);
     }
   };
-  auto stage = [&](int i, unsigned char* dst) {  // registers -> LDS, rows past vmax zeroed
-    const int tok0 = (tile0 + i) * kPfTile;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int t = chunk_tok(c);
-      const int off = c < CPT_L ? (t * LP + (c * kPfThreads + tid) % LCH) * 16
-                                : LAT + (t * RP + ((c - CPT_L) * kPfThreads + tid) % RCH) * 16;
-      *reinterpret_cast<u32x4*>(dst + off) = tok0 + t < vmax ? buf[c] : u32x4{};
-    }
+  // wait until this wave's loads of the tile before the newest one (or of all) are in LDS
+  auto wait_loads = [&](bool newer_in_flight) {
+    if (newer_in_flight)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | NLW);  // vmcnt(NLW)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
   };
 
   f32x16 accA[NDT], accB[NDT];
@@ -258,18 +295,35 @@ mlra_prefill(PrefillParams p) {
   for (int dt = 0; dt < NDT; ++dt) accA[dt] = accB[dt] = f32x16{};
   float mA = -INFINITY, lA = 0.f, mB = -INFINITY, lB = 0.f;
 
-  const int a_l = (n * LP + g * (LCH / 2)) * 16;  // S^T A operand: token row n
-  const int a_r = (n * RP + g * (RCH / 2)) * 16;
-  const int a_t = (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
-                  (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  // LDS byte offsets this lane reads inside a 32-token sub-tile (all
+  // swizzles have period 16 in the row, so sub-tiles and the row halves
+  // 16..31 reuse them): S^T A operands (token row n, k-step st), and the
+  // transposed C^T operands (rows r0 + 8*half (+16), feature tile dt).
+  int a_l[NL], a_r[NR], a_t[2][NDT];
+#pragma unroll
+  for (int st = 0; st < NL; ++st) a_l[st] = (n * LP + ((g * (LCH / 2) + st) ^ lat_swz<LCH>(n))) * 16;
+#pragma unroll
+  for (int st = 0; st < NR; ++st) a_r[st] = LAT + (n * RP + ((g * (RCH / 2) + st) ^ rope_swz<RCH>(n))) * 16;
+  {
+    const int r0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int lc0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        a_t[half][dt] = (r0 + 8 * half) * LP * 16 + (((lc0 + 4 * dt) ^ lat_swz<LCH>(r0 + 8 * half)) * 16) +
+                        (lane & 1) * 8;
+  }
 
-  // S^T of both row tiles for the sub-tile with latent rows at sl, RoPE at sr.
-  auto scores = [&](const unsigned char* sl, const unsigned char* sr, f32x16& sa, f32x16& sb) {
+  // S^T of both row tiles for sub-tile u of the tile at buf.
+  auto scores = [&](const unsigned char* buf, int u, f32x16& sa, f32x16& sb) {
     bf16x8 aR[NR], aL[NL];
+    const unsigned char* sl = buf + u * 32 * LP * 16;
+    const unsigned char* sr = buf + u * 32 * RP * 16;
 #pragma unroll
-    for (int st = 0; st < NR; ++st) aR[st] = pf_rd16(sr + a_r + st * 16);
+    for (int st = 0; st < NR; ++st) aR[st] = pf_rd16(sr + a_r[st]);
 #pragma unroll
-    for (int st = 0; st < NL; ++st) aL[st] = pf_rd16(sl + a_l + st * 16);
+    for (int st = 0; st < NL; ++st) aL[st] = pf_rd16(sl + a_l[st]);
     sa = f32x16{};
     sb = f32x16{};
 #pragma unroll
@@ -340,8 +394,8 @@ mlra_prefill(PrefillParams p) {
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const i16x4 lo = pf_read_tr(vl + a_t + (16 * h2) * LP * 16 + dt * 64);
-        const i16x4 hi = pf_read_tr(vl + a_t + (16 * h2 + 8) * LP * 16 + dt * 64);
+        const i16x4 lo = pf_read_tr(vl + a_t[0][dt] + (16 * h2) * LP * 16);
+        const i16x4 hi = pf_read_tr(vl + a_t[1][dt] + (16 * h2) * LP * 16);
         const bf16x8 at = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         accA[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pa[h2], accA[dt], 0, 0, 0);
         accB[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pb[h2], accB[dt], 0, 0, 0);
@@ -353,16 +407,21 @@ mlra_prefill(PrefillParams p) {
     // scores of j while the probabilities of j-1 are formed and multiplied
     // into the outputs, so the vector work of one sub-tile runs beside the
     // matrix work of the next. Tile i (sub-tiles 2i, 2i+1) sits in buffer
-    // i % 3; it is staged from registers and published by a barrier at the
-    // start of iteration 2i, and the loads of tile i+1 leave right after.
-    // The buffer staged there last held tile i-3, whose last reads were in
-    // iteration 2i-4, before the barrier of iteration 2i-2.
-    issue(0);
-    stage(0, smem);
-    if (ntile > 1) issue(1);
+    // i % 4; its loads leave at the start of iteration 2i-4 (two tiles
+    // ahead), and at the start of iteration 2i each wave waits for its own
+    // loads of it and a barrier publishes them. The buffer those loads
+    // write last held tile i-4, whose last reads were in iteration 2i-6,
+    // before the barrier of iteration 2i-4 that precedes them.
+    pf_lds_barrier();  // block ids staged
+    issue(0, smem, block_of(0));
+    if (ntile > 1) issue(1, smem + BUF, block_of(1));
+    wait_loads(ntile > 1);
     pf_lds_barrier();
+    // the transition into tile 0: tile 2 leaves now
+    if (ntile > 2) issue(2, smem + 2 * BUF, block_of(2));
+    int phys_next = ntile > 3 ? block_of(3) : 0;
     f32x16 sA, sB;
-    scores(smem, smem + LAT, sA, sB);
+    scores(smem, 0, sA, sB);
     if (jm == 0)
       settle(row_max(sA, visA, t_lo, std::true_type{}), row_max(sB, visB, t_lo, std::true_type{}));
     else
@@ -371,15 +430,19 @@ mlra_prefill(PrefillParams p) {
     auto step = [&](int j, auto mask) {
       prev = cur;
       if ((j & 1) == 0) {
-        cur = cur == 2 ? 0 : cur + 1;
-        stage(j >> 1, smem + cur * BUF);
+        const int t = j >> 1;
+        cur = (cur + 1) & 3;
+        wait_loads(t + 1 < ntile);
         pf_lds_barrier();
-        if ((j >> 1) + 1 < ntile) issue((j >> 1) + 1);
+        if (t + 2 < ntile) {
+          issue(t + 2, smem + ((cur + 2) & 3) * BUF, phys_next);
+          phys_next = t + 3 < ntile ? block_of(t + 3) : 0;
+        }
       }
       const unsigned char* kb = smem + cur * BUF;
       const unsigned char* vb = smem + prev * BUF + ((j - 1) & 1) * 32 * LP * 16;
       f32x16 nA, nB;
-      scores(kb + (j & 1) * 32 * LP * 16, kb + LAT + (j & 1) * 32 * RP * 16, nA, nB);
+      scores(kb, j & 1, nA, nB);
       bf16x8 pA[2], pB[2];
       probs(sA, mA, lA, pA);
       probs(sB, mB, lB, pB);
@@ -542,6 +605,8 @@ mlra_status prefill_plan(const Resolved& r, int32_t num_cus, int32_t num_splits,
     want = 1;
   else
     want = std::min<int64_t>(pf_cdiv(num_cus, base), std::max<int64_t>(1, max_tiles / 2));
+  // a split's block ids are staged in LDS: at most kPfMaxTiles tiles
+  want = std::max<int64_t>(want, pf_cdiv(max_tiles, kPfMaxTiles));
   const int64_t tps = pf_cdiv(max_tiles, std::min<int64_t>(want, max_tiles));
   const int64_t spl = pf_cdiv(max_tiles, tps);
   if (base * spl > INT32_MAX) return MLRA_ERR_UNSUPPORTED;
@@ -554,8 +619,8 @@ mlra_status prefill_plan(const Resolved& r, int32_t num_cus, int32_t num_splits,
   p.tiles_per_split = (int32_t)tps;
   p.splits_per_seq = (int32_t)spl;
   p.kernel_variant = kVariantPrefillBf16;
-  p.lds_bytes = r.DC == 128 ? (r.DR == 64 ? PfLayout<128, 64>::LDS : PfLayout<128, 32>::LDS)
-                            : (r.DR == 64 ? PfLayout<64, 64>::LDS : PfLayout<64, 32>::LDS);
+  p.lds_bytes = r.DC == 128 ? (r.DR == 64 ? PfLayout<128, 64>::TOTAL : PfLayout<128, 32>::TOTAL)
+                            : (r.DR == 64 ? PfLayout<64, 64>::TOTAL : PfLayout<64, 32>::TOTAL);
   p.row_groups = (int32_t)RT;
   if (!dir) {
     const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;
@@ -568,7 +633,7 @@ mlra_status prefill_plan(const Resolved& r, int32_t num_cus, int32_t num_splits,
 
 template <int DC, int DR>
 hipError_t launch_prefill(const PrefillParams& pp, int64_t groups, hipStream_t st) {
-  constexpr uint32_t lds = PfLayout<DC, DR>::LDS;
+  constexpr uint32_t lds = PfLayout<DC, DR>::TOTAL;
   // more than 64 KB of dynamic LDS must be allowed once per kernel instance
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&mlra_prefill<DC, DR>),

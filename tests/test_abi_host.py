@@ -246,6 +246,7 @@ def test_prefill_plan_covers_rows_and_tiles(lib, cfg):
     assert p.splits_per_seq * p.tiles_per_split >= max_tiles
     assert (p.splits_per_seq - 1) * p.tiles_per_split < max_tiles
     assert p.target_groups == p.row_groups * cfg.num_seqs * cfg.n_branch * p.splits_per_seq
+    assert p.tiles_per_split <= 1024  # a split's block ids are staged in LDS
     assert p.lds_bytes <= 160 * 1024
     direct = p.splits_per_seq == 1 and cfg.n_branch == 1
     if direct:
@@ -267,6 +268,10 @@ def test_prefill_plan_splits_only_when_rows_leave_cus_idle(lib):
     d = _dims(small, num_splits=3)
     st, p = _pplan(lib, d, 1)
     assert st == 0 and p.splits_per_seq == 3
+    # a split covers at most 1024 tiles even when the rows alone fill the GPU
+    d = _dims(cfg.with_(context=2_000_000))
+    st, p = _pplan(lib, d, 1)
+    assert st == 0 and p.tiles_per_split <= 1024 and p.splits_per_seq == 31
     # CONCAT with one split needs no workspace even with four branches
     d = _dims(cfg.with_(n_branch=4), reduce=_lib.MLRA_BRANCH_CONCAT)
     st, p = _pplan(lib, d, 4)

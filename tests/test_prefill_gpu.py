@@ -202,3 +202,22 @@ def test_full_size_fused_branches_sampled_tokens():
     cfg = configs.MLRA4_FUSED_PREFILL
     for reduce in ("sum", "concat"):
         _sampled(cfg, [0, 5, 256, 511], reduce)
+
+
+def test_long_context_splits_past_the_staged_block_ids():
+    # 70,000 cached tokens (1094 tiles) and rows enough that one split would
+    # fill the GPU: a split's block ids are staged in LDS (at most 1024
+    # tiles), so the context is cut in two and the halves merged
+    cfg = _cfg(num_seqs=1, q_len=2048, num_heads=32, n_branch=1, context=70_000,
+               context_range=None, seed=47)
+    inp = make_inputs(cfg)
+    d = to_device(inp)
+    dims = api.make_dims(d["q_latent"], d["q_rope"], d["latent_cache"], d["rope_cache"],
+                         d["block_table"], max_seq_len=inp.max_seq_len, causal=True)
+    plan = api.make_prefill_plan(dims, 1)
+    assert plan.splits_per_seq == 2 and plan.tiles_per_split <= 1024
+    _say("prefill long context 70000, two splits")
+    out, lse = run_prefill(inp, "sum", dev=d)
+    js = [0, 1, 1023, 2047]
+    ro, rl = oracle_tokens(inp, 0, js, "sum")
+    assert_parity(out[0, js], lse[0, js], ro, rl)
