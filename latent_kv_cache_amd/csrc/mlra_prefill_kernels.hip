@@ -14,9 +14,9 @@
 // changes is the key: every head of a query token scores the same cached
 // latent and RoPE key (absorbed form), so a workgroup's rows -- 8 query
 // tokens x 32 heads at H = 32 -- share one stream of cache tiles. Each
-// 64-token tile is read from HBM (or L2) once per workgroup, staged in LDS,
-// and used by all 4 waves (one per SIMD); a wave holds two 32-row tiles of
-// queries in registers, so every operand it reads from LDS feeds both.
+// 64-token tile is read from HBM (or L2) once per workgroup, loaded straight
+// into LDS, and used by all 8 waves (two per SIMD), each holding 32 query
+// rows in registers.
 //
 // Per wave and 32-token sub-tile:
 //   S^T = [c ; k_r] [q_lat ; q_rope]^T        32x32x16 bf16 MFMA, K = DC + DR
@@ -46,9 +46,10 @@ constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfLn2 = 0.69314718055994531f;
 // Lazy softmax reference: probabilities exp2(score - m_ref) stay below 2^8.
 constexpr float kPfLazyLog2 = 8.0f;
-constexpr int kPfWaves = 4;               // one per SIMD
-constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfRows = 64 * kPfWaves;    // query rows per workgroup (two 32-row tiles per wave)
+constexpr int kPfRows = 256;              // query rows per workgroup
+// 32-row tiles per wave (8 / kPfNT waves): 1, two waves per SIMD, measured
+// 2-4% faster than one wave per SIMD holding two tiles (kPfNT = 2)
+constexpr int kPfNT = 1;
 constexpr int kPfTile = kBlock;           // tokens per staged tile = one cache block
 constexpr int32_t kVariantPrefillBf16 = 8;  // mlra_decode_plan.kernel_variant of prefill
 constexpr int kPfMaxTiles = 1024;           // 64-token tiles per split (block ids staged in LDS)
@@ -166,20 +167,27 @@ struct PfLayout {
   static constexpr int TOTAL = LDS + kPfMaxTiles * 4;         // + block ids of a split
 };
 
-template <int DC, int DR>
-__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NT 32-row tiles of queries per wave and 8/NT waves per workgroup (256
+// rows either way): NT = 2 is one wave per SIMD holding 64 rows, every LDS
+// operand feeding two tiles; NT = 1 is two waves per SIMD of 32 rows, so
+// one wave's waits are filled by the other's work.
+template <int DC, int DR, int NT>
+__global__ void __launch_bounds__(64 * (8 / NT)) __attribute__((amdgpu_waves_per_eu(3 - NT, 3 - NT)))
 mlra_prefill(PrefillParams p) {
+  constexpr int W = 8 / NT, THREADS = 64 * W;
   constexpr int NL = DC / 16, NR = DR / 16, NDT = DC / 32;
   constexpr int LCH = DC / 8, RCH = DR / 8;
   using Lay = PfLayout<DC, DR>;
   constexpr int LP = Lay::LP, RP = Lay::RP, LAT = Lay::LAT, BUF = Lay::BUF;
   // A tile buffer is filled by direct global->LDS loads of 64 lanes x 16
   // bytes: load q covers buffer chunks 64q..64q+63; wave w issues loads
-  // w, w + 4, ... (NLW of the NLD).
+  // w, w + W, ... (NLW of the NLD; where W does not divide NLD the last ones
+  // repeat load NLD-1, writing the same bytes again).
   constexpr int NLD = BUF / 1024;
-  constexpr int NLW = NLD / kPfWaves;
-  static_assert((BUF / 16) % (64 * kPfWaves) == 0, "every wave issues the same number of loads");
+  constexpr int NLW = (NLD + W - 1) / W;
+  static_assert(BUF % 1024 == 0, "loads cover a buffer exactly");
   static_assert(Lay::TOTAL <= 160 * 1024, "LDS");
+  static_assert(W * 32 * NT == kPfRows, "256 rows per workgroup");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   // workgroup -> (split, branch, sequence, row tile); the last row tiles,
@@ -210,45 +218,39 @@ mlra_prefill(PrefillParams p) {
   // sub-tiles from jm on hold some token that some row of the group may not see
   const int jm = vmin - t_lo >= 32 ? (vmin - t_lo) / 32 : 0;
 
-  // Two 32-row tiles per wave: A = rows wr0 + n, B = rows wr0 + 32 + n.
-  const int wr0 = r0 + 64 * wave;
-  const int rowA = wr0 + n, rowB = wr0 + 32 + n;
-  const bool liveA = rowA < p.rows, liveB = rowB < p.rows;
-  const int visA = liveA ? pf_visible(L, p.Q, p.H, rowA, p.causal) : 0;
-  const int visB = liveB ? pf_visible(L, p.Q, p.H, rowB, p.causal) : 0;
+  // Row tile t of this wave: rows wr0 + 32t + n.
+  const int wr0 = r0 + 32 * NT * wave;
+  int row[NT], vis[NT];
+  bool live[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    row[t] = wr0 + 32 * t + n;
+    live[t] = row[t] < p.rows;
+    vis[t] = live[t] ? pf_visible(L, p.Q, p.H, row[t], p.causal) : 0;
+  }
 
   // Query rows in registers as the B operand of S^T: k-step st takes
   // features 8st..8st+7 (g = 0) and DC/2 + 8st.. (g = 1), the order the
   // staged rows are read in.
-  bf16x8 qLA[NL], qRA[NR], qLB[NL], qRB[NR];
-  {
-    const int64_t qa = (int64_t)s * p.rows + (liveA ? rowA : 0);
-    const int64_t qb = (int64_t)s * p.rows + (liveB ? rowB : 0);
-    const __bf16* la = p.q_lat + (qa * p.NB + b) * DC + g * (DC / 2);
-    const __bf16* lb = p.q_lat + (qb * p.NB + b) * DC + g * (DC / 2);
-    const __bf16* ra = p.q_rope + qa * DR + g * (DR / 2);
-    const __bf16* rb = p.q_rope + qb * DR + g * (DR / 2);
+  bf16x8 qL[NT][NL], qR[NT][NR];
 #pragma unroll
-    for (int st = 0; st < NL; ++st) {
-      qLA[st] = __builtin_bit_cast(bf16x8, liveA ? ld16(la + 8 * st) : u32x4{});
-      qLB[st] = __builtin_bit_cast(bf16x8, liveB ? ld16(lb + 8 * st) : u32x4{});
-    }
+  for (int t = 0; t < NT; ++t) {
+    const int64_t qrow = (int64_t)s * p.rows + (live[t] ? row[t] : 0);
+    const __bf16* ql = p.q_lat + (qrow * p.NB + b) * DC + g * (DC / 2);
+    const __bf16* qr = p.q_rope + qrow * DR + g * (DR / 2);
 #pragma unroll
-    for (int st = 0; st < NR; ++st) {
-      qRA[st] = __builtin_bit_cast(bf16x8, liveA ? ld16(ra + 8 * st) : u32x4{});
-      qRB[st] = __builtin_bit_cast(bf16x8, liveB ? ld16(rb + 8 * st) : u32x4{});
-    }
+    for (int st = 0; st < NL; ++st) qL[t][st] = __builtin_bit_cast(bf16x8, live[t] ? ld16(ql + 8 * st) : u32x4{});
+#pragma unroll
+    for (int st = 0; st < NR; ++st) qR[t][st] = __builtin_bit_cast(bf16x8, live[t] ? ld16(qr + 8 * st) : u32x4{});
   }
 
-  // Tile loads: chunk c of thread tid is latent chunk c*256 + tid (c <
-  // CPT_L) or RoPE chunk (c - CPT_L)*256 + tid of the tile.
   const int64_t tab_base = (int64_t)s * p.max_blocks;
   const int tile0 = t_lo / kPfTile;
   // The split's block ids, staged in LDS before any tile load: once tile
   // loads are in flight a vector load of the table would make the compiler
   // wait for all of them (it does not track them).
   int* const tabl = reinterpret_cast<int*>(smem + Lay::LDS);
-  for (int i = tid; i < ntile; i += kPfThreads)
+  for (int i = tid; i < ntile; i += THREADS)
     tabl[i] = pf_clamp_block(p.table[tab_base + min(tile0 + i, p.max_blocks - 1)], p.num_blocks);
   auto block_of = [&](int i) { return __builtin_amdgcn_readfirstlane(tabl[i]); };
   const unsigned char* lat_b = reinterpret_cast<const unsigned char*>(p.lat) + (int64_t)b * p.lsbr * 2;
@@ -258,7 +260,7 @@ mlra_prefill(PrefillParams p) {
   bool llat[NLW];
 #pragma unroll
   for (int i = 0; i < NLW; ++i) {
-    const int q = wave + kPfWaves * i;
+    const int q = min(wave + W * i, NLD - 1);
     const int pos = 64 * q + lane;  // 16-byte chunk of the buffer
     llat[i] = pos < LAT / 16;
     const int pr = llat[i] ? pos : pos - LAT / 16;
@@ -275,7 +277,7 @@ mlra_prefill(PrefillParams p) {
     const int last = vmax - 1 - (tile0 + i) * kPfTile;  // >= 0: the tile holds a visible token
 #pragma unroll
     for (int l = 0; l < NLW; ++l) {
-      const int q = wave + kPfWaves * l;
+      const int q = min(wave + W * l, NLD - 1);
       const int r = min(lrow[l], last);
       const unsigned char* src = llat[l] ? lb + (int64_t)r * p.lst * 2 + lch[l] * 16
                                          : rb + (int64_t)r * p.rst * 2 + lch[l] * 16;
@@ -290,10 +292,15 @@ mlra_prefill(PrefillParams p) {
       __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
   };
 
-  f32x16 accA[NDT], accB[NDT];
+  f32x16 acc[NT][NDT];
+  float m[NT], l[NT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) accA[dt] = accB[dt] = f32x16{};
-  float mA = -INFINITY, lA = 0.f, mB = -INFINITY, lB = 0.f;
+  for (int t = 0; t < NT; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[t][dt] = f32x16{};
+  }
 
   // LDS byte offsets this lane reads inside a 32-token sub-tile (all
   // swizzles have period 16 in the row, so sub-tiles and the row halves
@@ -305,18 +312,18 @@ mlra_prefill(PrefillParams p) {
 #pragma unroll
   for (int st = 0; st < NR; ++st) a_r[st] = LAT + (n * RP + ((g * (RCH / 2) + st) ^ rope_swz<RCH>(n))) * 16;
   {
-    const int r0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int tr0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
     const int lc0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        a_t[half][dt] = (r0 + 8 * half) * LP * 16 + (((lc0 + 4 * dt) ^ lat_swz<LCH>(r0 + 8 * half)) * 16) +
-                        (lane & 1) * 8;
+        a_t[half][dt] = (tr0 + 8 * half) * LP * 16 +
+                        (((lc0 + 4 * dt) ^ lat_swz<LCH>(tr0 + 8 * half)) * 16) + (lane & 1) * 8;
   }
 
-  // S^T of both row tiles for sub-tile u of the tile at buf.
-  auto scores = [&](const unsigned char* buf, int u, f32x16& sa, f32x16& sb) {
+  // S^T of the wave's row tiles for sub-tile u of the tile at buf.
+  auto scores = [&](const unsigned char* buf, int u, f32x16 (&sc)[NT]) {
     bf16x8 aR[NR], aL[NL];
     const unsigned char* sl = buf + u * 32 * LP * 16;
     const unsigned char* sr = buf + u * 32 * RP * 16;
@@ -324,72 +331,77 @@ mlra_prefill(PrefillParams p) {
     for (int st = 0; st < NR; ++st) aR[st] = pf_rd16(sr + a_r[st]);
 #pragma unroll
     for (int st = 0; st < NL; ++st) aL[st] = pf_rd16(sl + a_l[st]);
-    sa = f32x16{};
-    sb = f32x16{};
 #pragma unroll
-    for (int st = 0; st < NR; ++st) {
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qRA[st], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qRB[st], sb, 0, 0, 0);
-    }
+    for (int t = 0; t < NT; ++t) sc[t] = f32x16{};
 #pragma unroll
-    for (int st = 0; st < NL; ++st) {
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qLA[st], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qLB[st], sb, 0, 0, 0);
-    }
+    for (int st = 0; st < NR; ++st)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qR[t][st], sc[t], 0, 0, 0);
+#pragma unroll
+    for (int st = 0; st < NL; ++st)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[t][st], sc[t], 0, 0, 0);
   };
-  // Row maximum of a sub-tile (first token tb), in base-2 units; with MASK,
-  // tokens at or past the row's visible length become -inf first. Element r
-  // of lane (n, g) holds token tb + 4g + 8(r/4) + r%4.
-  auto row_max = [&](f32x16& sc, int vis, int tb, auto mask) {
-    if constexpr (decltype(mask)::value) {
-      const int lim = vis - tb - 4 * g;
+  // Row maxima of a sub-tile (first token tb), in base-2 units, then the
+  // lazily moved reference maximum: rescale only when a row maximum exceeds
+  // it by more than kPfLazyLog2 (log2 units). With MASK, tokens at or past
+  // a row's visible length become -inf first; element r of lane (n, g)
+  // holds token tb + 4g + 8(r/4) + r%4.
+  auto settle = [&](f32x16 (&sc)[NT], int tb, auto mask) {
+    float mx[NT];
+    bool first[NT], grow[NT], any = false, rescale = false;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = 8 * (r >> 2) + (r & 3) < lim ? sc[r] : -INFINITY;
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (decltype(mask)::value) {
+        const int lim = vis[t] - tb - 4 * g;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[t][r] = 8 * (r >> 2) + (r & 3) < lim ? sc[t][r] : -INFINITY;
+      }
+      float x = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x = fmaxf(x, sc[t][r]);
+      mx[t] = pf_max_halves(x) * p.score_scale;
+      first[t] = m[t] == -INFINITY;
+      grow[t] = first[t] ? mx[t] > -INFINITY : mx[t] > m[t] + kPfLazyLog2;
+      any = any || grow[t];
+      rescale = rescale || (grow[t] && !first[t]);
     }
-    float mx = -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(any)) {
+      float al[NT];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    return pf_max_halves(mx) * p.score_scale;
-  };
-  // Lazily moved reference maximum: rescale only when a row maximum exceeds
-  // it by more than kPfLazyLog2 (log2 units).
-  auto settle = [&](float mxA, float mxB) {
-    const bool firstA = mA == -INFINITY, firstB = mB == -INFINITY;
-    const bool growA = firstA ? mxA > -INFINITY : mxA > mA + kPfLazyLog2;
-    const bool growB = firstB ? mxB > -INFINITY : mxB > mB + kPfLazyLog2;
-    if (__builtin_amdgcn_ballot_w64(growA || growB)) {
-      const float alA = growA ? __builtin_amdgcn_exp2f(mA - mxA) : 1.f;
-      const float alB = growB ? __builtin_amdgcn_exp2f(mB - mxB) : 1.f;
-      mA = growA ? mxA : mA;
-      mB = growB ? mxB : mB;
-      lA *= alA;
-      lB *= alB;
-      if (__builtin_amdgcn_ballot_w64((growA && !firstA) || (growB && !firstB))) {
+      for (int t = 0; t < NT; ++t) {
+        al[t] = grow[t] ? __builtin_amdgcn_exp2f(m[t] - mx[t]) : 1.f;
+        m[t] = grow[t] ? mx[t] : m[t];
+        l[t] *= al[t];
+      }
+      if (__builtin_amdgcn_ballot_w64(rescale)) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          accA[dt] *= alA;
-          accB[dt] *= alB;
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[t][dt] *= al[t];
       }
     }
   };
   // Probabilities of a sub-tile against the reference, as the B operand of
-  // O^T += C^T P^T, and their sum.
-  auto probs = [&](const f32x16& sc, float m, float& l, bf16x8 (&pb)[2]) {
-    const float m_use = m == -INFINITY ? 0.f : m;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  // O^T += C^T P^T, and their sums.
+  auto probs = [&](const f32x16 (&sc)[NT], bf16x8 (&pb)[NT][2]) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int t = 0; t < NT; ++t) {
+      const float m_use = m[t] == -INFINITY ? 0.f : m[t];
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(sc[8 * h2 + e], p.score_scale, -m_use));
-        ps[e & 3] += pe;
-        pb[h2][e] = (__bf16)pe;
-      }
-    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sc[t][8 * h2 + e], p.score_scale, -m_use));
+          ps[e & 3] += pe;
+          pb[t][h2][e] = (__bf16)pe;
+        }
+      l[t] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
   };
-  // O^T += C^T P^T for both row tiles; value rows (the sub-tile's latent) at vl.
-  auto values = [&](const unsigned char* vl, const bf16x8 (&pa)[2], const bf16x8 (&pb)[2]) {
+  // O^T += C^T P^T for the wave's row tiles; value rows (the sub-tile's latent) at vl.
+  auto values = [&](const unsigned char* vl, const bf16x8 (&pb)[NT][2]) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -397,8 +409,9 @@ mlra_prefill(PrefillParams p) {
         const i16x4 lo = pf_read_tr(vl + a_t[0][dt] + (16 * h2) * LP * 16);
         const i16x4 hi = pf_read_tr(vl + a_t[1][dt] + (16 * h2) * LP * 16);
         const bf16x8 at = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        accA[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pa[h2], accA[dt], 0, 0, 0);
-        accB[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pb[h2], accB[dt], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pb[t][h2], acc[t][dt], 0, 0, 0);
       }
   };
 
@@ -420,12 +433,12 @@ mlra_prefill(PrefillParams p) {
     // the transition into tile 0: tile 2 leaves now
     if (ntile > 2) issue(2, smem + 2 * BUF, block_of(2));
     int phys_next = ntile > 3 ? block_of(3) : 0;
-    f32x16 sA, sB;
-    scores(smem, 0, sA, sB);
+    f32x16 sc[NT];
+    scores(smem, 0, sc);
     if (jm == 0)
-      settle(row_max(sA, visA, t_lo, std::true_type{}), row_max(sB, visB, t_lo, std::true_type{}));
+      settle(sc, t_lo, std::true_type{});
     else
-      settle(row_max(sA, visA, t_lo, std::false_type{}), row_max(sB, visB, t_lo, std::false_type{}));
+      settle(sc, t_lo, std::false_type{});
     int cur = 0, prev = 0;  // buffers of sub-tiles j and j-1
     auto step = [&](int j, auto mask) {
       prev = cur;
@@ -439,38 +452,33 @@ mlra_prefill(PrefillParams p) {
           phys_next = t + 3 < ntile ? block_of(t + 3) : 0;
         }
       }
-      const unsigned char* kb = smem + cur * BUF;
-      const unsigned char* vb = smem + prev * BUF + ((j - 1) & 1) * 32 * LP * 16;
-      f32x16 nA, nB;
-      scores(kb, j & 1, nA, nB);
-      bf16x8 pA[2], pB[2];
-      probs(sA, mA, lA, pA);
-      probs(sB, mB, lB, pB);
-      values(vb, pA, pB);
-      sA = nA;
-      sB = nB;
-      const int tb = t_lo + 32 * j;
-      settle(row_max(sA, visA, tb, mask), row_max(sB, visB, tb, mask));
+      f32x16 nsc[NT];
+      scores(smem + cur * BUF, j & 1, nsc);
+      bf16x8 pb[NT][2];
+      probs(sc, pb);
+      values(smem + prev * BUF + ((j - 1) & 1) * 32 * LP * 16, pb);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sc[t] = nsc[t];
+      settle(sc, t_lo + 32 * j, mask);
     };
     const int j1 = min(max(jm, 1), nsub);
     for (int j = 1; j < j1; ++j) step(j, std::false_type{});
     for (int j = j1; j < nsub; ++j) step(j, std::true_type{});
-    bf16x8 pA[2], pB[2];
-    probs(sA, mA, lA, pA);
-    probs(sB, mB, lB, pB);
-    values(smem + cur * BUF + ((nsub - 1) & 1) * 32 * LP * 16, pA, pB);
+    bf16x8 pb[NT][2];
+    probs(sc, pb);
+    values(smem + cur * BUF + ((nsub - 1) & 1) * 32 * LP * 16, pb);
   }
 
-  lA = pf_sum_halves(lA);
-  lB = pf_sum_halves(lB);
   // O^T element (dt, r) of lane (n, g) is feature dt*32 + 8(r/4) + 4g + r%4 of row n
-  auto write_row = [&](int row, bool live, const f32x16 (&acc)[NDT], float m, float l) {
-    if (!live) return;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse_v = l > 0.f ? (m + __log2f(l)) * kPfLn2 : -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float lt = pf_sum_halves(l[t]);
+    if (!live[t]) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_v = lt > 0.f ? (m[t] + __log2f(lt)) * kPfLn2 : -INFINITY;
     if (p.direct) {
       const float f = inv * p.out_rescale;
-      __bf16* o = p.out + ((int64_t)(s * (int64_t)p.rows + row) * (p.concat ? p.NB : 1) +
+      __bf16* o = p.out + ((int64_t)(s * (int64_t)p.rows + row[t]) * (p.concat ? p.NB : 1) +
                            (p.concat ? b : 0)) * DC;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -478,24 +486,22 @@ mlra_prefill(PrefillParams p) {
         for (int q = 0; q < 4; ++q) {
           bf16x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[dt][4 * q + e] * f);
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[t][dt][4 * q + e] * f);
           *reinterpret_cast<bf16x4*>(o + dt * 32 + 8 * q + 4 * g) = v;
         }
-      if (g == 0) p.lse[((int64_t)s * p.rows + row) * p.NB + b] = lse_v;
+      if (g == 0) p.lse[((int64_t)s * p.rows + row[t]) * p.NB + b] = lse_v;
     } else {
-      const int64_t ri = (((int64_t)s * p.spl + k) * p.NB + b) * p.rows + row;
+      const int64_t ri = (((int64_t)s * p.spl + k) * p.NB + b) * p.rows + row[t];
       float* o = p.part_o + ri * DC;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
-              f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} * inv;
+              f32x4{acc[t][dt][4 * q], acc[t][dt][4 * q + 1], acc[t][dt][4 * q + 2], acc[t][dt][4 * q + 3]} * inv;
       if (g == 0) p.part_lse[ri] = lse_v;
     }
-  };
-  write_row(rowA, liveA, accA, mA, lA);
-  write_row(rowB, liveB, accB, mB, lB);
+  }
 }
 
 // Merge of split partials: one thread per (sequence, row, 4 features). Row r
@@ -615,7 +621,7 @@ mlra_status prefill_plan(const Resolved& r, int32_t num_cus, int32_t num_splits,
   std::memset(&p, 0, sizeof(p));
   p.num_cus = num_cus;
   p.target_groups = (int32_t)(base * spl);
-  p.waves_per_group = kPfWaves;
+  p.waves_per_group = 8 / kPfNT;
   p.tiles_per_split = (int32_t)tps;
   p.splits_per_seq = (int32_t)spl;
   p.kernel_variant = kVariantPrefillBf16;
@@ -636,10 +642,11 @@ hipError_t launch_prefill(const PrefillParams& pp, int64_t groups, hipStream_t s
   constexpr uint32_t lds = PfLayout<DC, DR>::TOTAL;
   // more than 64 KB of dynamic LDS must be allowed once per kernel instance
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&mlra_prefill<DC, DR>),
+      reinterpret_cast<const void*>(&mlra_prefill<DC, DR, kPfNT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((mlra_prefill<DC, DR>), dim3((uint32_t)groups), dim3(kPfThreads), lds, st, pp);
+  hipLaunchKernelGGL((mlra_prefill<DC, DR, kPfNT>), dim3((uint32_t)groups), dim3(64 * (8 / kPfNT)), lds,
+                     st, pp);
   return hipGetLastError();
 }
 

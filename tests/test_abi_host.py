@@ -239,7 +239,7 @@ def _pplan(lib, d, nb, cus=256):
 def test_prefill_plan_covers_rows_and_tiles(lib, cfg):
     d = _dims(cfg)
     st, p = _pplan(lib, d, cfg.n_branch)
-    assert st == 0 and p.kernel_variant == 8 and p.waves_per_group == 4
+    assert st == 0 and p.kernel_variant == 8 and p.waves_per_group == 8
     rows = cfg.num_heads * cfg.q_len
     assert p.row_groups == -(-rows // 256)
     max_tiles = -(-d.max_seq_len // 64)
