@@ -172,6 +172,38 @@ def test_repeat_calls_are_bitwise_identical():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_branch_major_latent_and_padded_rope_strides():
+    # latent stored branch-major [blocks][NB][64][DC] (viewed token-major), RoPE
+    # keys in rows of twice their width: the loads follow the stride arguments
+    cfg = _cfg(num_seqs=2, q_len=30, num_heads=16, n_branch=4, context_range=(30, 400), seed=48)
+    inp = make_inputs(cfg)
+    d = to_device(inp)
+    d["latent_cache"] = d["latent_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert d["latent_cache"].stride(2) == 64 * cfg.d_latent
+    wide = torch.zeros(d["rope_cache"].shape[:2] + (2 * cfg.d_rope,), dtype=d["rope_cache"].dtype,
+                       device=d["rope_cache"].device)
+    wide[..., :cfg.d_rope] = d["rope_cache"]
+    d["rope_cache"] = wide[..., :cfg.d_rope]
+    assert d["rope_cache"].stride(1) == 2 * cfg.d_rope
+    for reduce in ("sum", "concat"):
+        _say(f"prefill strided caches {reduce}")
+        out, lse = run_prefill(inp, reduce, dev=d)
+        assert_parity(out, lse, *oracle(inp, reduce))
+
+
+def test_seq_len_above_max_is_clamped_not_read_out_of_bounds():
+    # a length past max_seq_len is treated as max_seq_len (never a read past
+    # the block table); the result equals the clamped call's
+    cfg = _cfg(num_seqs=2, q_len=20, num_heads=8, context=256, context_range=None, seed=49)
+    inp = make_inputs(cfg)
+    big = np.array([256, 100_000], dtype=np.int32)
+    _say("prefill clamped length")
+    out, lse = run_prefill(inp, "sum", seq_lens=big)
+    ref = run_prefill(inp, "sum", seq_lens=np.array([256, 256], dtype=np.int32))
+    assert np.array_equal(out, ref[0]) and np.array_equal(lse, ref[1])
+    assert_parity(out, lse, *oracle(inp, "sum"))
+
+
 def _sampled(cfg, tokens, reduce="sum"):
     inp = make_inputs(cfg)
     _say(f"prefill full {cfg.name} {reduce}")
