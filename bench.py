@@ -9,6 +9,11 @@ kernel + log-sum-exp combine) over the batch.
 Timing: the caches are replicated into enough copies (each with its own
 block table) that consecutive steps never find their data in the 256 MB
 Infinity Cache; HIP events on the launch stream bracket the K timed steps.
+With --graph the timed steps are replayed from a HIP graph holding one call
+per cache copy (as a serving loop would capture its decode step), and the
+same K steps issued as individual launches are reported as eager_ms_per_step
+(on one box graph replay saved 1.5 us per step, on another it cost 0.4 us,
+so the default stays with individual launches).
 value = algorithmic HBM bytes per step / time per step (GB/s); algorithmic
 bytes = cache rows read + queries + block-table entries + seq_lens + outputs.
 Two more passes issue K launches of each kernel alone (split kernel, then
@@ -25,7 +30,7 @@ paged caches) on the workload's layout, default mlra4_append_b4096_q2.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
                        [--workload NAME] [--no-cpu-baseline] [--graph] [--append]
-                       [--outproj]
+                       [--outproj] [--prefill]
 """
 from __future__ import annotations
 
@@ -476,7 +481,9 @@ def main() -> int:
                          "mlra4_tp_share_prefill_b4_c2048_t8192) instead of decode attention")
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0: enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the timed steps from a HIP graph (the individual-launch time is "
+                         "reported beside as eager_ms_per_step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run K plain device-to-device copies of MIB MiB (the known-size "
                          "reference for scaling HBM byte counters) and exit")
@@ -550,22 +557,28 @@ def main() -> int:
 
     # Timed region: K steps between two events on the launch stream (torch's
     # current stream, which the prepared call enqueues on).
-    torch.cuda.synchronize()
-    head_start()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    def timed_steps(use_graph):
+        torch.cuda.synchronize()
+        head_start()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        if use_graph:
+            reps = max(1, args.steps // copies)
+            for _ in range(reps):
+                graph.replay()
+            n = reps * copies
+        else:
+            for i in range(args.steps):
+                step(i)
+            n = args.steps
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / n, n
+
+    eager_ms, steps = timed_steps(False)
+    ms = eager_ms
     if graph is not None:
-        reps = max(1, args.steps // copies)
-        for _ in range(reps):
-            graph.replay()
-        steps = reps * copies
-    else:
-        for i in range(args.steps):
-            step(i)
-        steps = args.steps
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
+        ms, steps = timed_steps(True)
 
     # Kernel passes: the same K steps issued as one half of the call at a time
     # (K split-kernel launches, then K combine launches over the last
@@ -623,6 +636,7 @@ def main() -> int:
         "tokens_per_s": round(cfg.num_seqs * cfg.q_len / (ms * 1e-3), 1),
         "kv_tokens_per_s": round(ab["kv_tokens"] / (ms * 1e-3), 1),
         "median_step_ms": round(med_ms, 5),
+        "eager_ms_per_step": round(eager_ms, 5),
         "algorithmic_bytes_per_step": ab["total"],
         "kernels": {"split_avg_us": round(split_avg * 1e3, 3),
                     "combine_avg_us": round(comb_avg * 1e3, 3),
