@@ -46,11 +46,10 @@ enum Variant : int32_t {
 // holds at most kPcMaxTiles 64-token tiles (the planner splits longer runs).
 constexpr int kPcMaxTiles = 1024;
 // LDS layout (byte offsets): ring [nslot][slot_bytes] at 0 (the staged query
-// rows alias it), then the merge records of the token streams that finish
-// before the last one of their branch (NB * (4/NB - 1) records of
+// rows alias it), then the merge records of every token stream but the first
+// of its branch, which merges them (NB * (4/NB - 1) records of
 // (DC/32 * 4 + 1) x 64 x 16 bytes; none with four branches), then the block
-// ids, then the counters ready[nslot], consumed[nslot], qdone, arrived[NB],
-// recorded[NB].
+// ids, then the counters ready[nslot], consumed[nslot], qdone, recorded[NB].
 struct PcLds {
   int32_t slot_bytes, nslot, merge, table, flags, total;
 };

@@ -656,11 +656,12 @@ mlra_split_mfma(SplitParams p) {
 // (WT = 4 / NB); per sub-tile it runs S^T = C . Q^T (MFMA, A = slot rows,
 // B = query rows in registers), the online softmax, and O^T += C^T . P^T
 // (A = transpose reads of the slot). With WT > 1 the token streams of a
-// branch merge (m, l, O) at the end without a workgroup barrier: each stream
-// takes an arrival number from an LDS counter; all but the last of a branch
-// leave their state as a record in a dedicated LDS area and exit, and the
-// last one merges those records with its own registers and writes the
-// partial.
+// branch merge (m, l, O) at the end without a workgroup barrier: every
+// stream but the one holding the split's last sub-tile leaves its state as
+// a record in a dedicated LDS area, counts it on an LDS counter and exits;
+// that last stream waits for them and merges the records with its own
+// registers in a fixed stream order (so the partial does not depend on
+// which stream finished first) and writes it.
 __device__ __forceinline__ void lds_wait_geq(const int* flag, int target) {
   // A few million polls (s_sleep 1 each) is far longer than any wait here.
   for (int it = 0; it < (1 << 22); ++it) {
@@ -693,8 +694,7 @@ mlra_split_pc(SplitParams p) {
   int* const ready = reinterpret_cast<int*>(smem + lay.flags);
   int* const consumed = ready + NSLOT;
   int* const qdone = consumed + NSLOT;
-  int* const arrived = qdone + 1;     // [NB] token streams done, per branch
-  int* const recorded = arrived + NB;  // [NB] merge records written, per branch
+  int* const recorded = qdone + 1;  // [NB] merge records written, per branch
   int* const tabl = reinterpret_cast<int*>(smem + lay.table);
 
   const int lane = threadIdx.x & 63;
@@ -843,7 +843,7 @@ mlra_split_pc(SplitParams p) {
 #pragma unroll
     for (int kq = 0; kq < QK; ++kq)
       if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(smem + qdst[kq]) = qv[kq];
-    if (threadIdx.x < 2 * NSLOT + 1 + 2 * NB) ready[threadIdx.x] = 0;  // every counter
+    if (threadIdx.x < 2 * NSLOT + 1 + NB) ready[threadIdx.x] = 0;  // every counter
     lds_barrier();
     // ---------------- compute ----------------
     const unsigned char* const qb = smem + b * kSub * LP * 16 + (n * LP + g * (LCH / 2)) * 16;
@@ -974,12 +974,13 @@ mlra_split_pc(SplitParams p) {
     // Merge the WT token streams of each branch (see above).
     constexpr int REC = NDT * 4 + 1;  // 64-lane f32x4 rows per record
     if (wave >= 4) return;
-    int a = 0;
-    if (lane == 0) a = __hip_atomic_fetch_add(arrived + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    a = __builtin_amdgcn_readfirstlane(a);
     f32x4* const M = reinterpret_cast<f32x4*>(smem + lay.merge) + b * (WT - 1) * REC * 64;
-    if (a < WT - 1) {
-      f32x4* my = M + a * REC * 64;
+    // The stream holding the split's last sub-tile (it finishes last) merges;
+    // stream mst + r (mod WT) writes record r - 1.
+    const int mst = (nsub - 1) % WT;
+    const int r = (strm - mst + WT) % WT;
+    if (r > 0) {
+      f32x4* my = M + (r - 1) * REC * 64;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -990,15 +991,18 @@ mlra_split_pc(SplitParams p) {
       lds_signal(recorded + b);
       return;
     }
-    // The last stream of the branch: the others are done and write one
-    // record each, so this wait is short and always ends.
+    // Stream mst merges the others' records with its own registers in the
+    // order mst, mst + 1, ... (fixed by the split's sub-tile count, so the
+    // result does not depend on which stream finished first). The others
+    // took the sub-tiles before its last one, so this wait is short, and it
+    // always ends.
     lds_wait_geq(recorded + b, WT - 1);
     float ms[WT], ls[WT];
-    ms[WT - 1] = m_run;
-    ls[WT - 1] = l_run;
+    ms[0] = m_run;
+    ls[0] = l_run;
 #pragma unroll
-    for (int w = 0; w < WT - 1; ++w) {
-      const f32x4 ml = M[(w * REC + REC - 1) * 64 + lane];
+    for (int w = 1; w < WT; ++w) {
+      const f32x4 ml = M[((w - 1) * REC + REC - 1) * 64 + lane];
       ms[w] = ml[0];
       ls[w] = ml[1];
     }
@@ -1023,9 +1027,9 @@ mlra_split_pc(SplitParams p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         f32x4 v = f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} *
-                  wsc[WT - 1];
+                  wsc[0];
 #pragma unroll
-        for (int w = 0; w < WT - 1; ++w) v += M[(w * REC + dt * 4 + q) * 64 + lane] * wsc[w];
+        for (int w = 1; w < WT; ++w) v += M[((w - 1) * REC + dt * 4 + q) * 64 + lane] * wsc[w];
         *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
       }
     if (g == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;

@@ -617,6 +617,8 @@ mlra_status prefill_plan(const Resolved& r, int32_t num_cus, int32_t num_splits,
   const int64_t spl = pf_cdiv(max_tiles, tps);
   if (base * spl > INT32_MAX) return MLRA_ERR_UNSUPPORTED;
   const bool dir = spl == 1 && (r.NB == 1 || r.reduce == MLRA_BRANCH_CONCAT);
+  // the merge runs one thread per (sequence, row, 4 features)
+  if (!dir && pf_cdiv((int64_t)r.S * r.rows * (r.DC / 4), 256) > INT32_MAX) return MLRA_ERR_UNSUPPORTED;
   mlra_decode_plan p;
   std::memset(&p, 0, sizeof(p));
   p.num_cus = num_cus;

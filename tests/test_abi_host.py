@@ -291,6 +291,17 @@ def test_prefill_rejects_bad_dims(lib, field, value, status):
     assert st == status, (field, value, st)
 
 
+def test_prefill_rejects_a_merge_grid_past_the_launch_limit(lib):
+    # 1024 sequences x 2^24 rows: 2^27 attention workgroups per branch fit the
+    # grid, but a branch sum needs 2^31 merge workgroups (rows x 32 feature
+    # groups / 256); one branch writes directly, with no merge, and is planned
+    d = _dims(configs.MLRA4_TP_PREFILL, num_seqs=1024, num_heads=1 << 10, q_len=1 << 14)
+    st, _ = _pplan(lib, d, 2)
+    assert st == 3
+    st, p = _pplan(lib, d, 1)
+    assert st == 0 and p.workspace_bytes == 0
+
+
 def test_prefill_rejects_too_many_rows_and_bad_pointers(lib):
     d = _dims(configs.MLRA4_TP_PREFILL, num_heads=1 << 13, q_len=1 << 14)
     st, _ = _pplan(lib, d, 1)
