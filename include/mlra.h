@@ -151,7 +151,9 @@ mlra_status mlra_decode_workspace_size(const mlra_decode_dims* dims, int32_t n_b
  * arithmetic (they may hold NaN). Memory safety on bad input: a seq_lens
  * entry above max_seq_len is treated as max_seq_len, and a table entry
  * outside [0, num_blocks) reads block 0 instead; both give wrong results
- * for that sequence but never an out-of-bounds access.
+ * for that sequence but never an out-of-bounds access. Results are
+ * deterministic: repeated calls with the same inputs, dims and device give
+ * bit-identical out and lse.
  */
 mlra_status mlra_decode_attention(const void* q_latent, const void* q_rope,
                                   const void* latent_cache, const void* rope_cache,
@@ -300,10 +302,15 @@ mlra_status mlra_out_projection(const void* x, const void* w_packed, void* y, in
  *  - bf16 only, d_latent in {64, 128}, d_rope in {32, 64}, n_branch in
  *    {1, 2, 4}; other shapes (and fp32) give MLRA_ERR_UNSUPPORTED;
  *  - num_splits: 0 lets the library split long contexts when the query rows
- *    alone do not fill the GPU; > 0 asks for that many token splits;
+ *    alone do not fill the GPU; > 0 asks for that many token splits; either
+ *    way a split covers at most 1024 64-token tiles (65536 tokens) and longer
+ *    contexts get more splits;
  *  - the workspace is needed only with more than one split, or with
  *    MLRA_BRANCH_SUM over more than one branch: mlra_prefill_workspace_size
- *    returns 0 otherwise, and workspace may then be NULL.
+ *    returns 0 otherwise, and workspace may then be NULL;
+ *  - shapes whose grid would pass 2^31 - 1 workgroups (attention, or the
+ *    merge of splits and branches) give MLRA_ERR_UNSUPPORTED.
+ * Results are deterministic: repeated calls give bit-identical out and lse.
  * mlra_prefill_make_plan fills the decode plan struct: row_groups counts
  * 256-row workgroups per sequence and branch, kernel_variant is 8.
  */
