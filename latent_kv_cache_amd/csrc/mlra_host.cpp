@@ -103,11 +103,14 @@ KernelShape choose_shape(const Resolved& r) {
     return k;
   }
   if (r.DC <= 128) {
-    // Loader/compute kernel: 32 query rows per workgroup, four loader waves
-    // and four compute waves; any tile count per split (up to kPcMaxTiles).
+    // Loader/compute kernel: four loader waves and four compute waves, each
+    // compute wave one (branch, 32-row tile) pair; any tile count per split
+    // (up to kPcMaxTiles). Up to 64 rows, every workgroup of a split reads
+    // only its own branches: four branches at 64 rows take two XCD-paired
+    // workgroups per split, which share the RoPE key through L2.
     k.variant = kVariantPcBf16;
     k.NT = 1;
-    k.NRT = r.rows > 32 ? 2 : 1;  // 64 rows: two XCD-paired workgroups per split
+    k.NRT = r.NB / pc_nbw(r.NB, r.rows);
     k.WD = 1;
     k.WT = 1;
     k.NPF = 0;
@@ -202,7 +205,7 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
   p.lds_bytes = k.variant == kVariantMfmaBf16
                     ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, r.DR, k.NT, k.WT, mfma_qreg(k.NT, r.DC))
                 : k.variant == kVariantPcBf16
-                    ? pc_lds(r.NB, r.DC, r.DR).total
+                    ? pc_lds(pc_nbw(r.NB, r.rows), pc_rt(r.rows), r.DC, r.DR).total
                     : 0;
   // Partials: output [S][spl][NB][rows][DC] and lse [S][spl][NB][rows], fp32.
   const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;

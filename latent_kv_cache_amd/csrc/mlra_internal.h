@@ -45,22 +45,31 @@ enum Variant : int32_t {
 // Loader/compute kernel: block ids of one split are staged in LDS, so a split
 // holds at most kPcMaxTiles 64-token tiles (the planner splits longer runs).
 constexpr int kPcMaxTiles = 1024;
-// LDS layout (byte offsets): ring [nslot][slot_bytes] at 0 (the staged query
-// rows alias it), then the merge records of every token stream but the first
-// of its branch, which merges them (NB * (4/NB - 1) records of
-// (DC/32 * 4 + 1) x 64 x 16 bytes; none with four branches), then the block
-// ids, then the counters ready[nslot], consumed[nslot], qdone, recorded[NB].
+// A workgroup holds RT 32-row tiles of query rows (1 up to 32 rows, 2 up to
+// 64) and NBW of the NB branches: all of them with one row tile; with two,
+// at most two, so that its four compute waves cover every (branch, row tile)
+// pair; four branches then take two workgroups per split (branch groups).
+constexpr int pc_rt(int rows) { return rows > 32 ? 2 : 1; }
+constexpr int pc_nbw(int NB, int rows) { return rows > 32 && NB > 2 ? 2 : NB; }
+// LDS layout (byte offsets): ring [nslot][slot_bytes] at 0 (a slot holds the
+// NBW latents and the RoPE key of 32 tokens; the staged query rows, RT
+// slots' worth, alias it), then the merge records of every token stream but
+// the merging one of each (branch, row tile) pair (P * (4/P - 1) records of
+// (DC/32 * 4 + 1) x 64 x 16 bytes, P = NBW * RT; none when P = 4), then the
+// block ids, then the counters ready[nslot], consumed[nslot], qdone,
+// recorded[P].
 struct PcLds {
   int32_t slot_bytes, nslot, merge, table, flags, total;
 };
-constexpr PcLds pc_lds(int NB, int DC, int DR) {
-  const int slot = (NB * kSub * (DC / 8 + 2) + kSub * (DR / 8 + 1)) * 16;
+constexpr PcLds pc_lds(int NBW, int RT, int DC, int DR) {
+  const int slot = (NBW * kSub * (DC / 8 + 2) + kSub * (DR / 8 + 1)) * 16;
   const int fixed = kPcMaxTiles * 4 + 256;
-  const int rec = NB * (4 / NB - 1) * ((DC / 32) * 4 + 1) * 64 * 16;
+  const int P = NBW * RT;
+  const int rec = P * (4 / P - 1) * ((DC / 32) * 4 + 1) * 64 * 16;
   int nslot = (160 * 1024 - fixed - rec) / slot;
   if (nslot > 12) nslot = 12;
   const int ring = nslot * slot;
-  const int qry = slot;  // the query rows use one slot's layout
+  const int qry = RT * slot;  // the query rows use RT slots' layout
   const int front = ring > qry ? ring : qry;
   return PcLds{slot, nslot, front, front + rec, front + rec + kPcMaxTiles * 4, front + rec + fixed};
 }
@@ -69,8 +78,8 @@ constexpr PcLds pc_lds(int NB, int DC, int DR) {
 // accepts some 32-48 KB of outstanding loads before issue starts to stall;
 // a loader stalled in issue cannot hand over slots whose data has arrived.
 constexpr int kPcLoaderKB = 12;
-constexpr int pc_pl(int NB, int DC, int DR) {
-  const int nload = NB * (DC / 16) + DR / 16;  // 16-byte-per-lane loads per sub-tile
+constexpr int pc_pl(int NBW, int DC, int DR) {
+  const int nload = NBW * (DC / 16) + DR / 16;  // 16-byte-per-lane loads per sub-tile
   const int per = (nload + 3) / 4;
   const int pl = (kPcLoaderKB + per - 1) / per;
   return pl < 2 ? 2 : (pl > 12 ? 12 : pl);
@@ -90,7 +99,8 @@ struct Resolved {
 struct KernelShape {
   int32_t variant;
   int32_t NT;       // 32-row tiles of query rows one wave holds (bf16: 1)
-  int32_t NRT;      // workgroups per split, one per 32 query rows (H*Q <= 64: 1 or 2)
+  int32_t NRT;      // workgroups per split: one per 32 query rows (width-split kernel),
+                    // one per branch group (loader/compute kernel); 1 or 2
   int32_t WD;       // waves that split the latent width of one branch (DC = 512 -> 4)
   int32_t WT;       // waves that split the workgroup's tokens (merged in LDS)
   int32_t NPF;      // sub-tiles in flight per wave (register prefetch depth)

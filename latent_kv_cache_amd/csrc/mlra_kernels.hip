@@ -53,7 +53,7 @@ struct SplitParams {
   float* part_lse;  // [S][spl][NB][rows]
   int64_t lsb, lst, lsbr, rsb, rst;
   int32_t S, Q, H, rows, NB, DC, DR, spl, tps, max_blocks, num_blocks, lcap, causal;
-  int32_t nrt;        // workgroups per split (one per 32 query rows)
+  int32_t nrt;        // workgroups per split: row groups or branch groups (1 or 2)
   float score_scale;  // scale * log2(e): scores kept in base-2 units
 };
 
@@ -645,23 +645,29 @@ mlra_split_mfma(SplitParams p) {
 // (every fourth of its 16-byte-per-lane load instructions, all branches and
 // the shared RoPE key once), so the RoPE key is read once per token.
 //
-// Slot hand-off uses two cumulative LDS counters per slot: ready (loader parts
-// written, 4 per use) and consumed (compute waves done, NB per use). A loader
-// refills slot j % NSLOT for sub-tile j only when the previous occupant was
-// consumed NB times; a compute wave reads it once it is ready 4 times. Every
-// wait is a bounded spin (it ends even if the protocol were broken, leaving
-// wrong results rather than a hung GPU).
+// A workgroup holds NBW branches (branch group grp: branches NBW*grp ...)
+// and RT 32-row tiles of query rows; a slot holds the NBW latents and the
+// RoPE key of one sub-tile, so every cache byte of the split is read once per
+// workgroup, whatever the number of query rows.
 //
-// Compute wave c takes branch b = c % NB and sub-tiles j = c / NB + WT*i
-// (WT = 4 / NB); per sub-tile it runs S^T = C . Q^T (MFMA, A = slot rows,
-// B = query rows in registers), the online softmax, and O^T += C^T . P^T
-// (A = transpose reads of the slot). With WT > 1 the token streams of a
-// branch merge (m, l, O) at the end without a workgroup barrier: every
-// stream but the one holding the split's last sub-tile leaves its state as
-// a record in a dedicated LDS area, counts it on an LDS counter and exits;
-// that last stream waits for them and merges the records with its own
-// registers in a fixed stream order (so the partial does not depend on
-// which stream finished first) and writes it.
+// Slot hand-off uses two cumulative LDS counters per slot: ready (loader parts
+// written, 4 per use) and consumed (compute waves done, P = NBW * RT per use).
+// A loader refills slot j % NSLOT for sub-tile j only when the previous
+// occupant was consumed P times; a compute wave reads it once it is ready 4
+// times. Every wait is a bounded spin (it ends even if the protocol were
+// broken, leaving wrong results rather than a hung GPU).
+//
+// Compute wave c takes the (branch, row tile) pair pi = c % P (branch
+// pi % NBW, row tile pi / NBW) and sub-tiles j = c / P + WT*i (WT = 4 / P);
+// per sub-tile it runs S^T = C . Q^T (MFMA, A = slot rows, B = query rows in
+// registers), the online softmax, and O^T += C^T . P^T (A = transpose reads
+// of the slot). With WT > 1 the token streams of a pair merge (m, l, O) at
+// the end without a workgroup barrier: every stream but the one holding the
+// split's last sub-tile leaves its state as a record in a dedicated LDS
+// area, counts it on an LDS counter and exits; that last stream waits for
+// them and merges the records with its own registers in a fixed stream
+// order (so the partial does not depend on which stream finished first) and
+// writes it.
 __device__ __forceinline__ void lds_wait_geq(const int* flag, int target) {
   // A few million polls (s_sleep 1 each) is far longer than any wait here.
   for (int it = 0; it < (1 << 22); ++it) {
@@ -676,17 +682,19 @@ __device__ __forceinline__ void lds_signal(int* flag) {
     __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <int NB, int DC, int DR, int NSLOT, int PL>
+template <int NBW, int RT, int DC, int DR, int NSLOT, int PL>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mlra_split_pc(SplitParams p) {
-  constexpr int WT = 4 / NB;     // compute waves per branch (token streams)
+  constexpr int NP = NBW * RT;   // (branch, row tile) pairs, one compute wave each
+  constexpr int WT = 4 / NP;     // compute waves per pair (token streams)
   constexpr int NL = DC / 16, NR = DR / 16, NDT = DC / 32;
   constexpr int LCH = DC / 8, RCH = DR / 8;
   constexpr int LQ = kSub * LCH / 64, RQ = kSub * RCH / 64;  // load instructions per sub-tile part
-  constexpr int NLOAD = NB * LQ + RQ;                        // per sub-tile
+  constexpr int NLOAD = NBW * LQ + RQ;                       // per sub-tile
   constexpr int P = (NLOAD + 3) / 4;                         // per loader per sub-tile
   constexpr int LP = mfma_lpitch(DC), RP = mfma_rpitch(DR);
-  constexpr PcLds lay = pc_lds(NB, DC, DR);
+  constexpr PcLds lay = pc_lds(NBW, RT, DC, DR);
+  static_assert(NP == 1 || NP == 2 || NP == 4, "pairs");
   static_assert(lay.nslot == NSLOT && NSLOT >= 2, "slot count");
   static_assert(lay.total <= 160 * 1024, "LDS");
   static_assert((PL - 1) * P <= 63, "outstanding loads fit the counter");
@@ -694,29 +702,31 @@ mlra_split_pc(SplitParams p) {
   int* const ready = reinterpret_cast<int*>(smem + lay.flags);
   int* const consumed = ready + NSLOT;
   int* const qdone = consumed + NSLOT;
-  int* const recorded = qdone + 1;  // [NB] merge records written, per branch
+  int* const recorded = qdone + 1;  // [NP] merge records written, per pair
   int* const tabl = reinterpret_cast<int*>(smem + lay.table);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
-  int k, s, rt = 0;
+  int k, s, grp = 0;
   if (p.nrt == 1) {
     k = blockIdx.x;
     s = blockIdx.y;
-  } else {  // two row groups per split: ids 16c+i and 16c+8+i, dealt to one XCD together
+  } else {  // two branch groups per split: ids 16c+i and 16c+8+i, dealt to one XCD together
     const int id = blockIdx.x;
     const int pr = (id >> 4) * 8 + (id & 7);
     if (pr >= p.S * p.spl) return;
-    rt = (id >> 3) & 1;
+    grp = (id >> 3) & 1;
     s = pr / p.spl;
     k = pr % p.spl;
   }
-  const int row0 = rt * kSub;
+  const int bo = grp * NBW;  // first branch of this workgroup
+  const int NBT = RT == 1 ? NBW : p.NB;  // branches of the call (one group with one row tile)
   const int t0 = k * p.tps;
-  const __bf16* __restrict__ qlat = static_cast<const __bf16*>(p.q_lat);
+  // query and cache bases moved to the workgroup's first branch
+  const __bf16* __restrict__ qlat = static_cast<const __bf16*>(p.q_lat) + bo * DC;
   const __bf16* __restrict__ qrop = static_cast<const __bf16*>(p.q_rope);
-  const __bf16* __restrict__ lat = static_cast<const __bf16*>(p.lat);
+  const __bf16* __restrict__ lat = static_cast<const __bf16*>(p.lat) + bo * p.lsbr;
   const __bf16* __restrict__ rope = static_cast<const __bf16*>(p.rope);
 
   // Prologue. Loader waves read the split's first 64 block ids into a
@@ -732,7 +742,7 @@ mlra_split_pc(SplitParams p) {
   u32x4 buf[PL][P];
   // Load instruction x of a sub-tile (x = q*4 + ld, wrapping: loaders with
   // fewer real loads repeat one, writing the same bytes twice): branch
-  // latent x / LQ instruction x % LQ, or RoPE instruction x - NB*LQ.
+  // latent x / LQ instruction x % LQ, or RoPE instruction x - NBW*LQ.
   auto issue = [&](int j, int phys, u32x4 (&d)[P]) {
     const int sub = (j & 1) * kSub;
     const char* lb = reinterpret_cast<const char*>(lat) + ((int64_t)phys * p.lsb + (int64_t)sub * p.lst) * 2;
@@ -740,8 +750,8 @@ mlra_split_pc(SplitParams p) {
 #pragma unroll
     for (int q = 0; q < P; ++q) {
       const int x = (q * 4 + ld) % NLOAD;
-      const bool isl = x < NB * LQ;
-      const int bb = isl ? x / LQ : 0, ql = isl ? x % LQ : x - NB * LQ;
+      const bool isl = x < NBW * LQ;
+      const int bb = isl ? x / LQ : 0, ql = isl ? x % LQ : x - NBW * LQ;
       const uint32_t off = isl ? (uint32_t)(bb * p.lsbr * 2 + (ql * (64 / LCH) + lane / LCH) * p.lst * 2 + (lane % LCH) * 16)
                                : (uint32_t)((ql * (64 / RCH) + lane / RCH) * p.rst * 2 + (lane % RCH) * 16);
       d[q] = ld16((isl ? lb : rb) + off);
@@ -755,8 +765,10 @@ mlra_split_pc(SplitParams p) {
   };
   f32x16 acc[NDT];
   float m_run = -INFINITY, l_run = 0.f;
-  const int b = wave % NB;          // compute waves: branch
-  const int strm = (wave % 4) / NB;  // compute waves: token stream
+  const int pi = wave % NP;          // compute waves: (branch, row tile) pair
+  const int b = pi % NBW;            // its branch within the group
+  const int row0 = (pi / NBW) * kSub;  // its first query row
+  const int strm = (wave % 4) / NP;  // compute waves: token stream
   // Each role synchronises once with the other (s_barrier counts waves)
   // inside its own branch, so no register of one role is live in the other.
   if (is_loader) {
@@ -772,17 +784,17 @@ mlra_split_pc(SplitParams p) {
     // ---------------- loader ----------------
     auto write = [&](int j, u32x4 (&d)[P]) {
       const int slot = j % NSLOT;
-      lds_wait_geq(consumed + slot, (j / NSLOT) * NB);  // previous occupant done
+      lds_wait_geq(consumed + slot, (j / NSLOT) * NP);  // previous occupant done
       unsigned char* sb = smem + slot * lay.slot_bytes;
       const int tok0 = (t0 + (j >> 1)) * kBlock + (j & 1) * kSub;
 #pragma unroll
       for (int q = 0; q < P; ++q) {
         const int x = (q * 4 + ld) % NLOAD;
-        const bool isl = x < NB * LQ;
-        const int bb = isl ? x / LQ : 0, ql = isl ? x % LQ : x - NB * LQ;
+        const bool isl = x < NBW * LQ;
+        const int bb = isl ? x / LQ : 0, ql = isl ? x % LQ : x - NBW * LQ;
         const int row = isl ? ql * (64 / LCH) + lane / LCH : ql * (64 / RCH) + lane / RCH;
         const int dst = isl ? bb * LAT_B + (row * LP + lane % LCH) * 16
-                            : NB * LAT_B + (row * RP + lane % RCH) * 16;
+                            : NBW * LAT_B + (row * RP + lane % RCH) * 16;
         *reinterpret_cast<u32x4*>(sb + dst) = tok0 + row < L ? d[q] : u32x4{};
       }
       lds_signal(ready + slot);
@@ -811,8 +823,11 @@ mlra_split_pc(SplitParams p) {
 #pragma unroll
     for (int kt = 0; kt < TK; ++kt)
       tv[kt] = p.table[tab_base + min(t0 + kt * 256 + (int)threadIdx.x, p.max_blocks - 1)];
-    constexpr int QL_CH = NB * kSub * LCH;
-    constexpr int Q_CH = QL_CH + kSub * RCH;
+    // query rows of the workgroup: latent [NBW][RT*32 rows][LP chunks], then
+    // RoPE [RT*32][RP]
+    constexpr int QR = RT * kSub;
+    constexpr int QL_CH = NBW * QR * LCH;
+    constexpr int Q_CH = QL_CH + QR * RCH;
     constexpr int QK = (Q_CH + 255) / 256;
     u32x4 qv[QK];
     int qdst[QK];
@@ -821,20 +836,20 @@ mlra_split_pc(SplitParams p) {
       const int x = kq * 256 + threadIdx.x;
       const bool is_lat = x < QL_CH;
       const bool is_rope = !is_lat && x < Q_CH;
-      const int bb = x / (kSub * LCH), rem = x % (kSub * LCH);
+      const int bb = x / (QR * LCH), rem = x % (QR * LCH);
       const int rl = rem / LCH, cl = rem % LCH;
       const int xr = is_rope ? x - QL_CH : 0;
       const int rr = xr / RCH, cr = xr % RCH;
-      const int r = row0 + (is_lat ? rl : rr);
+      const int r = is_lat ? rl : rr;
       const bool live = (is_lat || is_rope) && r < p.rows;
       const int rs = live ? r : 0;
       const int64_t head = ((int64_t)s * p.Q + rs / p.H) * p.H + rs % p.H;
-      const __bf16* src = is_lat ? qlat + (head * NB + (is_lat ? bb : 0)) * DC + cl * 8
+      const __bf16* src = is_lat ? qlat + (head * NBT + (is_lat ? bb : 0)) * DC + cl * 8
                                  : qrop + head * DR + cr * 8;
       const u32x4 v = ld16(src);
       qv[kq] = live ? v : u32x4{};
-      qdst[kq] = is_lat ? ((bb * kSub + rl) * LP + cl) * 16
-                        : (is_rope ? NB * kSub * LP * 16 + (rr * RP + cr) * 16 : -1);
+      qdst[kq] = is_lat ? ((bb * QR + rl) * LP + cl) * 16
+                        : (is_rope ? NBW * QR * LP * 16 + (rr * RP + cr) * 16 : -1);
     }
     sizes();
     if (nsub == 0) return;  // uniform over the workgroup
@@ -843,11 +858,11 @@ mlra_split_pc(SplitParams p) {
 #pragma unroll
     for (int kq = 0; kq < QK; ++kq)
       if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(smem + qdst[kq]) = qv[kq];
-    if (threadIdx.x < 2 * NSLOT + 1 + NB) ready[threadIdx.x] = 0;  // every counter
+    if (threadIdx.x < 2 * NSLOT + 1 + NP) ready[threadIdx.x] = 0;  // every counter
     lds_barrier();
     // ---------------- compute ----------------
-    const unsigned char* const qb = smem + b * kSub * LP * 16 + (n * LP + g * (LCH / 2)) * 16;
-    const unsigned char* const qrb = smem + NB * kSub * LP * 16 + (n * RP + g * (RCH / 2)) * 16;
+    const unsigned char* const qb = smem + ((b * QR + row0 + n) * LP + g * (LCH / 2)) * 16;
+    const unsigned char* const qrb = smem + NBW * QR * LP * 16 + ((row0 + n) * RP + g * (RCH / 2)) * 16;
     auto rd16 = [](const unsigned char* a) {
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
     };
@@ -864,7 +879,7 @@ mlra_split_pc(SplitParams p) {
     const int vis = p.causal ? L - (p.Q - 1 - jr) : L;
     const int min_vis = p.causal ? L - (p.Q - 1) : L;
     const int a_l = (n * LP + g * (LCH / 2)) * 16 + b * LAT_B;  // S^T A operand, row n
-    const int a_r = (n * RP + g * (RCH / 2)) * 16 + NB * LAT_B;
+    const int a_r = (n * RP + g * (RCH / 2)) * 16 + NBW * LAT_B;
     const int a_t = b * LAT_B + (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     for (int j = strm; j < nsub; j += WT) {
@@ -961,7 +976,7 @@ mlra_split_pc(SplitParams p) {
     const int row = row0 + n;
     if (row >= p.rows) return;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int64_t ri = (slotp * NB + b) * p.rows + row;
+    const int64_t ri = (slotp * NBT + bo + b) * p.rows + row;
     float* o = p.part_o + ri * DC;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -971,10 +986,10 @@ mlra_split_pc(SplitParams p) {
             f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} * inv;
     if (g == 0) p.part_lse[ri] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   } else {
-    // Merge the WT token streams of each branch (see above).
+    // Merge the WT token streams of each pair (see above).
     constexpr int REC = NDT * 4 + 1;  // 64-lane f32x4 rows per record
     if (wave >= 4) return;
-    f32x4* const M = reinterpret_cast<f32x4*>(smem + lay.merge) + b * (WT - 1) * REC * 64;
+    f32x4* const M = reinterpret_cast<f32x4*>(smem + lay.merge) + pi * (WT - 1) * REC * 64;
     // The stream holding the split's last sub-tile (it finishes last) merges;
     // stream mst + r (mod WT) writes record r - 1.
     const int mst = (nsub - 1) % WT;
@@ -988,7 +1003,7 @@ mlra_split_pc(SplitParams p) {
           my[(dt * 4 + q) * 64 + lane] =
               f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]};
       my[(REC - 1) * 64 + lane] = f32x4{m_run, l_run, 0.f, 0.f};
-      lds_signal(recorded + b);
+      lds_signal(recorded + pi);
       return;
     }
     // Stream mst merges the others' records with its own registers in the
@@ -996,7 +1011,7 @@ mlra_split_pc(SplitParams p) {
     // result does not depend on which stream finished first). The others
     // took the sub-tiles before its last one, so this wait is short, and it
     // always ends.
-    lds_wait_geq(recorded + b, WT - 1);
+    lds_wait_geq(recorded + pi, WT - 1);
     float ms[WT], ls[WT];
     ms[0] = m_run;
     ls[0] = l_run;
@@ -1020,7 +1035,7 @@ mlra_split_pc(SplitParams p) {
     const int row = row0 + n;
     if (row >= p.rows) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t ri = (slotp * NB + b) * p.rows + row;
+    const int64_t ri = (slotp * NBT + bo + b) * p.rows + row;
     float* o = p.part_o + ri * DC;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -1419,12 +1434,12 @@ static hipError_t dispatch_nb(const SplitParams& sp, const mlra_decode_plan& pla
   return hipErrorInvalidValue;
 }
 
-template <int NB, int DC, int DR>
+template <int NBW, int RT, int DC, int DR>
 static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
                             hipStream_t stream) {
-  constexpr PcLds lay = pc_lds(NB, DC, DR);
-  constexpr int PL = pc_pl(NB, DC, DR);
-  auto kern = mlra_split_pc<NB, DC, DR, lay.nslot, PL>;
+  constexpr PcLds lay = pc_lds(NBW, RT, DC, DR);
+  constexpr int PL = pc_pl(NBW, DC, DR);
+  auto kern = mlra_split_pc<NBW, RT, DC, DR, lay.nslot, PL>;
   static bool attr_set = false;  // per instance; the call is idempotent
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1439,23 +1454,33 @@ static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
   return hipGetLastError();
 }
 
-template <int NB, int DC>
+template <int NBW, int RT, int DC>
 static hipError_t pc_dr(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
-  if (sp.DR == 64) return launch_pc<NB, DC, 64>(sp, plan, st);
-  return launch_pc<NB, DC, 32>(sp, plan, st);
+  if (sp.DR == 64) return launch_pc<NBW, RT, DC, 64>(sp, plan, st);
+  return launch_pc<NBW, RT, DC, 32>(sp, plan, st);
 }
 
-template <int NB>
+template <int NBW, int RT>
 static hipError_t pc_dc(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
-  if (sp.DC == 128) return pc_dr<NB, 128>(sp, plan, st);
-  return pc_dr<NB, 64>(sp, plan, st);
+  if (sp.DC == 128) return pc_dr<NBW, RT, 128>(sp, plan, st);
+  return pc_dr<NBW, RT, 64>(sp, plan, st);
 }
 
+// (branches per workgroup, row tiles) as the planner chose them
 static hipError_t pc_nb(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
-  switch (sp.NB) {
-    case 1: return pc_dc<1>(sp, plan, st);
-    case 2: return pc_dc<2>(sp, plan, st);
-    case 4: return pc_dc<4>(sp, plan, st);
+  const int nbw = pc_nbw(sp.NB, sp.rows), rt = pc_rt(sp.rows);
+  if (sp.NB != nbw * sp.nrt) return hipErrorInvalidValue;
+  if (rt == 1) {
+    switch (nbw) {
+      case 1: return pc_dc<1, 1>(sp, plan, st);
+      case 2: return pc_dc<2, 1>(sp, plan, st);
+      case 4: return pc_dc<4, 1>(sp, plan, st);
+    }
+  } else {
+    switch (nbw) {
+      case 1: return pc_dc<1, 2>(sp, plan, st);
+      case 2: return pc_dc<2, 2>(sp, plan, st);
+    }
   }
   return hipErrorInvalidValue;
 }

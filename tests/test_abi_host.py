@@ -86,6 +86,25 @@ def test_plan_covers_every_tile(lib, cfg):
     assert p.lds_bytes <= 160 * 1024
 
 
+@pytest.mark.parametrize("nb,dc,h,q", [(1, 128, 32, 1), (1, 128, 24, 2), (2, 64, 32, 2),
+                                     (4, 128, 16, 1), (4, 128, 32, 1), (4, 128, 17, 2),
+                                     (4, 64, 32, 2), (1, 512, 32, 2), (2, 256, 24, 2)])
+def test_workgroups_per_split(lib, nb, dc, h, q):
+    # latent 64/128: a workgroup holds every row (up to 64) of at most two
+    # branches when there are more than 32 rows, so only four branches at
+    # 33-64 rows take two workgroups per split (branch groups); the 256/512
+    # width-split kernel takes one workgroup per 32 rows
+    cfg = configs.MLRA4_FUSED.with_(n_branch=nb, d_latent=dc, num_heads=h, q_len=q)
+    st, p = _plan(lib, _dims(cfg), nb)
+    rows = h * q
+    assert st == 0
+    if dc <= 128:
+        assert p.row_groups == (2 if nb == 4 and rows > 32 else 1)
+    else:
+        assert p.row_groups == (2 if rows > 32 else 1)
+    assert p.lds_bytes <= 160 * 1024
+
+
 def test_plan_fills_the_gpu_for_the_single_branch_share(lib):
     d = _dims(configs.MLRA4_TP_SHARE)
     st, p = _plan(lib, d, 1)

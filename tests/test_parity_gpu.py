@@ -168,15 +168,16 @@ def test_fp32_path_small_shapes():
             assert_parity(out, lse, *oracle(inp, reduce), fp32=True)
 
 
-@pytest.mark.parametrize("nb,dc", [(1, 128), (4, 128), (1, 512)])
-def test_split_count_invariance(nb, dc):
+@pytest.mark.parametrize("nb,dc,q", [(1, 128, 1), (4, 128, 1), (1, 512, 1), (4, 128, 2),
+                                    (2, 64, 2)])
+def test_split_count_invariance(nb, dc, q):
     cfg = _cfg(n_branch=nb, d_latent=dc, num_seqs=2, context=None, context_range=(3000, 5000),
-               seed=5 + nb)
+               q_len=q, seed=5 + nb + 10 * q)
     inp = make_inputs(cfg)
     ro, rl = oracle(inp)
     dev = to_device(inp)
     for ns in (1, 2, 7, 0, 79):
-        _say(f"splits nb={nb} dc={dc} num_splits={ns}")
+        _say(f"splits nb={nb} dc={dc} q={q} num_splits={ns}")
         out, lse = run_gpu(inp, num_splits=ns, dev=dev)
         assert_parity(out, lse, ro, rl)
 
@@ -198,10 +199,13 @@ def test_block_relabelling_and_determinism_are_bitwise():
     assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
 
 
-def test_fused_equals_sum_of_single_branch_shares():
-    cfg = _cfg(num_seqs=2, context_range=(500, 1500), seed=9)
+@pytest.mark.parametrize("q", [1, 2])
+def test_fused_equals_sum_of_single_branch_shares(q):
+    # with 64 query rows the fused call splits the branches over two
+    # workgroups per split, a single-branch share holds both row tiles
+    cfg = _cfg(num_seqs=2, context_range=(500, 1500), seed=9, q_len=q)
     inp = make_inputs(cfg)
-    _say("fused vs single-branch shares")
+    _say(f"fused vs single-branch shares q={q}")
     fused, lse_f = run_gpu(inp)
     d = to_device(inp)
     acc = 0
@@ -219,15 +223,16 @@ def test_fused_equals_sum_of_single_branch_shares():
     assert np.linalg.norm(acc - fused) / np.linalg.norm(fused) <= 1e-2
 
 
-def test_branch_major_cache_strides():
-    cfg = _cfg(num_seqs=2, context_range=(64, 900), seed=13)
+@pytest.mark.parametrize("q", [1, 2])
+def test_branch_major_cache_strides(q):
+    cfg = _cfg(num_seqs=2, context_range=(64, 900), seed=13, q_len=q)
     inp = make_inputs(cfg)
     d = to_device(inp)
     # same values stored branch-major [blocks][NB][64][DC], viewed as [blocks][64][NB][DC]
     bm = d["latent_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     assert bm.stride(2) == 64 * cfg.d_latent
     d["latent_cache"] = bm
-    _say("branch-major strides")
+    _say(f"branch-major strides q={q}")
     out, lse = run_gpu(inp, dev=d)
     assert_parity(out, lse, *oracle(inp))
 
