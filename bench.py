@@ -86,7 +86,7 @@ def kernel_source_digest(kernel: str = "mlra_split_pc") -> str:
 
 
 # Split kernel that serves each plan.kernel_variant (include/mlra.h).
-SPLIT_KERNELS = {1: "mlra_split_valu", 2: "mlra_split_mfma", 4: "mlra_split_pc"}
+SPLIT_KERNELS = {1: "mlra_split_valu", 4: "mlra_split_pc"}
 
 
 def measured_traffic(kernel: str, workload: str):

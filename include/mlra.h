@@ -111,10 +111,11 @@ typedef struct mlra_decode_plan {
   int32_t splits_per_seq;      /* splits of the longest sequence; grid = S x this */
   int32_t kernel_variant;      /* internal kernel id (for logs and tests) */
   int32_t lds_bytes;           /* LDS one split workgroup allocates */
-  int32_t row_groups;          /* split-kernel workgroups per split: one per 32 query rows
-                                  (latent 256/512), or, for latent 64/128, two when four
-                                  branches meet more than 32 rows (each takes two
-                                  branches), else one */
+  int32_t row_groups;          /* split-kernel workgroups per split (1 or 2): with more
+                                  than 32 query rows, two when the branches do not fit
+                                  one workgroup (four of width <= 128, two of 256: each
+                                  takes its own) or the latent is 512 wide (each takes
+                                  32 rows), else one */
   size_t workspace_bytes;      /* bytes of device workspace the call needs */
 } mlra_decode_plan;
 

@@ -93,39 +93,20 @@ KernelShape choose_shape(const Resolved& r) {
   KernelShape k{};
   if (r.dtype == MLRA_FP32) {
     k.variant = kVariantValuFp32;
-    k.NT = 1;
     k.NRT = 1;
-    k.WD = 1;
-    k.WT = 1;
-    k.NPF = 1;
     k.waves = 4;  // four (row, branch) pairs per workgroup
     k.groups_per_cu = 2;
     return k;
   }
-  if (r.DC <= 128) {
-    // Loader/compute kernel: four loader waves and four compute waves, each
-    // compute wave one (branch, 32-row tile) pair; any tile count per split
-    // (up to kPcMaxTiles). Up to 64 rows, every workgroup of a split reads
-    // only its own branches: four branches at 64 rows take two XCD-paired
-    // workgroups per split, which share the RoPE key through L2.
-    k.variant = kVariantPcBf16;
-    k.NT = 1;
-    k.NRT = r.NB / pc_nbw(r.NB, r.rows);
-    k.WD = 1;
-    k.WT = 1;
-    k.NPF = 0;
-    k.waves = 8;
-    k.groups_per_cu = 1;
-    return k;
-  }
-  k.variant = kVariantMfmaBf16;
-  // A wave holds 32 query rows; 64 rows run as two workgroups per split.
-  k.NT = 1;
-  k.NRT = r.rows > 32 ? 2 : 1;
-  k.WD = mfma_wd(r.DC);
-  k.WT = mfma_wt(r.NB, r.DC, k.NT);
-  k.NPF = 2;  // sub-tiles in flight per wave (register prefetch)
-  k.waves = r.NB * k.WD * k.WT;
+  // Loader/compute kernel: four loader waves and four compute waves, each
+  // compute wave one (branch, 32-row tile, 128-column latent slice) triple;
+  // any tile count per split (up to kPcMaxTiles). A workgroup reads only its
+  // own branches' latents: the groups of a split (branch groups, or row
+  // groups for the 512-wide latent at 64 rows) are XCD-paired and share the
+  // rest through L2.
+  k.variant = kVariantPcBf16;
+  k.NRT = pc_groups(r.NB, r.rows, r.DC);
+  k.waves = 8;
   k.groups_per_cu = 1;  // one workgroup fills a CU
   return k;
 }
@@ -143,16 +124,19 @@ KernelShape choose_shape(const Resolved& r) {
 static int64_t choose_tiles_per_split(const Resolved& r, const KernelShape& k,
                                       int64_t slots, int64_t max_tiles, int64_t sum_seq_lens) {
   const int64_t elem = r.dtype == MLRA_BF16 ? 2 : 4;
-  const double tile_bytes = (double)kBlock * (r.NB * r.DC + r.DR) * elem;
-  const double partial_bytes = (double)r.NB * (r.rows / k.NRT) * (r.DC + 1) * 4;
+  // one workgroup's share: its branches' tiles and partial results
+  const int nbw = k.variant == kVariantPcBf16 ? pc_nbw(r.NB, r.rows, r.DC) : r.NB;
+  const int row_groups = k.NRT / (r.NB / nbw);
+  const double tile_bytes = (double)kBlock * (nbw * r.DC + r.DR) * elem;
+  const double partial_bytes = (double)nbw * (r.rows / row_groups) * (r.DC + 1) * 4;
   const double fixed = 2.0 + 2.0 * partial_bytes / tile_bytes;
   const bool uniform = sum_seq_lens <= 0 || sum_seq_lens >= (int64_t)r.S * r.lcap;
   const int64_t total = uniform ? (int64_t)r.S * max_tiles : cdiv(sum_seq_lens, kBlock);
-  int64_t top = std::max<int64_t>(cdiv(std::max<int64_t>(max_tiles, 1), k.WT) * k.WT, k.WT);
+  int64_t top = std::max<int64_t>(max_tiles, 1);
   if (k.variant == kVariantPcBf16) top = std::min<int64_t>(top, kPcMaxTiles);
   int64_t best = top;
   double best_cost = -1.0;
-  for (int64_t tps = top; tps >= k.WT; tps -= k.WT) {
+  for (int64_t tps = top; tps >= 1; --tps) {
     const int64_t groups = k.NRT * (uniform ? (int64_t)r.S * cdiv(max_tiles, tps)
                                             : cdiv(total, tps) + cdiv(r.S, 2));
     const double cost =
@@ -188,8 +172,6 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
   }
   if (num_splits > 0) {
     tps = cdiv(std::max<int64_t>(max_tiles, 1), num_splits);
-    tps = std::max<int64_t>(tps, k.WT);
-    tps = cdiv(tps, k.WT) * k.WT;  // every token-split wave gets the same tile count
     // The loader/compute kernel stages a split's block ids in LDS: a request
     // for fewer splits than that allows is raised.
     if (k.variant == kVariantPcBf16) tps = std::min<int64_t>(tps, kPcMaxTiles);
@@ -202,10 +184,8 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
   p.tiles_per_split = (int32_t)tps;
   p.splits_per_seq = (int32_t)spl;
   p.row_groups = k.NRT;
-  p.lds_bytes = k.variant == kVariantMfmaBf16
-                    ? mfma_lds_bytes(r.NB, r.DC / k.WD, k.WD, r.DR, k.NT, k.WT, mfma_qreg(k.NT, r.DC))
-                : k.variant == kVariantPcBf16
-                    ? pc_lds(pc_nbw(r.NB, r.rows), pc_rt(r.rows), r.DC, r.DR).total
+  p.lds_bytes = k.variant == kVariantPcBf16
+                    ? pc_lds(pc_nbw(r.NB, r.rows, r.DC), pc_rt(r.rows, r.DC), pc_wd(r.DC), r.DC, r.DR).total
                     : 0;
   // Partials: output [S][spl][NB][rows][DC] and lse [S][spl][NB][rows], fp32.
   const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;

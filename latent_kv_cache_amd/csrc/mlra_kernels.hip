@@ -9,19 +9,18 @@
 // k_r[t] shared by all branches.
 //
 // Decode is bound by moving the cache from HBM (arXiv 2603.02188 abstract), so
-// the split kernel streams each cache byte exactly once:
-//   * one workgroup per (sequence, split); a split is a run of 64-token tiles
-//     (one cache block each); waves of the workgroup take a branch (NB), a
-//     slice of the latent width (WD) and/or an interleaved share of the tiles
-//     (WT);
-//   * a wave loads 32-token sub-tiles with 16-byte loads straight into the A
-//     operand of v_mfma_f32_32x32x16_bf16: lane (m, g) holds 8 consecutive
-//     features of token m, so S^T = C . Q^T needs no shuffles;
-//   * the score tile lands with the query row along the lanes, so the online
-//     softmax is lane-local plus one v_permlane32_swap for the row max, and
-//     the probabilities are already in B-operand order for O^T += C^T . P^T;
-//   * C^T (tokens along K) is read back from a wave-private LDS copy of the
-//     sub-tile written row-major with 16-byte stores;
+// the split kernel streams each cache byte once per workgroup that needs it:
+//   * one workgroup per (sequence, split, group); a split is a run of 64-token
+//     tiles (one cache block each); four loader waves stream its 32-token
+//     sub-tiles into a ring of LDS slots and four compute waves take them,
+//     each one (branch, 32-row tile, 128-column latent slice) triple;
+//   * S^T = C . Q^T on v_mfma_f32_32x32x16_bf16 with the slot rows as the A
+//     operand (lane (m, g) reads 8 consecutive features of token m) and the
+//     query rows in registers as B; the score tile lands with the query row
+//     along the lanes, so the online softmax is lane-local plus one
+//     v_permlane32_swap for the row max, and the probabilities are already in
+//     B-operand order for O^T += C^T . P^T, whose A operand (tokens along K)
+//     comes from transposing LDS reads of the same slot;
 //   * each (split, branch, row) writes a partial (output / l, lse); the combine
 //     kernel merges the splits with the log-sum-exp rule, sums the branches
 //     (or lays them side by side) and applies the output factor.
@@ -97,7 +96,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 split kernel (MFMA)
+// LDS helpers of the bf16 split kernel
 // ---------------------------------------------------------------------------
 // LDS transpose read (gfx950 ds_read_b64_tr_b16): within each 16-lane group,
 // lane j supplies the address of 4 bf16 at row j/4, column 4*(j%4) of a 4x16
@@ -108,532 +107,15 @@ __device__ __forceinline__ i16x4 lds_read_tr(const unsigned char* p) {
 }
 
 // Staged rows are padded so that every LDS address is a per-lane base plus a
-// compile-time offset. Latent rows get 2 spare 16-byte chunks (pitch = 2 mod 16
-// chunks for 256-byte rows, 10 mod 16 for 128-byte rows): 8 lanes reading one
-// chunk of 8 consecutive rows, and a 16-lane transpose read of 4 consecutive
-// rows x 32 bytes, both land on distinct banks. RoPE rows (read row-wise
-// only) get 1 spare chunk, an odd pitch.
-
-template <int NB, int DCW, int WD, int DR, int NT, int WT, int WPS, int PD, bool QREG>
-__global__ void __launch_bounds__(64 * NB * WD * WT)
-__attribute__((amdgpu_waves_per_eu(WPS)))
-mlra_split_mfma(SplitParams p) {
-  constexpr int DC = DCW * WD;
-  constexpr int NL = DCW / 16;   // S^T k-steps over this wave's latent slice
-  constexpr int NR = DR / 16;    // S^T k-steps over the RoPE key (wave wd == 0)
-  constexpr int NDT = DCW / 32;  // 32-wide d tiles of O^T
-  constexpr int LCH = DCW / 8;   // 16-byte chunks per staged latent row
-  constexpr int RCH = DR / 8;    // 16-byte chunks per staged RoPE row
-  constexpr int LQ = kSub * LCH / 64;  // coalesced 16-byte loads per lane per sub-tile
-  constexpr int RQ = kSub * RCH / 64;
-  // QREG: query rows (the B operand of S^T) live in each wave's registers
-  // (no workgroup barrier before the first MFMA); otherwise they are staged
-  // once per workgroup in LDS.
-  static_assert(!QREG || NT == 1, "register queries hold one row tile");
-  constexpr int WAVES = NB * WD * WT;
-  constexpr int LP = mfma_lpitch(DCW);  // staged row pitch, 16-byte chunks
-  constexpr int RP = mfma_rpitch(DR);
-  static_assert(LQ >= 1 && RQ >= 1 && NDT >= 1, "bad shape");
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
-  const int wd = wave % WD;
-  const int b = (wave / WD) % NB;
-  const int wt = wave / (WD * NB);
-  const int n = lane & 31;
-  const int g = lane >> 5;
-  const bool has_rope = WD == 1 || wd == 0;  // uniform per wave
-
-  // Workgroup -> (split k, sequence s, 32-row tile rt). With two row tiles,
-  // ids 16c + i and 16c + 8 + i (i < 8) are the two row tiles of split pair
-  // 8c + i: workgroups are dealt round-robin over the 8 XCDs, so both land on
-  // one XCD at about the same time and the second reads the tiles from L2.
-  int k, s, rt;
-  if (p.nrt == 1) {
-    k = blockIdx.x;
-    s = blockIdx.y;
-    rt = 0;
-  } else {
-    const int id = blockIdx.x;
-    const int pr = (id >> 4) * 8 + (id & 7);
-    if (pr >= p.S * p.spl) return;  // grid rounded up to 16
-    rt = (id >> 3) & 1;
-    s = pr / p.spl;
-    k = pr % p.spl;
-  }
-  const int row0 = rt * 32;  // first query row of this workgroup
-  const int t0 = k * p.tps;
-  const __bf16* __restrict__ qlat = static_cast<const __bf16*>(p.q_lat);
-  const __bf16* __restrict__ qrop = static_cast<const __bf16*>(p.q_rope);
-  const __bf16* __restrict__ lat = static_cast<const __bf16*>(p.lat);
-  const __bf16* __restrict__ rope = static_cast<const __bf16*>(p.rope);
-
-  // Independent loads first: sequence length, this wave's first 64 block ids
-  // (any id below max_blocks lies inside the table) and the queries.
-  const int L_raw = p.seq_lens[s];
-  const int64_t tab_base = (int64_t)s * p.max_blocks;
-  // Loads in this prologue are unconditional (clamped, in-bounds addresses,
-  // results selected afterwards) so that the compiler can count outstanding
-  // loads exactly and never waits on more than it needs.
-  int tab = p.table[tab_base + min(t0 + wt + WT * lane, p.max_blocks - 1)];
-  int tab_chunk = 0;
-
-  // Query rows (the B operand of S^T = C . Q^T) are staged once per workgroup
-  // in LDS, padded like the cache tiles: latent rows per (branch, width
-  // slice), RoPE rows once (shared by all branches). Every wave loads a share
-  // first, before its cache loads, so that writing it to LDS waits only on
-  // these loads. K-slot (g, e) of step st is latent feature g*DCW/2 + 8*st + e
-  // of the slice, or RoPE feature g*DR/2 + 8*st + e. Padding rows are zero.
-  constexpr int QL_CH = NB * WD * NT * kSub * LCH;  // latent query chunks
-  constexpr int Q_CH = QL_CH + NT * kSub * RCH;     // + RoPE query chunks
-  constexpr int QK = QREG ? 0 : (Q_CH + WAVES * 64 - 1) / (WAVES * 64);
-  u32x4 qv[QK > 0 ? QK : 1];
-  int qdst[QK > 0 ? QK : 1];  // LDS byte offset in the query region, -1 = none
-#pragma unroll
-  for (int kq = 0; kq < QK; ++kq) {
-    const int x = (kq * WAVES + wave) * 64 + lane;
-    const bool is_lat = x < QL_CH;
-    const bool is_rope = !is_lat && x < Q_CH;
-    // latent chunk coordinates
-    const int gq = x / (NT * kSub * LCH), rem = x % (NT * kSub * LCH);
-    const int rl = rem / LCH, cl = rem % LCH;
-    // RoPE chunk coordinates
-    const int xr = is_rope ? x - QL_CH : 0;
-    const int rr = xr / RCH, cr = xr % RCH;
-    const int r = row0 + (is_lat ? rl : rr);
-    const bool live = (is_lat || is_rope) && r < p.rows;
-    const int rs = live ? r : 0;
-    const int j = rs / p.H, h = rs % p.H;
-    const int64_t head = ((int64_t)s * p.Q + j) * p.H + h;
-    const __bf16* src = is_lat ? qlat + (head * NB + (is_lat ? gq / WD : 0)) * DC +
-                                     (is_lat ? gq % WD : 0) * DCW + cl * 8
-                               : qrop + head * DR + cr * 8;
-    const u32x4 v = ld16(src);
-    qv[kq] = live ? v : u32x4{};
-    qdst[kq] = is_lat ? ((gq * NT * kSub + rl) * LP + cl) * 16
-                      : (is_rope ? NB * WD * NT * kSub * LP * 16 + (rr * RP + cr) * 16 : -1);
-  }
-
-  int jrow[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = row0 + nt * 32 + n;
-    jrow[nt] = row < p.rows ? row / p.H : 0;
-  }
-  // Register-resident queries: lane (n, g) holds row n's features of K-slot
-  // group g (same K-slot order as the staged layout). Loaded unconditionally
-  // from a clamped row, zeroed for padding rows.
-  constexpr int NLq = QREG ? NL : 1, NRq = QREG ? NR : 1;
-  bf16x8 qLr[NLq], qRr[NRq];
-  if constexpr (QREG) {
-    const int row = row0 + n;
-    const bool ok = row < p.rows;
-    const int rs = ok ? row : 0;
-    const int j = rs / p.H, h = rs % p.H;
-    const int64_t head = ((int64_t)s * p.Q + j) * p.H + h;
-    const __bf16* ql = qlat + (head * NB + b) * DC + wd * DCW + g * (DCW / 2);
-    const __bf16* qr = qrop + head * DR + g * (DR / 2);
-#pragma unroll
-    for (int st = 0; st < NL; ++st) {
-      const u32x4 v = ld16(ql + 8 * st);
-      qLr[st] = __builtin_bit_cast(bf16x8, ok ? v : u32x4{});
-    }
-#pragma unroll
-    for (int st = 0; st < NR; ++st) {
-      const u32x4 v = ld16(qr + 8 * st);
-      qRr[st] = __builtin_bit_cast(bf16x8, (ok && has_rope) ? v : u32x4{});
-    }
-  }
-
-  const int L = L_raw < 0 ? 0 : (L_raw > p.lcap ? p.lcap : L_raw);
-  const int ntiles = (L + kBlock - 1) / kBlock;
-  if (t0 >= ntiles) return;  // uniform over the workgroup: no barrier skipped
-  const int t1 = min(t0 + p.tps, ntiles);
-  int vis[NT];
-  const int min_vis = p.causal ? L - (p.Q - 1) : L;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) vis[nt] = p.causal ? L - (p.Q - 1 - jrow[nt]) : L;
-
-  // Query rows, the B operand of S^T = C . Q^T, staged once per (branch,
-  // width slice) in LDS with the same padded row layout as the cache tiles.
-  // K-slot (g, e) of step st is latent feature g*DCW/2 + 8*st + e of this
-  // wave's slice, or RoPE feature g*DR/2 + 8*st + e. Padding rows are zero.
-  // LDS layout (see mfma_lds_bytes). The RoPE query rows are shared by all
-  // branches and staged once; RoPE tiles only by the waves that use them.
-  // Slotted layout (one latent and RoPE stage per wave, WD == 1, queries in
-  // registers): each wave owns one slot that later holds its merge record, so
-  // a wave that has finished its tiles publishes its record without waiting
-  // for the others.
-  constexpr int REC_B = (NT * NDT * 4 + 1) * 64 * 16;  // merge record bytes per wave
-  constexpr int STAGE_B = kSub * (LP + RP) * 16;
-  constexpr bool kSlotted = mfma_slotted(WD, WT, QREG);
-  constexpr int SLOT_B = STAGE_B > REC_B ? STAGE_B : REC_B;
-  static_assert(!kSlotted || WAVES * SLOT_B <= 160 * 1024, "slotted LDS layout exceeds 160 KB");
-  unsigned char* stage_l = kSlotted ? smem + wave * SLOT_B : smem + wave * kSub * LP * 16;
-  unsigned char* const rope_base = smem + WAVES * kSub * LP * 16;
-  unsigned char* stage_r = kSlotted ? stage_l + kSub * LP * 16
-                                    : rope_base + (wt * NB + b) * kSub * RP * 16;
-  unsigned char* const q_base = rope_base + NB * WT * kSub * RP * 16;
-  unsigned char* q_l = q_base + (b * WD + wd) * NT * kSub * LP * 16;
-  unsigned char* q_r = q_base + NB * WD * NT * kSub * LP * 16;
-  float* xchg = reinterpret_cast<float*>(QREG ? q_base : q_r + NT * kSub * RP * 16);
-  f32x16 acc[NT][NDT];
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[nt][dt] = f32x16{};
-  }
-
-  // This wave's tiles are t0 + wt + WT*i; each is two 32-token sub-tiles.
-  const int nu = 2 * ((t1 - t0 + WT - 1) / WT);
-
-  // Coalesced loads of one sub-tile: instruction q, lane -> 16-byte chunk
-  // x = 64*q + lane, i.e. row x / CH, chunk x % CH. Every address is valid: a
-  // missing tile reads block 0 and rows past L stay inside their block; such
-  // rows are zeroed (zero_tail) before any arithmetic.
-  u32x4 bl[PD][LQ], br[PD][RQ];
-  // lane -> (row, chunk) of the first load instruction; instruction q adds
-  // 64/CH rows. Offsets are bytes within one cache block (< 2^31, checked on
-  // the host).
-  const uint32_t l_lane = (uint32_t)((lane / LCH) * p.lst * 2 + (lane % LCH) * 16);
-  const uint32_t l_step = (uint32_t)((64 / LCH) * p.lst * 2);
-  const uint32_t r_lane = (uint32_t)((lane / RCH) * p.rst * 2 + (lane % RCH) * 16);
-  const uint32_t r_step = (uint32_t)((64 / RCH) * p.rst * 2);
-  auto load_unit = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
-    const int i = u >> 1;
-    const int ti = t0 + wt + WT * i;
-    const bool valid = (u < nu) && ti < t1;
-    if ((i >> 6) != tab_chunk) {  // uniform: next 64 block ids of this wave
-      tab_chunk = i >> 6;
-      tab = p.table[tab_base + min(t0 + wt + WT * (tab_chunk * 64 + lane), p.max_blocks - 1)];
-    }
-    const int phys = valid ? clamp_block(__builtin_amdgcn_readlane(tab, i & 63), p.num_blocks) : 0;
-    const int sub = (u & 1) * kSub;
-    // uniform base of this sub-tile (scalar registers) + 32-bit lane offset
-    const char* lb = reinterpret_cast<const char*>(lat) +
-                     ((int64_t)phys * p.lsb + (int64_t)sub * p.lst + (int64_t)b * p.lsbr + wd * DCW) * 2;
-#pragma unroll
-    for (int q = 0; q < LQ; ++q) dl[q] = ld16(lb + (size_t)q * l_step + l_lane);
-    if (has_rope) {
-      const char* rbp = reinterpret_cast<const char*>(rope) +
-                        ((int64_t)phys * p.rsb + (int64_t)sub * p.rst) * 2;
-#pragma unroll
-      for (int q = 0; q < RQ; ++q) dr[q] = ld16(rbp + (size_t)q * r_step + r_lane);
-    }
-  };
-  auto zero_tail = [&](int u, u32x4 (&dl)[LQ], u32x4 (&dr)[RQ]) {
-    const int ti = t0 + wt + WT * (u >> 1);
-    const bool valid = (u < nu) && ti < t1;
-    const int tok0 = ti * kBlock + (u & 1) * kSub;
-    if (!(valid && tok0 + kSub <= L)) {  // uniform
-#pragma unroll
-      for (int q = 0; q < LQ; ++q) {
-        const bool keep = valid && tok0 + (q * 64 + lane) / LCH < L;
-        dl[q] = keep ? dl[q] : u32x4{};
-      }
-#pragma unroll
-      for (int q = 0; q < RQ; ++q) {
-        const bool keep = valid && tok0 + (q * 64 + lane) / RCH < L;
-        dr[q] = keep ? dr[q] : u32x4{};
-      }
-    }
-  };
-  unsigned char* const wl_base = stage_l + ((lane / LCH) * LP + lane % LCH) * 16;
-  unsigned char* const wr_base = stage_r + ((lane / RCH) * RP + lane % RCH) * 16;
-  auto stage_unit = [&](const u32x4 (&dl)[LQ], const u32x4 (&dr)[RQ]) {
-#pragma unroll
-    for (int q = 0; q < LQ; ++q)
-      *reinterpret_cast<u32x4*>(wl_base + q * (64 / LCH) * LP * 16) = dl[q];
-    if (has_rope) {
-#pragma unroll
-      for (int q = 0; q < RQ; ++q)
-        *reinterpret_cast<u32x4*>(wr_base + q * (64 / RCH) * RP * 16) = dr[q];
-    }
-  };
-
-  // lane bases of the operand reads: row n, chunk g*CH/2 (A of S^T); the
-  // transpose reads of C^T start at row 4*(lane/32) + (lane%16)/4, column
-  // 16*((lane/16)%2) + 4*(lane%4).
-  const unsigned char* const al_base = stage_l + (n * LP + g * (LCH / 2)) * 16;
-  const unsigned char* const ar_base = stage_r + (n * RP + g * (RCH / 2)) * 16;
-  const unsigned char* const ql_base = q_l + (n * LP + g * (LCH / 2)) * 16;
-  const unsigned char* const qr_base = q_r + (n * RP + g * (RCH / 2)) * 16;
-  const unsigned char* const tr_base =
-      stage_l + (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
-      (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-
-  // One sub-tile: scores, masking, online softmax, P.C.
-  auto compute_unit = [&](int u) {
-    const int ti = t0 + wt + WT * (u >> 1);
-    const bool valid = (u < nu) && ti < t1;
-    const int tb = ti * kBlock + (u & 1) * kSub;
-
-    // Operands of this sub-tile, read from LDS before the first MFMA so that
-    // their latency overlaps: A of S^T (row-wise), and the C^T operands of
-    // P.C (transpose reads; K-slot e of lane group g in half h2 is token
-    // 16*h2 + 8*(e/4) + 4*g + e%4). With two row tiles the registers are
-    // short, and the C^T operands are read next to their MFMAs instead.
-    constexpr bool kEagerT = NT == 1;
-    auto read_t = [&](int h2, int dt) {
-      const i16x4 lo = lds_read_tr(tr_base + (16 * h2) * LP * 16 + dt * 64);
-      const i16x4 hi = lds_read_tr(tr_base + (16 * h2 + 8) * LP * 16 + dt * 64);
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8 aR[NR], aL[NL], aT[2][NDT];
-    if (has_rope) {
-#pragma unroll
-      for (int st = 0; st < NR; ++st)
-        aR[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ar_base + st * 16));
-    }
-#pragma unroll
-    for (int st = 0; st < NL; ++st)
-      aL[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(al_base + st * 16));
-    if constexpr (kEagerT) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) aT[h2][dt] = read_t(h2, dt);
-    }
-
-    // S^T[token][row] = C . Q^T
-    f32x16 sc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sc[nt] = f32x16{};
-    if (has_rope) {
-#pragma unroll
-      for (int st = 0; st < NR; ++st) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          bf16x8 qv;
-          if constexpr (QREG) qv = qRr[st];
-          else qv = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(qr_base + (nt * kSub * RP + st) * 16));
-          sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qv, sc[nt], 0, 0, 0);
-        }
-      }
-    }
-#pragma unroll
-    for (int st = 0; st < NL; ++st) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        bf16x8 qv;
-        if constexpr (QREG) qv = qLr[st];
-        else qv = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(ql_base + (nt * kSub * LP + st) * 16));
-        sc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qv, sc[nt], 0, 0, 0);
-      }
-    }
-
-    if constexpr (WD > 1) {
-      // Sum the WD partial score tiles (each wave holds a slice of the latent
-      // width; wave 0 also the RoPE part) in a fixed order so every wave gets
-      // identical scores.
-      const int grp = wt * NB + b;
-      f32x4* X = reinterpret_cast<f32x4*>(xchg);
-      lds_barrier();  // the previous sub-tile's reads of X are done
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          X[(((grp * WD + wd) * NT + nt) * 4 + q) * 64 + lane] =
-              f32x4{sc[nt][4 * q], sc[nt][4 * q + 1], sc[nt][4 * q + 2], sc[nt][4 * q + 3]};
-      lds_barrier();
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 t = X[(((grp * WD + 0) * NT + nt) * 4 + q) * 64 + lane];
-#pragma unroll
-          for (int w = 1; w < WD; ++w) t += X[(((grp * WD + w) * NT + nt) * 4 + q) * 64 + lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sc[nt][4 * q + e] = t[e];
-        }
-    }
-
-    // Mask tokens past a row's visible length (only when the sub-tile reaches
-    // past the shortest row, or holds no tile).
-    if (!(valid && tb + kSub <= min_vis)) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int lim = valid ? vis[nt] : 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = tb + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (tok >= lim) sc[nt][r] = -INFINITY;
-        }
-      }
-    }
-
-    // Online softmax per query row (row = lane column of the MFMA tile); the
-    // accumulator is rescaled only when some row's maximum grew.
-    bf16x8 pB[NT][2];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nt][r]);
-      mx = wave_max_halves(mx) * p.score_scale;
-      const bool grow = mx > m_run[nt];
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[nt] - mx) : 1.f;
-        m_run[nt] = grow ? mx : m_run[nt];
-        l_run[nt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[nt][dt] *= alpha;
-      }
-      const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
-      float sum = 0.f;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(sc[nt][8 * h2 + e], p.score_scale, -m_use));
-          sum += pe;
-          pB[nt][h2][e] = (__bf16)pe;
-        }
-      l_run[nt] += sum;
-    }
-
-    // O^T[d][row] += C^T[d][t] . P^T[t][row]
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8 at = kEagerT ? aT[h2][dt] : read_t(h2, dt);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pB[nt][h2], acc[nt][dt], 0, 0, 0);
-      }
-  };
-
-  // Software pipeline: PD sub-tiles in flight in registers. The wave stages
-  // the oldest into LDS, refills those registers with the sub-tile PD ahead,
-  // then computes it. The first sub-tile is staged before the wave waits for
-  // the other waves' query rows (when those are staged in LDS).
-  const int nsteps = (nu + PD - 1) / PD * PD;
-#pragma unroll
-  for (int i = 0; i < PD; ++i) load_unit(i, bl[i], br[i]);
-  if constexpr (!QREG) {
-#pragma unroll
-    for (int kq = 0; kq < QK; ++kq)
-      if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(q_base + qdst[kq]) = qv[kq];
-  }
-  for (int u0 = 0; u0 < nsteps; u0 += PD) {
-#pragma unroll
-    for (int i = 0; i < PD; ++i) {
-      const int u = u0 + i;
-      zero_tail(u, bl[i], br[i]);
-      stage_unit(bl[i], br[i]);
-      if (u + PD < nsteps) load_unit(u + PD, bl[i], br[i]);
-      if constexpr (!QREG) {
-        if (u == 0) lds_barrier();  // queries staged
-      }
-      compute_unit(u);
-    }
-  }
-
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) l_run[nt] = wave_sum_halves(l_run[nt]);
-
-  const int64_t slot = (int64_t)s * p.spl + k;
-  if constexpr (WT == 1) {
-    // Partial (output / l, lse) of this split for each (branch, row).
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int row = row0 + nt * 32 + n;
-      if (row >= p.rows) continue;
-      const float l = l_run[nt];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int64_t ri = (slot * NB + b) * p.rows + row;
-      float* o = p.part_o + ri * DC + wd * DCW;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
-              f32x4{acc[nt][dt][4 * q], acc[nt][dt][4 * q + 1], acc[nt][dt][4 * q + 2],
-                    acc[nt][dt][4 * q + 3]} * inv;
-      if (g == 0 && wd == 0)
-        p.part_lse[ri] = l > 0.f ? (m_run[nt] + __log2f(l)) * kLn2 : -INFINITY;
-    }
-  } else {
-    // Merge the WT token-split waves of each (branch, width slice): every wave
-    // publishes its record, then wave wt merges the d-tiles dt = wt, wt+WT, ...
-    constexpr int REC = NT * NDT * 4 + 1;  // float4 records per lane
-    // Record of wave (w, gi) starts at M + (w*NB*WD + gi) * RS float4s.
-    constexpr int RS = kSlotted ? SLOT_B / 16 : REC * 64;
-    if constexpr (!kSlotted) __syncthreads();  // all waves are done with the staged tiles
-    f32x4* M = reinterpret_cast<f32x4*>(smem);
-    const int gi = b * WD + wd;
-    {
-      f32x4* my = M + (wt * NB * WD + gi) * RS;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            my[((nt * NDT + dt) * 4 + q) * 64 + lane] =
-                f32x4{acc[nt][dt][4 * q], acc[nt][dt][4 * q + 1], acc[nt][dt][4 * q + 2],
-                      acc[nt][dt][4 * q + 3]};
-      my[(REC - 1) * 64 + lane] = f32x4{m_run[0], l_run[0], NT > 1 ? m_run[NT - 1] : 0.f,
-                                        NT > 1 ? l_run[NT - 1] : 0.f};
-    }
-    __syncthreads();
-    float ms[WT][NT], ls[WT][NT];
-#pragma unroll
-    for (int w = 0; w < WT; ++w) {
-      const f32x4 ml = M[(w * NB * WD + gi) * RS + (REC - 1) * 64 + lane];
-      ms[w][0] = ml[0];
-      ls[w][0] = ml[1];
-      if constexpr (NT > 1) {
-        ms[w][NT - 1] = ml[2];
-        ls[w][NT - 1] = ml[3];
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mm = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < WT; ++w) mm = fmaxf(mm, ms[w][nt]);
-      const float m_use = mm == -INFINITY ? 0.f : mm;
-      float wsc[WT];
-      float l = 0.f;
-#pragma unroll
-      for (int w = 0; w < WT; ++w) {
-        wsc[w] = __builtin_amdgcn_exp2f(ms[w][nt] - m_use);
-        l += ls[w][nt] * wsc[w];
-      }
-      const int row = row0 + nt * 32 + n;
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int64_t ri = (slot * NB + b) * p.rows + row;
-      if (row < p.rows) {
-        float* o = p.part_o + ri * DC + wd * DCW;
-        // float4 items (dt, q) of this row tile, spread over the WT waves
-#pragma unroll
-        for (int it = 0; it < NDT * 4; ++it) {
-          if (it % WT != wt) continue;
-          const int dt = it / 4, q = it % 4;
-          f32x4 v = f32x4{};
-#pragma unroll
-          for (int w = 0; w < WT; ++w)
-            v += M[(w * NB * WD + gi) * RS + ((nt * NDT + dt) * 4 + q) * 64 + lane] * wsc[w];
-          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
-        }
-        if (g == 0 && wd == 0 && wt == 0)
-          p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
-      }
-    }
-  }
-
-}
+// compile-time offset: latent rows get 2 spare 16-byte chunks, RoPE rows 1
+// (stage_lpitch, stage_rpitch). With 64 four-byte banks a 16-byte row read
+// serves 16 lanes per pass, and at these pitches 16 consecutive rows meet
+// each bank twice (a two-way conflict; the transpose reads likewise). An
+// unpadded layout with chunk swizzles free of conflicts (the prefill
+// kernel's) measured no faster here: the loader waves set the pace.
 
 // ---------------------------------------------------------------------------
-// bf16 split kernel for latent widths 64 and 128: loader and compute waves
+// bf16 split kernel: loader and compute waves
 // ---------------------------------------------------------------------------
 // A wave that issues loads while its CU's memory pipeline is full stalls in
 // issue, and a wave that waits for its own loads idles: both cost a wave that
@@ -646,28 +128,31 @@ mlra_split_mfma(SplitParams p) {
 // the shared RoPE key once), so the RoPE key is read once per token.
 //
 // A workgroup holds NBW branches (branch group grp: branches NBW*grp ...)
-// and RT 32-row tiles of query rows; a slot holds the NBW latents and the
-// RoPE key of one sub-tile, so every cache byte of the split is read once per
-// workgroup, whatever the number of query rows.
+// and RT 32-row tiles of query rows (the 512-wide latent: row group grp); a
+// slot holds the NBW latents and the RoPE key of one sub-tile, so every
+// cache byte of the split is read once per workgroup. Latents wider than 128
+// are split into WD slices of 128 columns, one compute wave each: a wave
+// scores its slice (and its share of the RoPE key), the WD partial scores
+// meet through LDS, and each wave accumulates P . C over its own columns.
 //
 // Slot hand-off uses two cumulative LDS counters per slot: ready (loader parts
-// written, 4 per use) and consumed (compute waves done, P = NBW * RT per use).
-// A loader refills slot j % NSLOT for sub-tile j only when the previous
-// occupant was consumed P times; a compute wave reads it once it is ready 4
-// times. Every wait is a bounded spin (it ends even if the protocol were
+// written, 4 per use) and consumed (compute waves done, NCW = NBW * RT * WD
+// per use). A loader refills slot j % NSLOT for sub-tile j only when the
+// previous occupant was consumed NCW times; a compute wave reads it once it
+// is ready 4 times. Every wait is a bounded spin (it ends even if the protocol were
 // broken, leaving wrong results rather than a hung GPU).
 //
-// Compute wave c takes the (branch, row tile) pair pi = c % P (branch
-// pi % NBW, row tile pi / NBW) and sub-tiles j = c / P + WT*i (WT = 4 / P);
-// per sub-tile it runs S^T = C . Q^T (MFMA, A = slot rows, B = query rows in
-// registers), the online softmax, and O^T += C^T . P^T (A = transpose reads
-// of the slot). With WT > 1 the token streams of a pair merge (m, l, O) at
-// the end without a workgroup barrier: every stream but the one holding the
-// split's last sub-tile leaves its state as a record in a dedicated LDS
-// area, counts it on an LDS counter and exits; that last stream waits for
-// them and merges the records with its own registers in a fixed stream
-// order (so the partial does not depend on which stream finished first) and
-// writes it.
+// Compute wave c takes slice c % WD of the (branch, row tile) pair
+// (c / WD) % NP (branch pair % NBW, row tile pair / NBW) and sub-tiles
+// j = c / NCW + WT*i (WT = 4 / NCW); per sub-tile it runs S^T = C . Q^T
+// (MFMA, A = slot rows, B = query rows in registers), the online softmax,
+// and O^T += C^T . P^T (A = transpose reads of the slot). With WT > 1 the
+// token streams of a triple merge (m, l, O) at the end without a workgroup
+// barrier: every stream but the one holding the split's last sub-tile leaves
+// its state as a record in a dedicated LDS area, counts it on an LDS counter
+// and exits; that last stream waits for them and merges the records with its
+// own registers in a fixed stream order (so the partial does not depend on
+// which stream finished first) and writes it.
 __device__ __forceinline__ void lds_wait_geq(const int* flag, int target) {
   // A few million polls (s_sleep 1 each) is far longer than any wait here.
   for (int it = 0; it < (1 << 22); ++it) {
@@ -682,19 +167,23 @@ __device__ __forceinline__ void lds_signal(int* flag) {
     __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <int NBW, int RT, int DC, int DR, int NSLOT, int PL>
+template <int NBW, int RT, int WD, int DC, int DR, int NSLOT, int PL>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mlra_split_pc(SplitParams p) {
-  constexpr int NP = NBW * RT;   // (branch, row tile) pairs, one compute wave each
-  constexpr int WT = 4 / NP;     // compute waves per pair (token streams)
-  constexpr int NL = DC / 16, NR = DR / 16, NDT = DC / 32;
+  constexpr int NP = NBW * RT;   // (branch, row tile) pairs
+  constexpr int NCW = NP * WD;   // compute waves per token stream
+  constexpr int WT = 4 / NCW;    // token streams
+  constexpr int DCW = DC / WD, DRW = DR / WD;  // a compute wave's slice of the dims
+  constexpr int NL = DCW / 16, NR = DRW / 16, NDT = DCW / 32;
+  constexpr int LCHW = DCW / 8, RCHW = DRW / 8;
   constexpr int LCH = DC / 8, RCH = DR / 8;
   constexpr int LQ = kSub * LCH / 64, RQ = kSub * RCH / 64;  // load instructions per sub-tile part
   constexpr int NLOAD = NBW * LQ + RQ;                       // per sub-tile
   constexpr int P = (NLOAD + 3) / 4;                         // per loader per sub-tile
-  constexpr int LP = mfma_lpitch(DC), RP = mfma_rpitch(DR);
-  constexpr PcLds lay = pc_lds(NBW, RT, DC, DR);
-  static_assert(NP == 1 || NP == 2 || NP == 4, "pairs");
+  constexpr int LP = stage_lpitch(DC), RP = stage_rpitch(DR);
+  constexpr PcLds lay = pc_lds(NBW, RT, WD, DC, DR);
+  static_assert(NCW == 1 || NCW == 2 || NCW == 4, "compute waves");
+  static_assert(NR >= 1 && RCHW >= 2, "RoPE slice of at least one k-step");
   static_assert(lay.nslot == NSLOT && NSLOT >= 2, "slot count");
   static_assert(lay.total <= 160 * 1024, "LDS");
   static_assert((PL - 1) * P <= 63, "outstanding loads fit the counter");
@@ -702,7 +191,8 @@ mlra_split_pc(SplitParams p) {
   int* const ready = reinterpret_cast<int*>(smem + lay.flags);
   int* const consumed = ready + NSLOT;
   int* const qdone = consumed + NSLOT;
-  int* const recorded = qdone + 1;  // [NP] merge records written, per pair
+  int* const recorded = qdone + 1;    // [4] merge records written, per compute wave of a stream
+  int* const exchanged = recorded + 4;  // [4] partial scores written, per compute wave
   int* const tabl = reinterpret_cast<int*>(smem + lay.table);
 
   const int lane = threadIdx.x & 63;
@@ -712,7 +202,7 @@ mlra_split_pc(SplitParams p) {
   if (p.nrt == 1) {
     k = blockIdx.x;
     s = blockIdx.y;
-  } else {  // two branch groups per split: ids 16c+i and 16c+8+i, dealt to one XCD together
+  } else {  // two groups per split: ids 16c+i and 16c+8+i, dealt to one XCD together
     const int id = blockIdx.x;
     const int pr = (id >> 4) * 8 + (id & 7);
     if (pr >= p.S * p.spl) return;
@@ -720,7 +210,11 @@ mlra_split_pc(SplitParams p) {
     s = pr / p.spl;
     k = pr % p.spl;
   }
-  const int bo = grp * NBW;  // first branch of this workgroup
+  // The groups of a split are row groups for the 512-wide latent (one
+  // branch, one row tile per workgroup), else branch groups (a workgroup
+  // holds every row).
+  const int bo = WD == 4 ? 0 : grp * NBW;     // first branch of this workgroup
+  const int rb0 = WD == 4 ? grp * kSub : 0;   // first query row of this workgroup
   const int NBT = RT == 1 ? NBW : p.NB;  // branches of the call (one group with one row tile)
   const int t0 = k * p.tps;
   // query and cache bases moved to the workgroup's first branch
@@ -765,10 +259,12 @@ mlra_split_pc(SplitParams p) {
   };
   f32x16 acc[NDT];
   float m_run = -INFINITY, l_run = 0.f;
-  const int pi = wave % NP;          // compute waves: (branch, row tile) pair
-  const int b = pi % NBW;            // its branch within the group
-  const int row0 = (pi / NBW) * kSub;  // its first query row
-  const int strm = (wave % 4) / NP;  // compute waves: token stream
+  const int cw = wave & 3;                // compute waves: index
+  const int wd = cw % WD;                 // latent slice
+  const int pi = (cw / WD) % NP;          // (branch, row tile) pair
+  const int b = pi % NBW;                 // its branch within the group
+  const int row0 = (pi / NBW) * kSub;     // its first query row in the workgroup
+  const int strm = cw / NCW;              // token stream
   // Each role synchronises once with the other (s_barrier counts waves)
   // inside its own branch, so no register of one role is live in the other.
   if (is_loader) {
@@ -784,7 +280,7 @@ mlra_split_pc(SplitParams p) {
     // ---------------- loader ----------------
     auto write = [&](int j, u32x4 (&d)[P]) {
       const int slot = j % NSLOT;
-      lds_wait_geq(consumed + slot, (j / NSLOT) * NP);  // previous occupant done
+      lds_wait_geq(consumed + slot, (j / NSLOT) * NCW);  // previous occupant done
       unsigned char* sb = smem + slot * lay.slot_bytes;
       const int tok0 = (t0 + (j >> 1)) * kBlock + (j & 1) * kSub;
 #pragma unroll
@@ -840,7 +336,7 @@ mlra_split_pc(SplitParams p) {
       const int rl = rem / LCH, cl = rem % LCH;
       const int xr = is_rope ? x - QL_CH : 0;
       const int rr = xr / RCH, cr = xr % RCH;
-      const int r = is_lat ? rl : rr;
+      const int r = rb0 + (is_lat ? rl : rr);
       const bool live = (is_lat || is_rope) && r < p.rows;
       const int rs = live ? r : 0;
       const int64_t head = ((int64_t)s * p.Q + rs / p.H) * p.H + rs % p.H;
@@ -858,11 +354,14 @@ mlra_split_pc(SplitParams p) {
 #pragma unroll
     for (int kq = 0; kq < QK; ++kq)
       if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(smem + qdst[kq]) = qv[kq];
-    if (threadIdx.x < 2 * NSLOT + 1 + NP) ready[threadIdx.x] = 0;  // every counter
+    if (threadIdx.x < 2 * NSLOT + 9) ready[threadIdx.x] = 0;  // every counter
     lds_barrier();
     // ---------------- compute ----------------
-    const unsigned char* const qb = smem + ((b * QR + row0 + n) * LP + g * (LCH / 2)) * 16;
-    const unsigned char* const qrb = smem + NBW * QR * LP * 16 + ((row0 + n) * RP + g * (RCH / 2)) * 16;
+    // this wave's slice of the query row (the k order of the score MFMAs:
+    // lane half g takes chunks g*LCHW/2 + st of the slice)
+    const unsigned char* const qb = smem + ((b * QR + row0 + n) * LP + wd * LCHW + g * (LCHW / 2)) * 16;
+    const unsigned char* const qrb =
+        smem + NBW * QR * LP * 16 + ((row0 + n) * RP + wd * RCHW + g * (RCHW / 2)) * 16;
     auto rd16 = [](const unsigned char* a) {
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
     };
@@ -874,14 +373,14 @@ mlra_split_pc(SplitParams p) {
     lds_signal(qdone);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
-    const int row = row0 + n;
+    const int row = rb0 + row0 + n;
     const int jr = row < p.rows ? row / p.H : 0;
     const int vis = p.causal ? L - (p.Q - 1 - jr) : L;
     const int min_vis = p.causal ? L - (p.Q - 1) : L;
-    const int a_l = (n * LP + g * (LCH / 2)) * 16 + b * LAT_B;  // S^T A operand, row n
-    const int a_r = (n * RP + g * (RCH / 2)) * 16 + NBW * LAT_B;
+    const int a_l = (n * LP + wd * LCHW + g * (LCHW / 2)) * 16 + b * LAT_B;  // S^T A operand, row n
+    const int a_r = (n * RP + wd * RCHW + g * (RCHW / 2)) * 16 + NBW * LAT_B;
     const int a_t = b * LAT_B + (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
-                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+                    (wd * DCW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     for (int j = strm; j < nsub; j += WT) {
       const int slot = j % NSLOT;
       lds_wait_geq(ready + slot, (j / NSLOT + 1) * 4);
@@ -925,6 +424,40 @@ mlra_split_pc(SplitParams p) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       lds_signal(consumed + slot);
       sc += sd;
+      if constexpr (WD > 1) {
+        // The WD waves of a (branch, row tile) pair hold partial scores over
+        // their slices: each leaves its part in the exchange area (double
+        // buffered by the stream's sub-tile parity), and all of them add the
+        // WD parts in slice order, so they hold bit-identical scores and take
+        // the same softmax decisions. A part is overwritten two sub-tiles
+        // later, after its readers have signalled the sub-tile in between.
+        const int u = j / WT;  // this stream's sub-tile count
+        f32x4* const X = reinterpret_cast<f32x4*>(smem + lay.xchg) + (u & 1) * 4 * 4 * 64;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          X[(cw * 4 + q) * 64 + lane] = f32x4{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
+        lds_signal(exchanged + cw);
+#pragma unroll
+        for (int w = 0; w < WD; ++w)
+          if (w != wd) lds_wait_geq(exchanged + cw - wd + w, u + 1);
+        f32x16 tot = f32x16{};
+#pragma unroll
+        for (int w = 0; w < WD; ++w) {
+          f32x16 part = sc;
+          if (w != wd) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 v = X[((cw - wd + w) * 4 + q) * 64 + lane];
+              part[4 * q] = v[0];
+              part[4 * q + 1] = v[1];
+              part[4 * q + 2] = v[2];
+              part[4 * q + 3] = v[3];
+            }
+          }
+          tot = w == 0 ? part : tot + part;
+        }
+        sc = tot;
+      }
       if (tb + kSub > min_vis) {  // uniform
         // element r holds token tb + 4g + 8(r/4) + r%4: compare the constant
         // part against a per-lane limit
@@ -973,23 +506,24 @@ mlra_split_pc(SplitParams p) {
   const int64_t slotp = (int64_t)s * p.spl + k;
   if constexpr (WT == 1) {
     if (wave >= 4) return;
-    const int row = row0 + n;
+    const int row = rb0 + row0 + n;
     if (row >= p.rows) return;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const int64_t ri = (slotp * NBT + bo + b) * p.rows + row;
-    float* o = p.part_o + ri * DC;
+    float* o = p.part_o + ri * DC + wd * DCW;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
             f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} * inv;
-    if (g == 0) p.part_lse[ri] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    if (g == 0 && wd == 0) p.part_lse[ri] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   } else {
-    // Merge the WT token streams of each pair (see above).
+    // Merge the WT token streams of each compute wave's triple (see above).
     constexpr int REC = NDT * 4 + 1;  // 64-lane f32x4 rows per record
     if (wave >= 4) return;
-    f32x4* const M = reinterpret_cast<f32x4*>(smem + lay.merge) + pi * (WT - 1) * REC * 64;
+    const int tri = cw % NCW;  // (branch, row tile, slice) within a stream
+    f32x4* const M = reinterpret_cast<f32x4*>(smem + lay.merge) + tri * (WT - 1) * REC * 64;
     // The stream holding the split's last sub-tile (it finishes last) merges;
     // stream mst + r (mod WT) writes record r - 1.
     const int mst = (nsub - 1) % WT;
@@ -1003,7 +537,7 @@ mlra_split_pc(SplitParams p) {
           my[(dt * 4 + q) * 64 + lane] =
               f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]};
       my[(REC - 1) * 64 + lane] = f32x4{m_run, l_run, 0.f, 0.f};
-      lds_signal(recorded + pi);
+      lds_signal(recorded + tri);
       return;
     }
     // Stream mst merges the others' records with its own registers in the
@@ -1011,7 +545,7 @@ mlra_split_pc(SplitParams p) {
     // result does not depend on which stream finished first). The others
     // took the sub-tiles before its last one, so this wait is short, and it
     // always ends.
-    lds_wait_geq(recorded + pi, WT - 1);
+    lds_wait_geq(recorded + tri, WT - 1);
     float ms[WT], ls[WT];
     ms[0] = m_run;
     ls[0] = l_run;
@@ -1032,11 +566,11 @@ mlra_split_pc(SplitParams p) {
       wsc[w] = __builtin_amdgcn_exp2f(ms[w] - m_use);
       l += ls[w] * wsc[w];
     }
-    const int row = row0 + n;
+    const int row = rb0 + row0 + n;
     if (row >= p.rows) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t ri = (slotp * NBT + bo + b) * p.rows + row;
-    float* o = p.part_o + ri * DC;
+    float* o = p.part_o + ri * DC + wd * DCW;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -1047,7 +581,7 @@ mlra_split_pc(SplitParams p) {
         for (int w = 1; w < WT; ++w) v += M[((w - 1) * REC + dt * 4 + q) * 64 + lane] * wsc[w];
         *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
       }
-    if (g == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
+    if (g == 0 && wd == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -1388,58 +922,13 @@ __global__ void __launch_bounds__(256) mlra_combine_cols(CombineParams c) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int NB, int DC, int DR, int NT>
-static hipError_t launch_mfma(const SplitParams& sp, const mlra_decode_plan& plan,
-                              hipStream_t stream) {
-  constexpr int WD = mfma_wd(DC);
-  constexpr int DCW = DC / WD;
-  constexpr int WT = mfma_wt(NB, DC, NT);
-  constexpr int WPS = mfma_waves_per_simd(NT, DC);
-  constexpr int PD = mfma_pd(NT, DC);
-  constexpr bool QREG = mfma_qreg(NT, DC);
-  auto kern = mlra_split_mfma<NB, DCW, WD, DR, NT, WT, WPS, PD, QREG>;
-  const int lds = mfma_lds_bytes(NB, DCW, WD, DR, NT, WT, QREG);
-  if (lds > 64 * 1024) {
-    static bool attr_set = false;  // per instance; the call is idempotent
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-  }
-  const dim3 grid = sp.nrt == 1
-                       ? dim3(plan.splits_per_seq, sp.S)
-                       : dim3((uint32_t)(((int64_t)sp.S * plan.splits_per_seq + 7) / 8 * 16));
-  hipLaunchKernelGGL(kern, grid, dim3(64 * NB * WD * WT), lds, stream, sp);
-  return hipGetLastError();
-}
-
-template <int NB, int DC, int NT>
-static hipError_t dispatch_dr(const SplitParams& sp, const mlra_decode_plan& plan,
-                              hipStream_t st) {
-  if (sp.DR == 64) return launch_mfma<NB, DC, 64, NT>(sp, plan, st);
-  return hipErrorInvalidValue;  // wide latents take the 64-wide RoPE key only
-}
-
-// The 8-wave width-split kernel serves the wide latents: the 512-wide single
-// latent (four 128-column slices) and 256-wide latents with one or two
-// branches (two slices).
-template <int NT>
-static hipError_t dispatch_nb(const SplitParams& sp, const mlra_decode_plan& plan,
-                              hipStream_t st) {
-  if (sp.NB == 1 && sp.DC == 512) return dispatch_dr<1, 512, NT>(sp, plan, st);
-  if (sp.NB == 1 && sp.DC == 256) return dispatch_dr<1, 256, NT>(sp, plan, st);
-  if (sp.NB == 2 && sp.DC == 256) return dispatch_dr<2, 256, NT>(sp, plan, st);
-  return hipErrorInvalidValue;
-}
-
 template <int NBW, int RT, int DC, int DR>
 static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
                             hipStream_t stream) {
-  constexpr PcLds lay = pc_lds(NBW, RT, DC, DR);
+  constexpr int WD = pc_wd(DC);
+  constexpr PcLds lay = pc_lds(NBW, RT, WD, DC, DR);
   constexpr int PL = pc_pl(NBW, DC, DR);
-  auto kern = mlra_split_pc<NBW, RT, DC, DR, lay.nslot, PL>;
+  auto kern = mlra_split_pc<NBW, RT, WD, DC, DR, lay.nslot, PL>;
   static bool attr_set = false;  // per instance; the call is idempotent
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1457,19 +946,32 @@ static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
 template <int NBW, int RT, int DC>
 static hipError_t pc_dr(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
   if (sp.DR == 64) return launch_pc<NBW, RT, DC, 64>(sp, plan, st);
-  return launch_pc<NBW, RT, DC, 32>(sp, plan, st);
+  if constexpr (DC <= 128) return launch_pc<NBW, RT, DC, 32>(sp, plan, st);
+  return hipErrorInvalidValue;  // wide latents take the 64-wide RoPE key only
 }
 
 template <int NBW, int RT>
 static hipError_t pc_dc(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
   if (sp.DC == 128) return pc_dr<NBW, RT, 128>(sp, plan, st);
-  return pc_dr<NBW, RT, 64>(sp, plan, st);
+  if (sp.DC == 64) return pc_dr<NBW, RT, 64>(sp, plan, st);
+  return hipErrorInvalidValue;
 }
 
-// (branches per workgroup, row tiles) as the planner chose them
+// (branches per workgroup, row tiles, latent width) as the planner chose them
 static hipError_t pc_nb(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
-  const int nbw = pc_nbw(sp.NB, sp.rows), rt = pc_rt(sp.rows);
-  if (sp.NB != nbw * sp.nrt) return hipErrorInvalidValue;
+  const int nbw = pc_nbw(sp.NB, sp.rows, sp.DC), rt = pc_rt(sp.rows, sp.DC);
+  if (sp.nrt != pc_groups(sp.NB, sp.rows, sp.DC)) return hipErrorInvalidValue;
+  if (sp.DC == 512) {  // one branch, four slices
+    if (nbw == 1 && rt == 1 && sp.DR == 64) return launch_pc<1, 1, 512, 64>(sp, plan, st);
+    return hipErrorInvalidValue;
+  }
+  if (sp.DC == 256) {  // two slices
+    if (sp.DR != 64) return hipErrorInvalidValue;
+    if (rt == 1 && nbw == 1) return launch_pc<1, 1, 256, 64>(sp, plan, st);
+    if (rt == 1 && nbw == 2) return launch_pc<2, 1, 256, 64>(sp, plan, st);
+    if (rt == 2 && nbw == 1) return launch_pc<1, 2, 256, 64>(sp, plan, st);
+    return hipErrorInvalidValue;
+  }
   if (rt == 1) {
     switch (nbw) {
       case 1: return pc_dc<1, 1>(sp, plan, st);
@@ -1488,7 +990,6 @@ static hipError_t pc_nb(const SplitParams& sp, const mlra_decode_plan& plan, hip
 static hipError_t launch_split(const SplitParams& sp, const KernelShape& ks,
                                const mlra_decode_plan& plan, hipStream_t st) {
   if (ks.variant == kVariantPcBf16) return pc_nb(sp, plan, st);
-  if (ks.variant == kVariantMfmaBf16) return dispatch_nb<1>(sp, plan, st);
   dim3 grid(plan.splits_per_seq, sp.S, (sp.rows * sp.NB + 3) / 4);
   switch (sp.DC / 64) {
     case 1: hipLaunchKernelGGL(mlra_split_valu<1>, grid, dim3(256), 0, st, sp); break;

@@ -71,37 +71,33 @@ def test_plan_covers_every_tile(lib, cfg):
     max_tiles = -(-d.max_seq_len // 64)
     assert p.splits_per_seq * p.tiles_per_split >= max_tiles
     assert (p.splits_per_seq - 1) * p.tiles_per_split < max(max_tiles, 1)
-    if cfg.dtype == "bf16" and cfg.d_latent >= 256:  # token-split waves get equal tile counts
-        wt = p.waves_per_group // (cfg.n_branch * (cfg.d_latent // 128))
-        assert p.tiles_per_split % wt == 0
-    if cfg.dtype == "bf16" and cfg.d_latent <= 128:  # block ids of a split fit the LDS table
+    if cfg.dtype == "bf16":  # block ids of a split fit the LDS table
         assert p.tiles_per_split <= 1024
     rows = cfg.num_heads * cfg.q_len
     slots = cfg.num_seqs * p.splits_per_seq * cfg.n_branch * rows
     assert p.workspace_bytes >= slots * (cfg.d_latent + 1) * 4
-    # 1: fp32 vector ALU; 2: bf16, 256/512-wide latent (width-split waves);
-    # 4: bf16, latent 64/128 (loader and compute waves)
-    expect = 1 if cfg.dtype != "bf16" else (2 if cfg.d_latent >= 256 else 4)
+    # 1: fp32 vector ALU; 4: bf16 (loader and compute waves)
+    expect = 1 if cfg.dtype != "bf16" else 4
     assert p.kernel_variant == expect
     assert p.lds_bytes <= 160 * 1024
 
 
-@pytest.mark.parametrize("nb,dc,h,q", [(1, 128, 32, 1), (1, 128, 24, 2), (2, 64, 32, 2),
-                                     (4, 128, 16, 1), (4, 128, 32, 1), (4, 128, 17, 2),
-                                     (4, 64, 32, 2), (1, 512, 32, 2), (2, 256, 24, 2)])
-def test_workgroups_per_split(lib, nb, dc, h, q):
-    # latent 64/128: a workgroup holds every row (up to 64) of at most two
-    # branches when there are more than 32 rows, so only four branches at
-    # 33-64 rows take two workgroups per split (branch groups); the 256/512
-    # width-split kernel takes one workgroup per 32 rows
+# (branches, latent, heads, q_len) -> workgroups per split. A workgroup's
+# four compute waves take (branch, 32-row tile, 128-column slice) triples:
+# with up to 32 rows one workgroup holds every branch; with 33-64 rows it
+# holds both row tiles of as many branches as fit (two of width <= 128, one
+# of 256), and the 512-wide latent (four slices) takes one row tile each.
+@pytest.mark.parametrize("nb,dc,h,q,groups", [
+    (1, 128, 32, 1, 1), (1, 128, 24, 2, 1), (2, 64, 32, 2, 1), (4, 128, 16, 1, 1),
+    (4, 128, 32, 1, 1), (4, 128, 17, 2, 2), (4, 64, 32, 2, 2), (1, 256, 32, 1, 1),
+    (1, 256, 32, 2, 1), (2, 256, 16, 1, 1), (2, 256, 24, 2, 2), (1, 512, 32, 1, 1),
+    (1, 512, 32, 2, 2)])
+def test_workgroups_per_split(lib, nb, dc, h, q, groups):
     cfg = configs.MLRA4_FUSED.with_(n_branch=nb, d_latent=dc, num_heads=h, q_len=q)
     st, p = _plan(lib, _dims(cfg), nb)
-    rows = h * q
     assert st == 0
-    if dc <= 128:
-        assert p.row_groups == (2 if nb == 4 and rows > 32 else 1)
-    else:
-        assert p.row_groups == (2 if rows > 32 else 1)
+    assert p.row_groups == groups
+    assert p.kernel_variant == 4 and p.waves_per_group == 8
     assert p.lds_bytes <= 160 * 1024
 
 

@@ -79,7 +79,7 @@ for nb in (1, 2, 4):
             for h, q in ((16, 1), (24, 2)):
                 SHAPES.append((nb, dc, dr, h, q))
 SHAPES += [(1, 512, 64, 32, 1), (1, 512, 64, 32, 2)]
-SHAPES += [(1, 256, 64, 32, 1), (2, 256, 64, 16, 1), (2, 256, 64, 24, 2)]
+SHAPES += [(1, 256, 64, 32, 1), (1, 256, 64, 24, 2), (2, 256, 64, 16, 1), (2, 256, 64, 24, 2)]
 
 
 @pytest.mark.parametrize("nb,dc,dr,h,q", SHAPES)
