@@ -44,7 +44,9 @@ def _replay_matches(graph, out, lse, ref_out, ref_lse, times=4):
 
 
 @pytest.mark.parametrize("cfg", [configs.MLRA4_TP_SHARE.with_(name="g_share", num_seqs=4, context=3000),
-                                 configs.MLRA4_FUSED.with_(name="g_fused", num_seqs=2, context=2500)],
+                                 configs.MLRA4_FUSED.with_(name="g_fused", num_seqs=2, context=2500),
+                                 configs.MLRA2_FUSED.with_(name="g_mlra2", num_seqs=2, context=2000),
+                                 configs.MLA_COMPARE.with_(name="g_mla", num_seqs=2, context=1800)],
                          ids=lambda c: c.name)
 def test_decode_graph_replays_match_eager(cfg):
     inp = make_inputs(cfg)

@@ -182,10 +182,13 @@ def test_split_count_invariance(nb, dc, q):
         assert_parity(out, lse, ro, rl)
 
 
-def test_block_relabelling_and_determinism_are_bitwise():
-    cfg = _cfg(num_seqs=4, context_range=(100, 2000), seed=77)
+@pytest.mark.parametrize("nb,dc,q", [(4, 128, 1), (2, 256, 1), (1, 512, 2)])
+def test_block_relabelling_and_determinism_are_bitwise(nb, dc, q):
+    # 256/512-wide latents also sum their slices' partial scores through LDS
+    cfg = _cfg(num_seqs=4, context_range=(100, 2000), seed=77, n_branch=nb, d_latent=dc, q_len=q,
+               scale=1 / np.sqrt(dc + 64))
     inp = make_inputs(cfg)
-    _say("determinism")
+    _say(f"determinism nb={nb} dc={dc} q={q}")
     a = run_gpu(inp)
     b = run_gpu(inp)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
