@@ -321,3 +321,35 @@ def test_two_phase_and_prepared_calls_match_the_single_call_bitwise():
         assert torch.equal(o, o1) and torch.equal(l, l1)
     assert_parity(o1.float().cpu().numpy().astype(np.float64),
                   l1.cpu().numpy().astype(np.float64), *oracle(inp))
+
+
+def _random_case(rng, i):
+    """One seeded random decode case over the supported shape space: branches
+    and latent width (with their RoPE widths), heads and query tokens up to 64
+    rows, ragged lengths including empty and single-token sequences, causal or
+    not, and an explicit split count or the planner's."""
+    nb, dc, dr = [(1, 64, 32), (1, 128, 64), (2, 64, 64), (2, 128, 32), (4, 64, 32),
+                  (4, 128, 64), (1, 256, 64), (2, 256, 64), (1, 512, 64)][rng.integers(9)]
+    q = int(rng.integers(1, 3))
+    h = int(rng.integers(1, 64 // q + 1))
+    s = int(rng.integers(1, 6))
+    hi = int(rng.integers(1, 1500))
+    cfg = _cfg(name=f"rand{i}", n_branch=nb, d_latent=dc, d_rope=dr, num_heads=h, q_len=q,
+               num_seqs=s, context_range=(1, hi), causal=bool(rng.integers(2)),
+               seed=1000 + i, scale=1 / np.sqrt(dc + dr), out_rescale=float(rng.uniform(0.3, 1.0)))
+    inp = make_inputs(cfg)
+    if s > 1 and rng.integers(3) == 0:
+        inp.seq_lens[int(rng.integers(s))] = 0  # an empty sequence
+    splits = int(rng.choice([0, 0, 1, 3, 17]))
+    return inp, splits
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes_match_the_oracle(i):
+    inp, splits = _random_case(np.random.default_rng(4242 + i), i)
+    c = inp.cfg
+    reduce = "concat" if i % 3 == 0 else "sum"
+    _say(f"random {i}: nb={c.n_branch} dc={c.d_latent} dr={c.d_rope} h={c.num_heads} q={c.q_len} "
+         f"causal={c.causal} {reduce} splits={splits} lens={inp.seq_lens.tolist()}")
+    out, lse = run_gpu(inp, reduce, num_splits=splits)
+    assert_parity(out, lse, *oracle(inp, reduce))
