@@ -253,3 +253,32 @@ def test_long_context_splits_past_the_staged_block_ids():
     js = [0, 1, 1023, 2047]
     ro, rl = oracle_tokens(inp, 0, js, "sum")
     assert_parity(out[0, js], lse[0, js], ro, rl)
+
+
+def _random_case(rng, i):
+    """One seeded random prefill case: branches, latent and RoPE widths, chunk
+    length and heads (row counts that do and do not fill 256-row groups),
+    ragged cached contexts behind the chunk, causal or not, and an explicit
+    split count or the planner's."""
+    nb = int(rng.choice([1, 2, 4]))
+    dc = int(rng.choice([64, 128]))
+    dr = int(rng.choice([32, 64]))
+    q = int(rng.integers(1, 97))
+    h = int(rng.integers(1, 25))
+    s = int(rng.integers(1, 4))
+    extra = int(rng.integers(0, 1001))
+    cfg = _cfg(name=f"prand{i}", n_branch=nb, d_latent=dc, d_rope=dr, q_len=q, num_heads=h,
+               num_seqs=s, context_range=(q, q + extra), causal=bool(rng.integers(4) > 0),
+               seed=2000 + i, scale=1 / np.sqrt(dc + dr), out_rescale=float(rng.uniform(0.3, 1.0)))
+    return make_inputs(cfg), int(rng.choice([0, 0, 1, 2, 5]))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shapes_match_the_oracle(i):
+    inp, splits = _random_case(np.random.default_rng(5151 + i), i)
+    c = inp.cfg
+    reduce = "concat" if i % 3 == 0 else "sum"
+    _say(f"prefill random {i}: nb={c.n_branch} dc={c.d_latent} dr={c.d_rope} q={c.q_len} "
+         f"h={c.num_heads} causal={c.causal} {reduce} splits={splits} lens={inp.seq_lens.tolist()}")
+    out, lse = run_prefill(inp, reduce, num_splits=splits)
+    assert_parity(out, lse, *oracle(inp, reduce))
