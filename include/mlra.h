@@ -85,7 +85,7 @@ typedef struct mlra_decode_dims {
   int32_t causal;              /* nonzero: query j sees t < L - (Q - 1 - j) */
   int32_t num_splits;          /* 0: library plans split-K; >0: at most this many splits per
                                 * sequence, raised where a split would exceed 1024 tiles
-                                * (65536 tokens) for latent widths 64 and 128 */
+                                * (65536 tokens) for bfloat16 */
   int32_t dtype;               /* mlra_dtype */
   int32_t reduce;              /* mlra_branch_reduce */
   int32_t reserved;            /* must be 0 */
