@@ -71,8 +71,11 @@ typedef enum mlra_branch_reduce {
  * dense default. The innermost (feature) dimension is always contiguous. */
 typedef struct mlra_decode_dims {
   int32_t num_seqs;            /* S  >= 1 */
-  int32_t q_len;               /* Q  in {1, 2}: new query tokens per sequence */
-  int32_t num_heads;           /* H  >= 1, H * Q <= 64 */
+  int32_t q_len;               /* Q  in {1, 2}: new query tokens per sequence (decode;
+                                * longer chunks, e.g. several draft tokens to verify, go
+                                * to mlra_prefill_attention, which computes the same
+                                * out and lse for any Q) */
+  int32_t num_heads;           /* H  >= 1, H * Q <= 64 (decode) */
   int32_t d_latent;            /* DC per branch: fp32 {64, 128, 256, 512}; bf16 {64, 128} with
                                   any n_branch, 256 with n_branch <= 2 and DR = 64 (MLRA-2:
                                   MLA's 512-wide latent in two branches), 512 with n_branch = 1

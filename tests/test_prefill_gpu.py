@@ -282,3 +282,26 @@ def test_random_shapes_match_the_oracle(i):
          f"h={c.num_heads} causal={c.causal} {reduce} splits={splits} lens={inp.seq_lens.tolist()}")
     out, lse = run_prefill(inp, reduce, num_splits=splits)
     assert_parity(out, lse, *oracle(inp, reduce))
+
+
+@pytest.mark.parametrize("q,h,nb", [(1, 32, 4), (2, 32, 1), (2, 16, 2)])
+def test_prefill_and_decode_calls_agree_on_short_chunks(q, h, nb):
+    # the two entry points compute the same function: on chunks the decode
+    # call accepts, their outputs agree to rounding (different kernels and
+    # split orders)
+    cfg = _cfg(q_len=q, num_heads=h, n_branch=nb, num_seqs=3, context_range=(q, 1500),
+               seed=300 + 10 * q + nb)
+    inp = make_inputs(cfg)
+    d = to_device(inp)
+    _say(f"prefill vs decode q={q} h={h} nb={nb} lens={inp.seq_lens.tolist()}")
+    po, pl = run_prefill(inp, "concat", dev=d)
+    do, dl = api.mlra_decode_attention(d["q_latent"], d["q_rope"], d["latent_cache"],
+                                       d["rope_cache"], d["block_table"], d["seq_lens"], nb,
+                                       cfg.scale, cfg.out_rescale, max_seq_len=inp.max_seq_len,
+                                       reduce="concat")
+    torch.cuda.synchronize()
+    do = do.float().cpu().numpy().astype(np.float64)
+    dl = dl.cpu().numpy().astype(np.float64)
+    assert np.abs(po - do).max() <= 2e-2
+    assert np.linalg.norm(po - do) / np.linalg.norm(do) <= 1e-2
+    assert np.abs(pl - dl).max() <= 1e-3
