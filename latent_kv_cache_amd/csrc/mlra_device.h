@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mlra {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -16,6 +18,42 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Host side. A kernel that takes more than 64 KB of dynamic LDS must be
+// allowed it on every device it runs on: set the limit on the current device
+// the first time (bit d of `done` records device d; devices past 63 set it on
+// every call). Safe from several threads: the call is idempotent.
+inline hipError_t allow_dynamic_lds(const void* kern, int bytes,
+                                    std::atomic<unsigned long long>& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  const unsigned long long bit = (dev >= 0 && dev < 64) ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
+// Host side: the current device's compute-unit count, cached per device.
+inline int device_cu_count(int* out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return 0;
+    }
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return -1;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  *out = cus;
+  return 0;
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }

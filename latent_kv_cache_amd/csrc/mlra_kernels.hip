@@ -929,13 +929,9 @@ static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
   constexpr PcLds lay = pc_lds(NBW, RT, WD, DC, DR);
   constexpr int PL = pc_pl(NBW, DC, DR);
   auto kern = mlra_split_pc<NBW, RT, WD, DC, DR, lay.nslot, PL>;
-  static bool attr_set = false;  // per instance; the call is idempotent
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<unsigned long long> lds_allowed{0};  // per instance, per device
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lay.total, lds_allowed);
+  if (e != hipSuccess) return e;
   const dim3 grid = sp.nrt == 1
                        ? dim3(plan.splits_per_seq, sp.S)
                        : dim3((uint32_t)(((int64_t)sp.S * plan.splits_per_seq + 7) / 8 * 16));
@@ -1023,22 +1019,7 @@ static void launch_combine(bool bf16, dim3 grid, const CombineParams& cp, hipStr
     launch_combine_kb<VPL, (kMax < 32 ? kMax : 32)>(bf16, grid, cp, st);
 }
 
-static int device_cus(int* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  static int cache[64] = {0};
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *out = cache[dev];
-    return 0;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    return -1;
-  if (dev >= 0 && dev < 64) cache[dev] = cus;
-  *out = cus;
-  return 0;
-}
+static int device_cus(int* out) { return device_cu_count(out); }
 
 
 // Which kernels one call enqueues: the split kernel (partial results of

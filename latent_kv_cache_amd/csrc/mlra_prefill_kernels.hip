@@ -558,22 +558,7 @@ __global__ void __launch_bounds__(256) mlra_prefill_merge(MergeParams p) {
 
 int64_t pf_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int pf_device_cus(int* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  static int cache[64] = {0};
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *out = cache[dev];
-    return 0;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    return -1;
-  if (dev >= 0 && dev < 64) cache[dev] = cus;
-  *out = cus;
-  return 0;
-}
+int pf_device_cus(int* out) { return device_cu_count(out); }
 
 // Validation: the decode rules for everything but the query count (checked
 // with one query row), then the prefill kernel's own limits.
@@ -642,10 +627,9 @@ mlra_status prefill_plan(const Resolved& r, int32_t num_cus, int32_t num_splits,
 template <int DC, int DR>
 hipError_t launch_prefill(const PrefillParams& pp, int64_t groups, hipStream_t st) {
   constexpr uint32_t lds = PfLayout<DC, DR>::TOTAL;
-  // more than 64 KB of dynamic LDS must be allowed once per kernel instance
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&mlra_prefill<DC, DR, kPfNT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<unsigned long long> lds_allowed{0};  // per instance, per device
+  const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void*>(&mlra_prefill<DC, DR, kPfNT>),
+                                            (int)lds, lds_allowed);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((mlra_prefill<DC, DR, kPfNT>), dim3((uint32_t)groups), dim3(64 * (8 / kPfNT)), lds,
                      st, pp);

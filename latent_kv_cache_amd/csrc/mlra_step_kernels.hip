@@ -268,14 +268,10 @@ static int outproj_sb(int M, int K, int KC) {
 }
 template <int MT>
 static hipError_t outproj_launch(dim3 grid, const OutProjParams& p, hipStream_t st) {
-  static bool attr_set = false;  // per instance; the call is idempotent
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mlra_outproj<MT>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             kOpXBytes + 16 * kOpMaxM);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<unsigned long long> lds_allowed{0};  // per device
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(mlra_outproj<MT>),
+                                         kOpXBytes + 16 * kOpMaxM, lds_allowed);
+  if (e != hipSuccess) return e;
   const size_t lds = (size_t)MT * 16 * (p.SB * 128 + 16);
   hipLaunchKernelGGL(mlra_outproj<MT>, grid, dim3(512), lds, st, p);
   return hipGetLastError();
