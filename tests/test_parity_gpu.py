@@ -226,16 +226,17 @@ def test_fused_equals_sum_of_single_branch_shares(q):
     assert np.linalg.norm(acc - fused) / np.linalg.norm(fused) <= 1e-2
 
 
-@pytest.mark.parametrize("q", [1, 2])
-def test_branch_major_cache_strides(q):
-    cfg = _cfg(num_seqs=2, context_range=(64, 900), seed=13, q_len=q)
+@pytest.mark.parametrize("q,nb,dc", [(1, 4, 128), (2, 4, 128), (1, 2, 256), (2, 2, 256)])
+def test_branch_major_cache_strides(q, nb, dc):
+    cfg = _cfg(num_seqs=2, context_range=(64, 900), seed=13, q_len=q, n_branch=nb, d_latent=dc,
+               scale=1 / np.sqrt(dc + 64))
     inp = make_inputs(cfg)
     d = to_device(inp)
     # same values stored branch-major [blocks][NB][64][DC], viewed as [blocks][64][NB][DC]
     bm = d["latent_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     assert bm.stride(2) == 64 * cfg.d_latent
     d["latent_cache"] = bm
-    _say(f"branch-major strides q={q}")
+    _say(f"branch-major strides q={q} nb={nb} dc={dc}")
     out, lse = run_gpu(inp, dev=d)
     assert_parity(out, lse, *oracle(inp))
 
