@@ -27,8 +27,8 @@ mlra_status resolve_dims(const mlra_decode_dims* d, int32_t n_branch, Resolved* 
   if (d->reserved != 0) return MLRA_ERR_BAD_DIMS;
   if (d->num_seqs < 1 || d->num_heads < 1 || d->q_len < 1) return MLRA_ERR_BAD_DIMS;
   if (d->num_seqs > kMaxSeqs) return MLRA_ERR_UNSUPPORTED;  // grid y dimension
-  if (d->q_len > 2) return MLRA_ERR_UNSUPPORTED;
-  if (d->num_heads * d->q_len > 64) return MLRA_ERR_UNSUPPORTED;
+  if (d->q_len > 4) return MLRA_ERR_UNSUPPORTED;
+  if (d->num_heads * d->q_len > 128) return MLRA_ERR_UNSUPPORTED;
   if (n_branch < 1) return MLRA_ERR_BAD_DIMS;
   if (!pow2_in(n_branch, {1, 2, 4})) return MLRA_ERR_UNSUPPORTED;
   if (d->d_latent < 1 || d->d_rope < 1) return MLRA_ERR_BAD_DIMS;

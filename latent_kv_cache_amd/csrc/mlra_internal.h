@@ -28,18 +28,26 @@ enum Variant : int32_t {
 constexpr int kPcMaxTiles = 1024;
 // Shape of a workgroup. Each of the four compute waves takes one (branch,
 // 32-row tile, latent slice) triple: WD waves split a latent wider than 128
-// into 128-column slices (WD = DC/128), a workgroup holds RT 32-row tiles of
-// query rows (2 when there are more than 32 rows and the slices leave room,
-// else 1) and NBW of the NB branches (as many as the remaining waves allow).
-// The rest goes to more workgroups per split: branch groups, and, for the
-// 512-wide latent with 64 rows, row groups.
+// into 128-column slices (WD = DC/128); a workgroup holds RT 32-row tiles of
+// query rows (the power of two covering the call's row tiles, as far as the
+// slices leave waves) and NBW of the NB branches (as many as the remaining
+// waves allow). The rest goes to more workgroups per split: branch groups
+// (NB / NBW) times row groups (the row tiles RT does not cover), at most 4.
 constexpr int pc_wd(int DC) { return DC > 128 ? DC / 128 : 1; }
-constexpr int pc_rt(int rows, int DC) { return rows > 32 && pc_wd(DC) <= 2 ? 2 : 1; }
+constexpr int pc_row_tiles(int rows) { return (rows + 31) / 32; }
+constexpr int pc_rt(int rows, int DC) {
+  return (pc_row_tiles(rows) <= 1 ? 1 : (pc_row_tiles(rows) <= 2 ? 2 : 4)) < 4 / pc_wd(DC)
+             ? (pc_row_tiles(rows) <= 1 ? 1 : (pc_row_tiles(rows) <= 2 ? 2 : 4))
+             : 4 / pc_wd(DC);
+}
 constexpr int pc_nbw(int NB, int rows, int DC) {
   return NB < 4 / (pc_rt(rows, DC) * pc_wd(DC)) ? NB : 4 / (pc_rt(rows, DC) * pc_wd(DC));
 }
+constexpr int pc_row_groups(int rows, int DC) {
+  return (pc_row_tiles(rows) + pc_rt(rows, DC) - 1) / pc_rt(rows, DC);
+}
 constexpr int pc_groups(int NB, int rows, int DC) {
-  return (NB / pc_nbw(NB, rows, DC)) * ((rows > 32 ? 2 : 1) / pc_rt(rows, DC));
+  return (NB / pc_nbw(NB, rows, DC)) * pc_row_groups(rows, DC);
 }
 // LDS layout (byte offsets): ring [nslot][slot_bytes] at 0 (a slot holds the
 // NBW latents and the RoPE key of 32 tokens; the staged query rows, RT
@@ -96,7 +104,7 @@ struct Resolved {
 // Shape of the split-kernel workgroup.
 struct KernelShape {
   int32_t variant;
-  int32_t NRT;      // workgroups per split (branch or row groups; 1 or 2)
+  int32_t NRT;      // workgroups per split (branch groups x row groups; 1 to 4)
   int32_t waves;    // waves per workgroup
   int32_t groups_per_cu;  // resident workgroups per CU the planner aims for
 };

@@ -198,23 +198,24 @@ mlra_split_pc(SplitParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
-  int k, s, grp = 0;
+  int k, s, bo = 0, rb0 = 0;  // bo, rb0: first branch and first query row of this workgroup
   if (p.nrt == 1) {
     k = blockIdx.x;
     s = blockIdx.y;
-  } else {  // two groups per split: ids 16c+i and 16c+8+i, dealt to one XCD together
+  } else {
+    // G groups per split: ids 8G*c + 8g + i (g < G) are dealt to one XCD
+    // together. Group g = row group * (NB / NBW) + branch group.
+    const int G = p.nrt;
     const int id = blockIdx.x;
-    const int pr = (id >> 4) * 8 + (id & 7);
+    const int pr = (id / (8 * G)) * 8 + (id & 7);
     if (pr >= p.S * p.spl) return;
-    grp = (id >> 3) & 1;
+    const int grp = (id >> 3) % G;
+    const int nbg = p.NB / NBW;
+    bo = (grp % nbg) * NBW;
+    rb0 = (grp / nbg) * RT * kSub;
     s = pr / p.spl;
     k = pr % p.spl;
   }
-  // The groups of a split are row groups for the 512-wide latent (one
-  // branch, one row tile per workgroup), else branch groups (a workgroup
-  // holds every row).
-  const int bo = WD == 4 ? 0 : grp * NBW;     // first branch of this workgroup
-  const int rb0 = WD == 4 ? grp * kSub : 0;   // first query row of this workgroup
   const int NBT = RT == 1 ? NBW : p.NB;  // branches of the call (one group with one row tile)
   const int t0 = k * p.tps;
   // query and cache bases moved to the workgroup's first branch
@@ -934,7 +935,7 @@ static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
   if (e != hipSuccess) return e;
   const dim3 grid = sp.nrt == 1
                        ? dim3(plan.splits_per_seq, sp.S)
-                       : dim3((uint32_t)(((int64_t)sp.S * plan.splits_per_seq + 7) / 8 * 16));
+                       : dim3((uint32_t)(((int64_t)sp.S * plan.splits_per_seq + 7) / 8 * 8 * sp.nrt));
   hipLaunchKernelGGL(kern, grid, dim3(512), lay.total, stream, sp);
   return hipGetLastError();
 }
@@ -974,11 +975,13 @@ static hipError_t pc_nb(const SplitParams& sp, const mlra_decode_plan& plan, hip
       case 2: return pc_dc<2, 1>(sp, plan, st);
       case 4: return pc_dc<4, 1>(sp, plan, st);
     }
-  } else {
+  } else if (rt == 2) {
     switch (nbw) {
       case 1: return pc_dc<1, 2>(sp, plan, st);
       case 2: return pc_dc<2, 2>(sp, plan, st);
     }
+  } else if (rt == 4 && nbw == 1) {
+    return pc_dc<1, 4>(sp, plan, st);
   }
   return hipErrorInvalidValue;
 }

@@ -84,14 +84,17 @@ def test_plan_covers_every_tile(lib, cfg):
 
 # (branches, latent, heads, q_len) -> workgroups per split. A workgroup's
 # four compute waves take (branch, 32-row tile, 128-column slice) triples:
-# with up to 32 rows one workgroup holds every branch; with 33-64 rows it
-# holds both row tiles of as many branches as fit (two of width <= 128, one
-# of 256), and the 512-wide latent (four slices) takes one row tile each.
+# with up to 32 rows one workgroup holds every branch; with more it holds
+# the power of two of row tiles that covers them (as far as the slices leave
+# waves) for as many branches as fit, and further branches and row tiles
+# take more workgroups (branch groups x row groups, at most 4).
 @pytest.mark.parametrize("nb,dc,h,q,groups", [
     (1, 128, 32, 1, 1), (1, 128, 24, 2, 1), (2, 64, 32, 2, 1), (4, 128, 16, 1, 1),
     (4, 128, 32, 1, 1), (4, 128, 17, 2, 2), (4, 64, 32, 2, 2), (1, 256, 32, 1, 1),
     (1, 256, 32, 2, 1), (2, 256, 16, 1, 1), (2, 256, 24, 2, 2), (1, 512, 32, 1, 1),
-    (1, 512, 32, 2, 2)])
+    (1, 512, 32, 2, 2), (1, 128, 32, 4, 1), (1, 64, 24, 4, 1), (2, 128, 32, 3, 2),
+    (4, 128, 32, 4, 4), (4, 64, 20, 4, 4), (1, 256, 32, 4, 2), (2, 256, 32, 4, 4),
+    (1, 512, 24, 4, 3), (1, 512, 32, 4, 4)])
 def test_workgroups_per_split(lib, nb, dc, h, q, groups):
     cfg = configs.MLRA4_FUSED.with_(n_branch=nb, d_latent=dc, num_heads=h, q_len=q)
     st, p = _plan(lib, _dims(cfg), nb)
@@ -121,7 +124,7 @@ def test_ragged_hint_balances_splits(lib):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("num_seqs", 0, 2), ("q_len", 3, 3), ("num_heads", 33, 3), ("d_latent", 96, 3),
+    ("num_seqs", 0, 2), ("q_len", 5, 3), ("num_heads", 65, 3), ("d_latent", 96, 3),
     ("d_rope", 48, 3), ("block_size", 32, 3), ("block_size", 0, 2), ("max_blocks_per_seq", 0, 2),
     ("max_seq_len", 10 ** 6, 2), ("max_seq_len", -1, 2), ("num_splits", -2, 2), ("dtype", 7, 2),
     ("reduce", 2, 2), ("reserved", 1, 2), ("latent_stride_block", 1000, 2),

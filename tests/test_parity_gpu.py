@@ -76,10 +76,11 @@ SHAPES = []
 for nb in (1, 2, 4):
     for dc in (64, 128):
         for dr in (32, 64):
-            for h, q in ((16, 1), (24, 2)):
+            for h, q in ((16, 1), (24, 2), (24, 4)):
                 SHAPES.append((nb, dc, dr, h, q))
-SHAPES += [(1, 512, 64, 32, 1), (1, 512, 64, 32, 2)]
-SHAPES += [(1, 256, 64, 32, 1), (1, 256, 64, 24, 2), (2, 256, 64, 16, 1), (2, 256, 64, 24, 2)]
+SHAPES += [(1, 512, 64, 32, 1), (1, 512, 64, 32, 2), (1, 512, 64, 24, 4), (1, 512, 64, 32, 4)]
+SHAPES += [(1, 256, 64, 32, 1), (1, 256, 64, 24, 2), (2, 256, 64, 16, 1), (2, 256, 64, 24, 2),
+           (1, 256, 64, 32, 4), (2, 256, 64, 32, 3)]
 
 
 @pytest.mark.parametrize("nb,dc,dr,h,q", SHAPES)
@@ -326,13 +327,13 @@ def test_two_phase_and_prepared_calls_match_the_single_call_bitwise():
 
 def _random_case(rng, i):
     """One seeded random decode case over the supported shape space: branches
-    and latent width (with their RoPE widths), heads and query tokens up to 64
-    rows, ragged lengths including empty and single-token sequences, causal or
+    and latent width (with their RoPE widths), heads and up to 4 query tokens
+    (up to 128 rows), ragged lengths including empty and single-token sequences, causal or
     not, and an explicit split count or the planner's."""
     nb, dc, dr = [(1, 64, 32), (1, 128, 64), (2, 64, 64), (2, 128, 32), (4, 64, 32),
                   (4, 128, 64), (1, 256, 64), (2, 256, 64), (1, 512, 64)][rng.integers(9)]
-    q = int(rng.integers(1, 3))
-    h = int(rng.integers(1, 64 // q + 1))
+    q = int(rng.integers(1, 5))
+    h = int(rng.integers(1, 128 // q + 1))
     s = int(rng.integers(1, 6))
     hi = int(rng.integers(1, 1500))
     cfg = _cfg(name=f"rand{i}", n_branch=nb, d_latent=dc, d_rope=dr, num_heads=h, q_len=q,
@@ -354,3 +355,18 @@ def test_random_shapes_match_the_oracle(i):
          f"causal={c.causal} {reduce} splits={splits} lens={inp.seq_lens.tolist()}")
     out, lse = run_gpu(inp, reduce, num_splits=splits)
     assert_parity(out, lse, *oracle(inp, reduce))
+
+
+@pytest.mark.parametrize("nb", [1, 4])
+def test_four_query_tokens_mid_size(nb):
+    # speculative-style verification of four new tokens per sequence: 128
+    # rows, four row tiles per workgroup (one branch) or four branch groups
+    # per split (four branches)
+    cfg = _cfg(num_seqs=4, q_len=4, num_heads=32, n_branch=nb, context_range=(1200, 3000),
+               seed=60 + nb)
+    inp = make_inputs(cfg)
+    dev = to_device(inp)
+    for reduce in ("sum", "concat"):
+        _say(f"four tokens nb={nb} {reduce} lens={inp.seq_lens.tolist()}")
+        out, lse = run_gpu(inp, reduce, dev=dev)
+        assert_parity(out, lse, *oracle(inp, reduce))
