@@ -71,11 +71,10 @@ typedef enum mlra_branch_reduce {
  * dense default. The innermost (feature) dimension is always contiguous. */
 typedef struct mlra_decode_dims {
   int32_t num_seqs;            /* S  >= 1 */
-  int32_t q_len;               /* Q  in {1, 2}: new query tokens per sequence (decode;
-                                * longer chunks, e.g. several draft tokens to verify, go
-                                * to mlra_prefill_attention, which computes the same
-                                * out and lse for any Q) */
-  int32_t num_heads;           /* H  >= 1, H * Q <= 64 (decode) */
+  int32_t q_len;               /* Q  in {1, 2, 3, 4}: new query tokens per sequence
+                                * (decode; longer chunks go to mlra_prefill_attention,
+                                * which computes the same out and lse for any Q) */
+  int32_t num_heads;           /* H  >= 1, H * Q <= 128 (decode) */
   int32_t d_latent;            /* DC per branch: fp32 {64, 128, 256, 512}; bf16 {64, 128} with
                                   any n_branch, 256 with n_branch <= 2 and DR = 64 (MLRA-2:
                                   MLA's 512-wide latent in two branches), 512 with n_branch = 1
@@ -114,11 +113,9 @@ typedef struct mlra_decode_plan {
   int32_t splits_per_seq;      /* splits of the longest sequence; grid = S x this */
   int32_t kernel_variant;      /* internal kernel id (for logs and tests) */
   int32_t lds_bytes;           /* LDS one split workgroup allocates */
-  int32_t row_groups;          /* split-kernel workgroups per split (1 or 2): with more
-                                  than 32 query rows, two when the branches do not fit
-                                  one workgroup (four of width <= 128, two of 256: each
-                                  takes its own) or the latent is 512 wide (each takes
-                                  32 rows), else one */
+  int32_t row_groups;          /* split-kernel workgroups per split (1 to 4): branch
+                                  groups times row groups, when the call's branches and
+                                  32-row tiles of query rows do not fit one workgroup */
   size_t workspace_bytes;      /* bytes of device workspace the call needs */
 } mlra_decode_plan;
 
