@@ -196,7 +196,7 @@ def bench_append(torch, args) -> int:
             reps += 1
         per = t_total / reps
         res["cpu_baseline"] = {
-            "value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "value": round(nbytes / per / 1e9, 4), "unit": "GB/s", **cpu_fields(1), "kind": "oracle",
             "sample": f"{reps} full passes of the {cfg.name} batch through the float64 oracle "
                       f"(single-threaded Python loop over tokens; {per * 1e3:.1f} ms per pass, "
                       f"{cfg.num_seqs * cfg.q_len / per:.0f} new tokens/s)"}
@@ -268,7 +268,7 @@ def bench_outproj(torch, args) -> int:
             reps += 1
         per = t_total / reps
         res["cpu_baseline"] = {
-            "value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": _blas_threads(),
+            "value": round(nbytes / per / 1e9, 3), "unit": "GB/s", **cpu_fields(_blas_threads()),
             "kind": "oracle",
             "sample": f"{reps} passes of the float64 oracle (NumPy matmul, float64 copy of the "
                       f"weight included) over the same operands, {per * 1e3:.1f} ms per pass"}
@@ -404,19 +404,48 @@ def bench_prefill(torch, args) -> int:
             ntok += 1
         res["cpu_baseline"] = {
             "value": round(done / t_total / 1e12, 6), "unit": "TFLOP/s",
-            "cores": _blas_threads(), "kind": "oracle",
+            **cpu_fields(_blas_threads()), "kind": "oracle",
             "sample": f"{ntok} query tokens of sequence 0 (all {H} heads, the last ones of the "
                       f"chunk) through the float64 NumPy oracle, {t_total:.1f} s"}
     print(json.dumps(res), flush=True)
     return 0
 
 
-def _blas_threads() -> int:
+def _blas_info() -> dict:
+    """BLAS library NumPy calls into: vendor (internal_api) and thread count."""
     try:
         from threadpoolctl import threadpool_info
-        return int(max([t.get("num_threads", 1) for t in threadpool_info()] or [1]))
+        blas = [t for t in threadpool_info() if t.get("user_api") == "blas"]
+        if blas:
+            return {"vendor": str(blas[0].get("internal_api", "unknown")),
+                    "threads": int(max(t.get("num_threads", 1) for t in blas))}
     except Exception:  # pragma: no cover
-        return 1
+        pass
+    return {"vendor": "unknown", "threads": 1}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_fields(threads_used: int) -> dict:
+    """What the CPU baseline ran on: `cores` is the threads the oracle used
+    (BLAS threads, never more than the cores this process may run on); the
+    affinity count, CPU model and BLAS vendor/threads are reported beside it."""
+    affinity = len(os.sched_getaffinity(0))
+    return {"cores": int(min(threads_used, affinity)), "affinity_cores": affinity,
+            "cpu_model": _cpu_model(), "blas": _blas_info()}
+
+
+def _blas_threads() -> int:
+    return _blas_info()["threads"]
 
 
 def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
@@ -434,7 +463,7 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
         t_total += time.perf_counter() - t0
         reps += 1
     per = t_total / reps
-    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", **cpu_fields(threads),
             "kind": "oracle",
             "sample": f"{reps} full passes of the {c.name} batch through the float64 NumPy "
                       f"oracle ({per * 1e3:.1f} ms per pass, {c.num_seqs * c.q_len / per:.1f} "

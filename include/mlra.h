@@ -289,9 +289,9 @@ mlra_status mlra_out_projection(const void* x, const void* w_packed, void* y, in
 
 /*
  * Chunked-prefill MLRA attention: the decode formula at the top of this
- * header for a chunk of many new query tokens per sequence. It is the
- * regime where the FlashAttention-3 pages place prefill (many queries per
- * key, bound by matrix throughput), over the same paged latent cache
+ * header for a chunk of many new query tokens per sequence (many queries
+ * per key, so the work is bound by matrix throughput rather than by HBM),
+ * over the same paged latent cache
  * (wispaper.ai blog "MLRA: Breaking the Sharding Bottleneck in Latent
  * Attention", "The Core Insight": every head scores the shared latent and
  * RoPE key of each token, one softmax per branch, branch outputs combined

@@ -14,8 +14,11 @@ Returns (out, lse): out [S][Q][H][DC] for reduce="sum", [S][Q][H][NB][DC] for
 "concat"; lse [S][Q][H][NB] float32.
 
 Calls that do not pass a workspace share one per device; such calls must not
-run concurrently on different streams. PreparedDecode validates and marshals
-once, for loops that repeat the same call.
+run concurrently on different streams, and they are refused while a stream is
+being captured into a HIP graph (the shared buffer is replaced when a later
+call needs more bytes, so a replayed graph would write freed memory): captured
+calls pass their own workspace, or use PreparedDecode, which owns one.
+PreparedDecode validates and marshals once, for loops that repeat the same call.
 """
 from __future__ import annotations
 
@@ -34,7 +37,14 @@ _workspaces: dict = {}
 
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A per-device scratch buffer that only grows (torch owns the memory)."""
+    """A per-device scratch buffer that only grows (torch owns the memory).
+
+    Refused under stream capture: a graph would keep the pointer of a buffer
+    that a later, larger call frees."""
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("a call captured into a HIP graph must pass its own workspace "
+                           "(or use PreparedDecode): the shared per-device workspace can be "
+                           "replaced by a later call")
     key = (device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:

@@ -51,14 +51,16 @@ constexpr int pc_groups(int NB, int rows, int DC) {
 }
 // LDS layout (byte offsets): ring [nslot][slot_bytes] at 0 (a slot holds the
 // NBW latents and the RoPE key of 32 tokens; the staged query rows, RT
-// slots' worth, alias it), then the merge records of every token stream but
+// slots' worth, alias its END, from qoff: loaders fill the first slots
+// before the compute waves have read their queries, and wait for that only
+// before the first write into slot qslot or later), then the merge records of every token stream but
 // the merging one of each compute wave's triple (C * (4/C - 1) records of
 // (DC/WD/32 * 4 + 1) x 64 x 16 bytes, C = NBW * RT * WD; none when C = 4),
 // then, with WD > 1, the partial-score exchange [2][4 waves][16 floats x 64
 // lanes], then the block ids, then the counters ready[nslot],
 // consumed[nslot], qdone, recorded[4], exchanged[4].
 struct PcLds {
-  int32_t slot_bytes, nslot, merge, xchg, table, flags, total;
+  int32_t slot_bytes, nslot, merge, xchg, table, flags, total, qoff, qslot;
 };
 constexpr PcLds pc_lds(int NBW, int RT, int WD, int DC, int DR) {
   const int slot = (NBW * kSub * (DC / 8 + 2) + kSub * (DR / 8 + 1)) * 16;
@@ -77,7 +79,9 @@ constexpr PcLds pc_lds(int NBW, int RT, int WD, int DC, int DR) {
                front + rec,
                front + rec + xchg,
                front + rec + xchg + kPcMaxTiles * 4,
-               front + rec + xchg + fixed};
+               front + rec + xchg + fixed,
+               front - qry,
+               (front - qry) / slot};
 }
 // Sub-tiles each loader keeps in flight: about kPcLoaderKB KB of loads per
 // loader, 48 KB per CU (measured best of 36..72 KB at B=16, T=8192). A CU

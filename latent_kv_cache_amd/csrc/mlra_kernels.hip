@@ -227,8 +227,9 @@ mlra_split_pc(SplitParams p) {
   // Prologue. Loader waves read the split's first 64 block ids into a
   // register and issue their first PL sub-tiles at once; compute waves stage
   // the split's block ids and the query rows (coalesced) in LDS, over the
-  // ring, and clear the counters. The first cache loads thus leave as soon as
-  // the block table arrives, not after the queries.
+  // ring's last slots, and clear the counters. The first cache loads thus
+  // leave as soon as the block table arrives, not after the queries, and the
+  // first slots are filled without waiting for the queries to be read.
   const int L_raw = p.seq_lens[s];
   const int64_t tab_base = (int64_t)s * p.max_blocks;
   const bool is_loader = wave >= 4;
@@ -281,6 +282,9 @@ mlra_split_pc(SplitParams p) {
     // ---------------- loader ----------------
     auto write = [&](int j, u32x4 (&d)[P]) {
       const int slot = j % NSLOT;
+      // first pass: slots from qslot on hold the staged query rows until
+      // every compute wave has read its own into registers
+      if (j >= lay.qslot && j < NSLOT) lds_wait_geq(qdone, 4);
       lds_wait_geq(consumed + slot, (j / NSLOT) * NCW);  // previous occupant done
       unsigned char* sb = smem + slot * lay.slot_bytes;
       const int tok0 = (t0 + (j >> 1)) * kBlock + (j & 1) * kSub;
@@ -297,7 +301,6 @@ mlra_split_pc(SplitParams p) {
       lds_signal(ready + slot);
     };
     auto phys_of = [&](int j) { return j < nsub ? tabl[min(j >> 1, kPcMaxTiles - 1)] : 0; };
-    lds_wait_geq(qdone, 4);  // the ring aliases the staged query rows
     // Steady state: write j, issue j + PL into the same registers (every
     // written sub-tile here is < nsub); then the last PL without new loads.
     // (Issuing fewer sub-tiles first and ramping up to PL was measured
@@ -345,8 +348,8 @@ mlra_split_pc(SplitParams p) {
                                  : qrop + head * DR + cr * 8;
       const u32x4 v = ld16(src);
       qv[kq] = live ? v : u32x4{};
-      qdst[kq] = is_lat ? ((bb * QR + rl) * LP + cl) * 16
-                        : (is_rope ? NBW * QR * LP * 16 + (rr * RP + cr) * 16 : -1);
+      qdst[kq] = is_lat ? lay.qoff + ((bb * QR + rl) * LP + cl) * 16
+                        : (is_rope ? lay.qoff + NBW * QR * LP * 16 + (rr * RP + cr) * 16 : -1);
     }
     sizes();
     if (nsub == 0) return;  // uniform over the workgroup
@@ -360,9 +363,10 @@ mlra_split_pc(SplitParams p) {
     // ---------------- compute ----------------
     // this wave's slice of the query row (the k order of the score MFMAs:
     // lane half g takes chunks g*LCHW/2 + st of the slice)
-    const unsigned char* const qb = smem + ((b * QR + row0 + n) * LP + wd * LCHW + g * (LCHW / 2)) * 16;
+    const unsigned char* const qb =
+        smem + lay.qoff + ((b * QR + row0 + n) * LP + wd * LCHW + g * (LCHW / 2)) * 16;
     const unsigned char* const qrb =
-        smem + NBW * QR * LP * 16 + ((row0 + n) * RP + wd * RCHW + g * (RCHW / 2)) * 16;
+        smem + lay.qoff + NBW * QR * LP * 16 + ((row0 + n) * RP + wd * RCHW + g * (RCHW / 2)) * 16;
     auto rd16 = [](const unsigned char* a) {
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a));
     };

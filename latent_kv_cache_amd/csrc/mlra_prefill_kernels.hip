@@ -9,9 +9,9 @@
 // position L - Q + j and sees every cached token up to its own position
 // (the cached context, then the chunk's earlier tokens and itself).
 //
-// This is the regime the FlashAttention-3 pages describe for prefill: many
-// queries per key, bound by matrix throughput rather than by HBM. What MLRA
-// changes is the key: every head of a query token scores the same cached
+// With many queries per key the work is bound by matrix throughput rather
+// than by HBM (per query row and visible token the kernel does 640 flops at
+// DC = 128, DR = 64, and reads nothing new). What MLRA changes is the key: every head of a query token scores the same cached
 // latent and RoPE key (absorbed form), so a workgroup's rows -- 8 query
 // tokens x 32 heads at H = 32 -- share one stream of cache tiles. Each
 // 64-token tile is read from HBM (or L2) once per workgroup, loaded straight
@@ -24,8 +24,8 @@
 //   O^T += c^T P^T                            32x32x16 bf16 MFMA, transposed LDS reads
 // software-pipelined by one sub-tile: the score MFMAs of sub-tile j are
 // issued between the vector instructions that turn the scores of sub-tile
-// j-1 into probabilities (the FlashAttention-3 pages' overlap of softmax
-// with the matrix products, here inside one wave's instruction stream).
+// j-1 into probabilities, so the matrix products overlap the softmax inside
+// one wave's instruction stream while the SIMD's other wave covers its waits.
 //
 // Outputs: with one split and no branch sum (one branch, or CONCAT) the
 // kernel writes out and lse directly; otherwise it writes the decode
