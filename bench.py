@@ -510,6 +510,9 @@ def main() -> int:
                          "mlra4_tp_share_prefill_b4_c2048_t8192) instead of decode attention")
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0: enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-merge", action="store_true",
+                    help="let the split kernel merge the splits itself where it can "
+                         "(MLRA_DECODE_FLAG_FUSED_MERGE) instead of a second kernel")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a HIP graph (the individual-launch time is "
                          "reported beside as eager_ms_per_step)")
@@ -558,7 +561,7 @@ def main() -> int:
               sum_seq_lens=int(inp.seq_lens.sum()))
     prep = api.PreparedDecode(d["q_latent"], d["q_rope"], lat_all, rope_all, tables[0],
                               d["seq_lens"], NB, cfg.scale, cfg.out_rescale, out=out, lse=lse,
-                              **kw)
+                              fused_merge=args.fused_merge, **kw)
     plan = prep.plan
 
     def step(i):
@@ -660,7 +663,8 @@ def main() -> int:
                    "q_len": cfg.q_len, "heads": cfg.num_heads, "n_branch": cfg.n_branch,
                    "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "block_size": cfg.block_size,
                    "cache_copies": copies, "tiles_per_split": plan.tiles_per_split,
-                   "splits_per_seq": plan.splits_per_seq, "graph": bool(graph)},
+                   "splits_per_seq": plan.splits_per_seq, "fused_merge": bool(plan.fused_merge),
+                   "graph": bool(graph)},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(cfg.num_seqs * cfg.q_len / (ms * 1e-3), 1),
         "kv_tokens_per_s": round(ab["kv_tokens"] / (ms * 1e-3), 1),

@@ -36,6 +36,15 @@
  *    launch failed (hipGetLastError); the stream may hold partial work.
  *  - No exceptions cross the ABI and the library prints nothing.
  *  - Two calls that share a workspace must not run concurrently.
+ *  - Every workspace (decode, prefill, output projection) starts with a
+ *    header of MLRA_DECODE_WS_HEADER_BYTES that belongs to decode calls and
+ *    that the other calls leave untouched, so one scratch buffer can serve
+ *    them all. It must hold zeros before the buffer's first decode call
+ *    (allocate it zero-filled, or call mlra_decode_workspace_init once);
+ *    every call leaves it ready for the next one. The rest of a workspace
+ *    needs no initialisation. The header holds a status word
+ *    (mlra_decode_read_status) and the counters through which the split
+ *    kernel's workgroups merge their results without a second launch.
  */
 #ifndef MLRA_H_
 #define MLRA_H_
@@ -67,6 +76,23 @@ typedef enum mlra_branch_reduce {
   MLRA_BRANCH_CONCAT = 1  /* out[S][Q][H][n_branch][DC] = out_rescale * o_b */
 } mlra_branch_reduce;
 
+/* Bytes at the start of every decode workspace that hold the status word and
+ * the in-kernel merge counters (zero before first use; see above). The
+ * per-split partial results follow at this offset. */
+#define MLRA_DECODE_WS_HEADER_BYTES 65792
+
+/* mlra_decode_dims.flags */
+#define MLRA_DECODE_FLAG_FUSED_MERGE 1  /* let the split kernel merge the splits itself where
+                                           it can (see mlra_decode_attention) */
+
+/* Status bits (mlra_decode_read_status). */
+#define MLRA_DEVSTATUS_WAIT_EXPIRED 1u  /* a bounded wait inside the split kernel gave up:
+                                           that call's out and lse are unreliable */
+#define MLRA_DEVSTATUS_MERGE_FAILED 2u  /* the in-kernel merge could not verify that a
+                                           sequence's workgroups shared one L2 (XCD), or
+                                           its waits expired: that sequence's out and lse
+                                           were written as NaN */
+
 /* Shapes and layout of one decode call. Strides are in ELEMENTS; 0 selects the
  * dense default. The innermost (feature) dimension is always contiguous. */
 typedef struct mlra_decode_dims {
@@ -90,7 +116,7 @@ typedef struct mlra_decode_dims {
                                 * (65536 tokens) for bfloat16 */
   int32_t dtype;               /* mlra_dtype */
   int32_t reduce;              /* mlra_branch_reduce */
-  int32_t reserved;            /* must be 0 */
+  int32_t flags;               /* MLRA_DECODE_FLAG_* bits (0 = defaults); others must be 0 */
   /* latent_cache element strides: block, token, branch. Defaults (0):
    * token-major [num_blocks][64][n_branch][DC] -> 64*n_branch*DC, n_branch*DC, DC */
   int64_t latent_stride_block, latent_stride_token, latent_stride_branch;
@@ -116,7 +142,10 @@ typedef struct mlra_decode_plan {
   int32_t row_groups;          /* split-kernel workgroups per split (1 to 4): branch
                                   groups times row groups, when the call's branches and
                                   32-row tiles of query rows do not fit one workgroup */
-  size_t workspace_bytes;      /* bytes of device workspace the call needs */
+  int32_t fused_merge;         /* 1: the split kernel merges the splits itself, with no
+                                  combine launch (see mlra_decode_attention) */
+  int32_t reserved0;
+  size_t workspace_bytes;      /* bytes of device workspace the call needs (header included) */
 } mlra_decode_plan;
 
 /* Plan a call without touching the GPU: split sequences into chunks of
@@ -130,6 +159,18 @@ mlra_status mlra_decode_make_plan(const mlra_decode_dims* dims, int32_t n_branch
 /* Workspace bytes for a call on the current device (queries its CU count). */
 mlra_status mlra_decode_workspace_size(const mlra_decode_dims* dims, int32_t n_branch,
                                        size_t* bytes);
+
+/* Zero the header of a decode workspace (asynchronous on stream, by a small
+ * kernel, so it may be captured into a HIP graph). Needed once per workspace
+ * unless it was allocated zero-filled. bytes >= MLRA_DECODE_WS_HEADER_BYTES. */
+mlra_status mlra_decode_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Read the status word of a decode workspace: MLRA_DEVSTATUS_* bits that
+ * calls on it have set since it was last cleared (0: nothing went wrong).
+ * Synchronous: waits for stream to reach this point, so not for graph
+ * capture. clear != 0 then zeroes the word. */
+mlra_status mlra_decode_read_status(void* workspace, uint32_t* bits, int32_t clear,
+                                    void* stream);
 
 /*
  * MLRA decode attention (formula above).
@@ -146,7 +187,23 @@ mlra_status mlra_decode_workspace_size(const mlra_decode_dims* dims, int32_t n_b
  *  out          SUM: [S][Q][H][DC]; CONCAT: [S][Q][H][n_branch][DC]; dtype
  *  lse          [S][Q][H][n_branch] float32, natural log; -inf where V <= 0
  *  workspace    device scratch of at least mlra_decode_workspace_size bytes,
- *               16-byte aligned; contents need no initialisation
+ *               16-byte aligned; its first MLRA_DECODE_WS_HEADER_BYTES must be
+ *               zero before its first decode call (see the conventions above)
+ *
+ * By default a second kernel merges the splits. With
+ * MLRA_DECODE_FLAG_FUSED_MERGE, when the plan reports fused_merge (bfloat16;
+ * S a multiple of 8 and at most 64; one workgroup per CU covers the whole
+ * call; every sequence the same length bound), the split kernel finishes the
+ * call itself: all workgroups of a sequence run on one XCD,
+ * each publishes its partial result through that XCD's shared L2 and a
+ * per-workgroup counter in the header, waits for the others and merges a
+ * slice of the sequence's output. The workgroups verify that they share an
+ * XCD; if they cannot (or their bounded waits expire), a workgroup that was
+ * dispatched after all others of its sequence merges what the rest gave up,
+ * or the sequence's out and lse are written as NaN and the status word says
+ * so. On an MI355X this measured slower than the second kernel at B=16,
+ * T=8192 (21.4 against 19.0 us per call): under load every round trip
+ * through the L2 costs about 1 us, and the merge needs several.
  *
  * Alignment: every tensor pointer 16-byte aligned; cache strides multiples
  * of 16 bytes. Table entries past ceil(L/64) are never used (they may hold
@@ -186,17 +243,18 @@ mlra_status mla_decode_attention(const void* q_latent, const void* q_rope,
  * Split-K with a log-sum-exp merge is exact: every split's softmax is
  * normalised on its own and re-weighted by exp(lse_split - lse_total).
  *
- * mlra_decode_partials runs the split kernel only. It takes the arguments of
- * mlra_decode_attention that the scores need and leaves, in the workspace,
- * with P = plan.splits_per_seq, T = plan.tiles_per_split, R = Q*H and
- * row r = j*H + h (plan from mlra_decode_make_plan with the same dims on the
- * same device):
- *   part_o   float32 [S][P][n_branch][R][DC] at byte offset 0:
+ * mlra_decode_partials runs the split kernel only (never the fused merge).
+ * It takes the arguments of mlra_decode_attention that the scores need and
+ * leaves, in the workspace, with P = plan.splits_per_seq, T =
+ * plan.tiles_per_split, R = Q*H, row r = j*H + h (plan from
+ * mlra_decode_make_plan with the same dims on the same device) and
+ * H0 = MLRA_DECODE_WS_HEADER_BYTES:
+ *   part_o   float32 [S][P][n_branch][R][DC] at byte offset H0:
  *            split k's softmax-weighted latent output over its tokens
  *            (already divided by its own sum of weights; 0 if it saw none);
  *   part_lse float32 [S][P][n_branch][R] at byte offset
- *            round_up(S*P*n_branch*R*DC*4, 256): natural log of the split's
- *            sum of exp(scaled score), -inf if it saw no visible token.
+ *            H0 + round_up(S*P*n_branch*R*DC*4, 256): natural log of the
+ *            split's sum of exp(scaled score), -inf if it saw no visible token.
  * Split k of sequence s covers tokens [64*T*k, min(64*T*(k+1), L)); only the
  * splits k < ceil(ceil(L/64) / T) are written, the rest of the slots keep
  * whatever they held.
@@ -333,6 +391,12 @@ mlra_status mlra_prefill_attention(const void* q_latent, const void* q_rope,
 
 /* Static, never-NULL description of a status code. */
 const char* mlra_status_string(mlra_status status);
+
+/* Testing only: bound every later decode call's internal waits by `polls`
+ * LDS polls and `polls` ticks (10 ns) of the in-kernel merge, so that tests
+ * can make them expire and check the status path while every kernel still
+ * ends; polls < 0 restores the defaults. Process-wide; not for production. */
+mlra_status mlra_testing_set_wait_limit(int32_t polls);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int32_t mlra_version(void);

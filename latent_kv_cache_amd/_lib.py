@@ -14,6 +14,9 @@ LIB_PATH = os.path.join(_PKG, "libmlra.so")
 
 MLRA_BF16, MLRA_FP32 = 0, 1
 MLRA_BRANCH_SUM, MLRA_BRANCH_CONCAT = 0, 1
+MLRA_DECODE_WS_HEADER_BYTES = 65792          # zero before a decode workspace's first use
+MLRA_DECODE_FLAG_FUSED_MERGE = 1
+MLRA_DEVSTATUS_WAIT_EXPIRED, MLRA_DEVSTATUS_MERGE_FAILED = 1, 2
 
 STATUS_NAMES = {0: "MLRA_OK", 1: "MLRA_ERR_NULL_PTR", 2: "MLRA_ERR_BAD_DIMS",
                 3: "MLRA_ERR_UNSUPPORTED", 4: "MLRA_ERR_WORKSPACE", 5: "MLRA_ERR_ALIGNMENT",
@@ -24,8 +27,8 @@ EXPORTS = ("mlra_decode_make_plan", "mlra_decode_workspace_size", "mlra_decode_a
            "mla_decode_attention", "mlra_decode_partials", "mlra_decode_combine",
            "mlra_cache_append", "mlra_out_projection_pack", "mlra_out_projection_workspace_size",
            "mlra_out_projection", "mlra_prefill_make_plan", "mlra_prefill_workspace_size",
-           "mlra_prefill_attention",
-           "mlra_status_string", "mlra_version")
+           "mlra_prefill_attention", "mlra_decode_workspace_init", "mlra_decode_read_status",
+           "mlra_testing_set_wait_limit", "mlra_status_string", "mlra_version")
 
 
 class DecodeDims(ctypes.Structure):
@@ -36,7 +39,7 @@ class DecodeDims(ctypes.Structure):
         ("max_blocks_per_seq", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
         ("max_seq_len", ctypes.c_int32), ("causal", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("dtype", ctypes.c_int32),
-        ("reduce", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("reduce", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("latent_stride_block", ctypes.c_int64), ("latent_stride_token", ctypes.c_int64),
         ("latent_stride_branch", ctypes.c_int64), ("rope_stride_block", ctypes.c_int64),
         ("rope_stride_token", ctypes.c_int64), ("sum_seq_lens", ctypes.c_int64),
@@ -49,6 +52,7 @@ class DecodePlan(ctypes.Structure):
         ("waves_per_group", ctypes.c_int32), ("tiles_per_split", ctypes.c_int32),
         ("splits_per_seq", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
         ("lds_bytes", ctypes.c_int32), ("row_groups", ctypes.c_int32),
+        ("fused_merge", ctypes.c_int32), ("reserved0", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -108,6 +112,12 @@ def load() -> ctypes.CDLL:
         lib.mlra_prefill_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, f32, f32, vp, vp,
                                                dims_p, vp, sz, vp]
         lib.mlra_prefill_attention.restype = i32
+        lib.mlra_decode_workspace_init.argtypes = [vp, sz, vp]
+        lib.mlra_decode_workspace_init.restype = i32
+        lib.mlra_decode_read_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), i32, vp]
+        lib.mlra_decode_read_status.restype = i32
+        lib.mlra_testing_set_wait_limit.argtypes = [i32]
+        lib.mlra_testing_set_wait_limit.restype = i32
         lib.mlra_status_string.argtypes = [i32]
         lib.mlra_status_string.restype = ctypes.c_char_p
         lib.mlra_version.argtypes = []

@@ -48,15 +48,40 @@ def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     key = (device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        # the library needs no initialised contents
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = new_workspace(device, nbytes)
         _workspaces[key] = ws
     return ws
 
 
+def new_workspace(device, nbytes: int) -> torch.Tensor:
+    """A decode workspace of at least nbytes, zero-filled: its header (status
+    word and in-kernel merge counters) must start at zero; every call leaves
+    it ready for the next."""
+    return torch.zeros(max(int(nbytes), _lib.MLRA_DECODE_WS_HEADER_BYTES), dtype=torch.uint8,
+                       device=device)
+
+
+def read_status(workspace: torch.Tensor, clear: bool = False, stream=None) -> int:
+    """MLRA_DEVSTATUS_* bits set by calls on this workspace (0: none).
+    Waits for the stream."""
+    lib = _lib.load()
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    bits = ctypes.c_uint32(0)
+    _lib.check(lib.mlra_decode_read_status(workspace.data_ptr(), ctypes.byref(bits),
+                                           1 if clear else 0, stream), "mlra_decode_read_status")
+    return int(bits.value)
+
+
+def default_workspace(device) -> Optional[torch.Tensor]:
+    """The shared per-device workspace of calls that pass none (or None)."""
+    dev = torch.device(device)
+    return _workspaces.get((dev.type, dev.index))
+
+
 def make_dims(q_latent, q_rope, latent_cache, rope_cache, block_table, *, max_seq_len: int,
               reduce: str = "sum", causal: bool = True, num_splits: int = 0,
-              sum_seq_lens: int = 0) -> _lib.DecodeDims:
+              sum_seq_lens: int = 0, fused_merge: bool = False) -> _lib.DecodeDims:
     S, Q, H, NB, DC = q_latent.shape
     if latent_cache.dim() != 4 or latent_cache.shape[2] != NB or latent_cache.shape[3] != DC:
         raise ValueError(f"latent_cache shape {tuple(latent_cache.shape)} does not match "
@@ -85,6 +110,7 @@ def make_dims(q_latent, q_rope, latent_cache, rope_cache, block_table, *, max_se
         latent_cache.stride(0), latent_cache.stride(1), latent_cache.stride(2))
     d.rope_stride_block, d.rope_stride_token = rope_cache.stride(0), rope_cache.stride(1)
     d.sum_seq_lens = int(sum_seq_lens)
+    d.flags = _lib.MLRA_DECODE_FLAG_FUSED_MERGE if fused_merge else 0
     return d
 
 
@@ -104,7 +130,7 @@ def make_prefill_plan(dims: _lib.DecodeDims, n_branch: int, num_cus: int = 0) ->
 
 def _call(entry: str, q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
           n_branch, scale, out_rescale, max_seq_len, reduce, causal, num_splits, sum_seq_lens,
-          out, lse, workspace, stream):
+          out, lse, workspace, stream, fused_merge=False):
     lib = _lib.load()
     tensors = (q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens)
     dev = q_latent.device
@@ -118,7 +144,7 @@ def _call(entry: str, q_latent, q_rope, latent_cache, rope_cache, block_table, s
         raise TypeError("seq_lens must be an int32 tensor of shape [S]")
     dims = make_dims(q_latent, q_rope, latent_cache, rope_cache, block_table,
                      max_seq_len=max_seq_len, reduce=reduce, causal=causal,
-                     num_splits=num_splits, sum_seq_lens=sum_seq_lens)
+                     num_splits=num_splits, sum_seq_lens=sum_seq_lens, fused_merge=fused_merge)
     S, Q, H, NB, DC = q_latent.shape
     oshape = (S, Q, H, DC) if reduce == "sum" else (S, Q, H, NB, DC)
     if entry == "partials":
@@ -281,13 +307,16 @@ def mlra_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
                           sum_seq_lens: int = 0, out: Optional[torch.Tensor] = None,
                           lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None,
-                          stream: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """MLRA decode attention; see include/mlra.h for the definition."""
+                          stream: Optional[int] = None,
+                          fused_merge: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MLRA decode attention; see include/mlra.h for the definition.
+    fused_merge=True lets the split kernel merge the splits itself where it
+    can (MLRA_DECODE_FLAG_FUSED_MERGE)."""
     if q_latent.dim() != 5 or q_latent.shape[3] != n_branch:
         raise ValueError("q_latent must be [S][Q][H][n_branch][DC]")
     return _call("mlra", q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
                  n_branch, scale, out_rescale, max_seq_len, reduce, causal, num_splits,
-                 sum_seq_lens, out, lse, workspace, stream)
+                 sum_seq_lens, out, lse, workspace, stream, fused_merge)
 
 
 def mlra_prefill_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
@@ -315,7 +344,8 @@ def mla_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
                          sum_seq_lens: int = 0, out: Optional[torch.Tensor] = None,
                          lse: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None,
-                         stream: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                         stream: Optional[int] = None,
+                         fused_merge: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """MLA-shaped single-latent call (n_branch = 1, out_rescale = 1).
 
     q_latent may be [S][Q][H][DC] or [S][Q][H][1][DC]; latent_cache may be
@@ -329,7 +359,7 @@ def mla_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
         lse = lse.unsqueeze(3)
     out, lse = _call("mla", q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
                      1, scale, 1.0, max_seq_len, "sum", causal, num_splits, sum_seq_lens, out,
-                     lse, workspace, stream)
+                     lse, workspace, stream, fused_merge)
     return out, lse[..., 0]
 
 
@@ -380,13 +410,15 @@ class PreparedDecode:
     def __init__(self, q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
                  n_branch: int, scale: float, out_rescale: float, *, max_seq_len: int,
                  reduce: str = "sum", causal: bool = True, num_splits: int = 0,
-                 sum_seq_lens: int = 0, out=None, lse=None, workspace=None, stream=None):
+                 sum_seq_lens: int = 0, out=None, lse=None, workspace=None, stream=None,
+                 fused_merge: bool = False):
         if q_latent.dim() != 5 or q_latent.shape[3] != n_branch:
             raise ValueError("q_latent must be [S][Q][H][n_branch][DC]")
         # one validated functional-path setup; its checks and shapes are reused
         self.dims = make_dims(q_latent, q_rope, latent_cache, rope_cache, block_table,
                               max_seq_len=max_seq_len, reduce=reduce, causal=causal,
-                              num_splits=num_splits, sum_seq_lens=sum_seq_lens)
+                              num_splits=num_splits, sum_seq_lens=sum_seq_lens,
+                              fused_merge=fused_merge)
         self.plan = make_plan(self.dims, n_branch)
         dev = q_latent.device
         S, Q, H, NB, DC = q_latent.shape
@@ -395,13 +427,13 @@ class PreparedDecode:
                                                            device=dev)
         self.lse = lse if lse is not None else torch.empty((S, Q, H, NB), dtype=torch.float32,
                                                            device=dev)
-        self.workspace = workspace if workspace is not None else torch.empty(
-            max(self.plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        self.workspace = workspace if workspace is not None else new_workspace(
+            dev, self.plan.workspace_bytes)
         self.stream = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
         # run the functional path once: validates every tensor and pointer rule
         _call("mlra", q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
               n_branch, scale, out_rescale, max_seq_len, reduce, causal, num_splits,
-              sum_seq_lens, self.out, self.lse, self.workspace, self.stream)
+              sum_seq_lens, self.out, self.lse, self.workspace, self.stream, fused_merge)
         self._table_shape = tuple(block_table.shape)
         self._table_dev = block_table.device
         self._lib = _lib.load()
@@ -431,7 +463,8 @@ class PreparedDecode:
         return self.out, self.lse
 
     def partials(self, block_table=None):
-        """The split kernel only (mlra_decode_partials)."""
+        """The split kernel only (mlra_decode_partials; never the in-kernel
+        merge, so partials() + combine() is the two-kernel form of run())."""
         q, qr, lc, rc = self._ptrs
         _lib.check(self._lib.mlra_decode_partials(
             q, qr, lc, rc, self._table_ptr(block_table), self._lens, self._nb, self._scale,

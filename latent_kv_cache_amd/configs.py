@@ -108,6 +108,10 @@ MLRA4_B1_T2M = DecodeConfig(
     d_latent=128, d_rope=64, dtype="bf16", context=1 << 21, seed=8,
     scale=_mlra_scale(128, 64), out_rescale=0.5)
 
+# The headline share with four new query tokens per sequence (speculative
+# decoding verifying three draft tokens: 128 query rows per sequence).
+MLRA4_TP_SHARE_Q4 = MLRA4_TP_SHARE.with_(name="mlra4_tp_share_b16_t8192_q4", q_len=4, seed=13)
+
 # Cache append at a large serving batch: 4096 sequences, 2 new tokens each,
 # all four MLRA-4 branches (one head: the append does not read queries).
 APPEND_B4096_Q2 = DecodeConfig(
@@ -136,7 +140,7 @@ MLRA4_FUSED_PREFILL = DecodeConfig(
 
 ALL = [TINY_MLRA4_FP32, MLRA4_TP_SHARE, MLRA4_FUSED, LONG_CONTEXT, RAGGED_Q2]
 # Variants and stress workloads beyond the five above.
-EXTRA = [MLRA2_FUSED, MLRA4_B1_T1M, MLRA4_B1_T2M, APPEND_B4096_Q2]
+EXTRA = [MLRA2_FUSED, MLRA4_B1_T1M, MLRA4_B1_T2M, APPEND_B4096_Q2, MLRA4_TP_SHARE_Q4]
 # Chunked-prefill workloads (mlra_prefill_attention).
 PREFILL = [MLRA4_TP_PREFILL, MLRA4_TP_PREFILL_WHOLE, MLRA4_FUSED_PREFILL]
 BY_NAME = {c.name: c for c in ALL + [MLA_COMPARE] + EXTRA + PREFILL}

@@ -24,7 +24,7 @@ mlra_status resolve_dims(const mlra_decode_dims* d, int32_t n_branch, Resolved* 
   if (!d || !r) return MLRA_ERR_NULL_PTR;
   if (d->dtype != MLRA_BF16 && d->dtype != MLRA_FP32) return MLRA_ERR_BAD_DIMS;
   if (d->reduce != MLRA_BRANCH_SUM && d->reduce != MLRA_BRANCH_CONCAT) return MLRA_ERR_BAD_DIMS;
-  if (d->reserved != 0) return MLRA_ERR_BAD_DIMS;
+  if (d->flags & ~MLRA_DECODE_FLAG_FUSED_MERGE) return MLRA_ERR_BAD_DIMS;
   if (d->num_seqs < 1 || d->num_heads < 1 || d->q_len < 1) return MLRA_ERR_BAD_DIMS;
   if (d->num_seqs > kMaxSeqs) return MLRA_ERR_UNSUPPORTED;  // grid y dimension
   if (d->q_len > 4) return MLRA_ERR_UNSUPPORTED;
@@ -62,6 +62,7 @@ mlra_status resolve_dims(const mlra_decode_dims* d, int32_t n_branch, Resolved* 
   o.causal = d->causal ? 1 : 0;
   o.dtype = d->dtype;
   o.reduce = d->reduce;
+  o.flags = d->flags;
   o.lsbr = d->latent_stride_branch ? d->latent_stride_branch : o.DC;
   o.lst = d->latent_stride_token ? d->latent_stride_token : (int64_t)o.NB * o.DC;
   o.lsb = d->latent_stride_block ? d->latent_stride_block : (int64_t)kBlock * o.lst;
@@ -187,11 +188,22 @@ mlra_status plan_call(const Resolved& r, const KernelShape& k, int32_t num_cus,
   p.lds_bytes = k.variant == kVariantPcBf16
                     ? pc_lds(pc_nbw(r.NB, r.rows, r.DC), pc_rt(r.rows, r.DC), pc_wd(r.DC), r.DC, r.DR).total
                     : 0;
-  // Partials: output [S][spl][NB][rows][DC] and lse [S][spl][NB][rows], fp32.
+  // In-kernel merge (when asked for): every workgroup of a sequence on one XCD (sequence s on
+  // the ids congruent to s mod kXcdSlots), all workgroups resident at once
+  // (one per CU), and a length bound shared by the batch (the hint, when
+  // given, says every sequence reaches it: a ragged batch would load the
+  // XCDs unevenly).
+  const int64_t per = spl * k.NRT;
+  const bool uniform = sum_seq_lens <= 0 || sum_seq_lens >= (int64_t)r.S * r.lcap;
+  p.fused_merge = k.variant == kVariantPcBf16 && (r.flags & MLRA_DECODE_FLAG_FUSED_MERGE) &&
+                  uniform && r.S % kXcdSlots == 0 && r.S <= kSyncSeqs && per <= kSyncSlots &&
+                  (int64_t)r.S * per <= num_cus && per * kXcdSlots <= num_cus;
+  // Header, then partials: output [S][spl][NB][rows][DC] and lse
+  // [S][spl][NB][rows], fp32.
   const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;
   const int64_t o_bytes = cdiv(slots * r.DC * 4, 256) * 256;
   const int64_t l_bytes = cdiv(slots * 4, 256) * 256;
-  p.workspace_bytes = (size_t)(o_bytes + l_bytes);
+  p.workspace_bytes = (size_t)(kWsHeaderBytes + o_bytes + l_bytes);
   *plan = p;
   return MLRA_OK;
 }

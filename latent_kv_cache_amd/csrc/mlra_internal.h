@@ -9,6 +9,22 @@
 namespace mlra {
 
 constexpr int kBlock = 64;      // tokens per cache block (= one split-K tile)
+// Decode workspace header: a status word, then one slot per sequence of the
+// in-kernel merge: kSyncSlots publication counters and kSyncSlots verdict
+// counters (64-bit each). Partial results follow the header.
+constexpr int kWsStatusBytes = 256;
+constexpr int kSyncSeqs = 64;           // sequences the in-kernel merge handles
+constexpr int kSyncSlots = 32;          // workgroups per sequence it handles
+constexpr int kSyncSlotBytes = 1024;    // 2 x 32 x 8 bytes, padded
+constexpr int kWsHeaderBytes = kWsStatusBytes + kSyncSeqs * kSyncSlotBytes;
+static_assert(kWsHeaderBytes == MLRA_DECODE_WS_HEADER_BYTES, "header size");
+static_assert(2 * kSyncSlots * 8 <= kSyncSlotBytes, "sync slot");
+// Workgroups whose ids are congruent modulo this many run on the same XCD
+// (the dispatcher deals workgroups to the XCDs round robin; the MI355X has 8,
+// and the 1- and 4-XCD partition modes divide it).
+constexpr int kXcdSlots = 8;
+// Default bound of the split kernel's LDS waits, in polls.
+constexpr int kDefaultWaitPolls = 1 << 22;
 constexpr int kMaxSeqs = 65535;  // grid y limit
 constexpr int kSub = 32;        // tokens per MFMA sub-tile (M of the 32x32 MFMA)
 
@@ -100,7 +116,7 @@ constexpr int pc_pl(int NBW, int DC, int DR) {
 // Dims after validation, with defaults resolved.
 struct Resolved {
   int32_t S, Q, H, rows, NB, DC, DR;
-  int32_t max_blocks, num_blocks, max_seq_len, lcap, causal, dtype, reduce;
+  int32_t max_blocks, num_blocks, max_seq_len, lcap, causal, dtype, reduce, flags;
   int64_t lsb, lst, lsbr;  // latent strides (elements): block, token, branch
   int64_t rsb, rst;        // rope strides (elements): block, token
 };

@@ -50,10 +50,20 @@ struct SplitParams {
   const int32_t* seq_lens;
   float* part_o;    // [S][spl][NB][rows][DC]
   float* part_lse;  // [S][spl][NB][rows]
+  unsigned* status;  // workspace status word (MLRA_DEVSTATUS_* bits)
+  // in-kernel merge: per-sequence slots of kSyncSlots publication counters
+  // then kSyncSlots verdict counters; the outputs; the bounds of its waits
+  uint64_t* sync;
+  void* out;
+  float* lse;
+  int64_t short_ticks, long_ticks;  // 10 ns ticks (s_memrealtime)
   int64_t lsb, lst, lsbr, rsb, rst;
   int32_t S, Q, H, rows, NB, DC, DR, spl, tps, max_blocks, num_blocks, lcap, causal;
   int32_t nrt;        // workgroups per split: row groups or branch groups (1 or 2)
+  int32_t wait_polls;  // bound of the LDS waits
+  int32_t concat;
   float score_scale;  // scale * log2(e): scores kept in base-2 units
+  float out_rescale;
 };
 
 struct CombineParams {
@@ -153,13 +163,26 @@ __device__ __forceinline__ i16x4 lds_read_tr(const unsigned char* p) {
 // and exits; that last stream waits for them and merges the records with its
 // own registers in a fixed stream order (so the partial does not depend on
 // which stream finished first) and writes it.
-__device__ __forceinline__ void lds_wait_geq(const int* flag, int target) {
-  // A few million polls (s_sleep 1 each) is far longer than any wait here.
-  for (int it = 0; it < (1 << 22); ++it) {
+// A wait that gives up (after `polls` polls, by default a few million: far
+// longer than any wait here) marks the wave's `expired`; the wave reports it
+// once, when it leaves the kernel, as MLRA_DEVSTATUS_WAIT_EXPIRED in the
+// workspace status word, so a broken hand-off is reported, not silent.
+// (An atomic after every wait measured 0.7 us slower at B=16, T=8192.)
+__device__ __forceinline__ void set_status(unsigned* status, unsigned bit) {
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void lds_wait_geq(const int* flag, int target, int polls, bool& expired) {
+  int it = 0;
+  for (; it < polls; ++it) {
     if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
     __builtin_amdgcn_s_sleep(1);
   }
+  if (it == polls) expired |= __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ void report_expired(unsigned* status, bool expired) {
+  if (expired) set_status(status, MLRA_DEVSTATUS_WAIT_EXPIRED);
 }
 __device__ __forceinline__ void lds_signal(int* flag) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -167,7 +190,204 @@ __device__ __forceinline__ void lds_signal(int* flag) {
     __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <int NBW, int RT, int WD, int DC, int DR, int NSLOT, int PL>
+// ---------------------------------------------------------------------------
+// In-kernel merge of a sequence's splits
+// ---------------------------------------------------------------------------
+// When the whole call runs as one round of workgroups (one per CU) and every
+// sequence's workgroups are dealt to one XCD (workgroup ids congruent modulo
+// kXcdSlots), the workgroups of a sequence merge their own partial results
+// instead of a second kernel doing it. The XCD's L2 is shared by its CUs, so
+// a partial or counter stored with ordinary stores is visible to the
+// sequence's other workgroups once the stores are acknowledged; reads that
+// must not hit this CU's L1 use the sc1 (agent-scope) bit.
+//
+// Every workgroup of sequence s owns a publication counter and a verdict
+// counter in the workspace header (slot rr: its index within the sequence).
+// All counters of a sequence advance in lock step, by one per call: a
+// workgroup reads its own counter N at the start, and after its partial is
+// stored publishes N+1 in its slot and in every slot no workgroup of this
+// call owns (so a later call with more workgroups finds them level). Values
+// carry the XCD id; a workgroup waits until every slot shows N+1 and all
+// XCD ids equal its own, then merges its share (chunk rr) of the sequence's
+// outputs. It writes its verdict: merging, gave up waiting, or found
+// another XCD. A workgroup that gives up after a short bound leaves its
+// chunk to the sequence's last workgroup (rr = per - 1), which is dealt to
+// its XCD after all others of the sequence, so it only waits for workgroups
+// that already run; it waits with a long bound, reads every verdict and
+// merges the chunks given up. Chunks that cannot be merged (workgroups on
+// different XCDs, or a long wait expired) are written as NaN and flagged in
+// the status word. A counter never goes back, so stale values never look
+// fresh; a header that was not zeroed leaves the slots uneven, which shows
+// as NaN and a flag rather than as wrong numbers.
+__device__ __forceinline__ uint64_t sync_load(const uint64_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Counters are published with plain stores: they stay in the XCD's L2,
+// where the sequence's other workgroups (same XCD) poll them with sc1 loads.
+// A workgroup on another XCD would not see them (its wait expires) or, if an
+// eviction wrote one back, would see a foreign XCD id: never stale data.
+__device__ __forceinline__ void sync_store(uint64_t* a, uint64_t v) {
+  *reinterpret_cast<volatile uint64_t*>(a) = v;
+}
+// A publication slot holds (count << 8) | XCD id: the workgroup's count.
+__device__ __forceinline__ uint64_t own_count(const uint64_t* sync, int s, int rr) {
+  return sync_load(sync + (size_t)s * (kSyncSlotBytes / 8) + rr) >> 8;
+}
+// XCC (XCD) id of the executing CU: hardware register 20 (HW_REG_XCC_ID), bits [3:0].
+__device__ __forceinline__ unsigned xcc_id() { return __builtin_amdgcn_s_getreg(6164) & 15u; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ void store_bf16x4(__bf16* d, f32x4 v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<bf16x4*>(d) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+
+// Merge the splits of sequence s for output items [i0, i1) (an item is four
+// columns of one row: of the branch sum, or of one branch with CONCAT),
+// thread tid of nthr; nan_fill writes NaN instead. Splits are merged in
+// order with a running log-sum-exp, 16 splits' loads in flight at a time.
+// The partials are read with plain loads: this CU has not touched those
+// lines in this kernel (its L1 holds no stale copy), so they come from the
+// XCD's L2, where their writers' acknowledged stores are.
+__device__ void merge_items(const SplitParams& p, int s, int nsplit, int i0, int i1, int tid,
+                            int nthr, bool nan_fill) {
+  const int C4 = p.DC >> 2;
+  const int64_t seq_rows = (int64_t)p.spl * p.NB * p.rows;  // partial rows of one sequence
+  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(p.part_o + (int64_t)s * seq_rows * p.DC);
+  const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(p.part_lse + (int64_t)s * seq_rows);
+  __bf16* const out = static_cast<__bf16*>(p.out);
+  for (int it = i0 + tid; it < i1; it += nthr) {
+    const int c4 = it % C4, rb = it / C4;
+    const int row = p.concat ? rb / p.NB : rb;
+    const int b0 = p.concat ? rb % p.NB : 0, b1 = p.concat ? b0 + 1 : p.NB;
+    const int64_t orow = (int64_t)s * p.rows + row;
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    for (int b = b0; b < b1; ++b) {
+      float m = -INFINITY, den = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < nsplit && !nan_fill; k0 += 16) {
+        float l[16];
+        f32x4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int pr = (min(k0 + u, nsplit - 1) * p.NB + b) * p.rows + row;
+          l[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, pr * 4, 0, 0));
+          v[u] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (pr * p.DC + 4 * c4) * 4, 0, 0));
+        }
+        // all 32 loads leave before the first wait (one round trip, not two)
+        __builtin_amdgcn_sched_barrier(0);
+        float mb = m;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (k0 + u < nsplit) mb = fmaxf(mb, l[u]);
+        if (mb == -INFINITY) continue;  // no visible token so far
+        const float sc = expf(m - mb);
+        den *= sc;
+        acc *= sc;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (k0 + u < nsplit) {
+            const float w = expf(l[u] - mb);
+            den += w;
+            acc += v[u] * w;
+          }
+        m = mb;
+      }
+      const f32x4 o = acc * (den > 0.f ? 1.f / den : 0.f);
+      const float lse_b = nan_fill ? NAN : (den > 0.f ? m + logf(den) : -INFINITY);
+      if (c4 == 0) p.lse[orow * p.NB + b] = lse_b;
+      if (p.concat)
+        store_bf16x4(out + (orow * p.NB + b) * p.DC + 4 * c4,
+                     nan_fill ? f32x4{NAN, NAN, NAN, NAN} : o * p.out_rescale);
+      else
+        tot += o;
+    }
+    if (!p.concat)
+      store_bf16x4(out + orow * p.DC + 4 * c4,
+                   nan_fill ? f32x4{NAN, NAN, NAN, NAN} : tot * p.out_rescale);
+  }
+}
+
+// The merge protocol (above) for workgroup rr of per of sequence s. Called by
+// the compute waves (cw 0-3) once their partial is stored; cw 0 drives. With
+// solo, only cw 0 runs (a workgroup with no tokens of its own) and merges
+// with its 64 lanes. N is the workgroup's own counter, read at its start.
+template <int NCW>
+__device__ void fused_merge(const SplitParams& p, int s, int rr, int per, int nsplit, uint64_t N,
+                            int cw, int lane, bool solo, int* stored, int* go, int* godec,
+                            bool& expired) {
+  const uint64_t next = N + 1;
+  uint64_t* const flags = p.sync + (size_t)s * (kSyncSlotBytes / 8);
+  uint64_t* const verd = flags + kSyncSlots;
+  const unsigned xcc = xcc_id();
+  const bool designated = rr == per - 1;
+  const int items = p.rows * (p.concat ? p.NB : 1) * (p.DC >> 2);
+  const int csz = (items + per - 1) / per;
+  auto lo = [&](int c) { return min(c * csz, items); };
+  auto hi = [&](int c) { return min((c + 1) * csz, items); };
+  int dec = 0;  // 1: merge own chunk; 2: gave up waiting; 3: another XCD found
+  if (cw == 0) {
+    if (!solo) lds_wait_geq(stored, NCW, p.wait_polls, expired);  // every partial writer's stores acknowledged
+    if (lane == 0)
+      for (int q = rr; q < kSyncSlots; q += per) sync_store(flags + q, (next << 8) | xcc);
+    const uint64_t bound = designated ? p.long_ticks : p.short_ticks;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool all = false, same = false;
+    for (;;) {
+      const uint64_t f = lane < per ? sync_load(flags + lane) : ((next << 8) | xcc);
+      if (__builtin_amdgcn_ballot_w64((f >> 8) != next) == 0) {
+        all = true;
+        same = __builtin_amdgcn_ballot_w64((f & 0xff) != xcc) == 0;
+        break;
+      }
+      if (__builtin_amdgcn_s_memrealtime() - t0 > bound) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    dec = !all ? 2 : (same ? 1 : 3);
+    if (lane == 0)
+      for (int q = rr; q < kSyncSlots; q += per)
+        sync_store(verd + q, (next << 2) | (uint64_t)(q == rr ? dec : 1));
+    if (!solo) {
+      if (lane == 0) *godec = dec;
+      lds_signal(go);
+    }
+  } else {
+    lds_wait_geq(go, 1, p.wait_polls, expired);
+    dec = *godec;
+  }
+  // The sequence's last workgroup reads the others' verdicts; its first read
+  // is issued before its own chunk, so the two overlap.
+  uint64_t v = (next << 2) | 1;
+  if (cw == 0 && designated && lane < per && lane != rr) v = sync_load(verd + lane);
+  if (dec == 1) merge_items(p, s, nsplit, lo(rr), hi(rr), solo ? lane : cw * 64 + lane, solo ? 64 : 256, false);
+  if (cw != 0 || !designated) return;
+  // Chunks the others gave up.
+  if (dec != 1) {
+    merge_items(p, s, nsplit, lo(rr), hi(rr), lane, 64, true);
+    set_status(p.status, MLRA_DEVSTATUS_MERGE_FAILED);
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_ballot_w64((v >> 2) != next) != 0) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)p.long_ticks) break;
+    __builtin_amdgcn_s_sleep(2);
+    if (lane < per && lane != rr) v = sync_load(verd + lane);
+  }
+  const int state = (v >> 2) == next ? (int)(v & 3) : 0;  // 0: no verdict in time
+  for (int q = 0; q < per; ++q) {
+    if (q == rr) continue;
+    const int sq = __builtin_amdgcn_readlane(state, q);
+    if (sq == 1) continue;  // merged by its own workgroup
+    const bool can = dec == 1 && sq == 2;
+    merge_items(p, s, nsplit, lo(q), hi(q), lane, 64, !can);
+    if (!can) set_status(p.status, MLRA_DEVSTATUS_MERGE_FAILED);
+  }
+}
+
+template <int NBW, int RT, int WD, int DC, int DR, int NSLOT, int PL, bool FUSED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mlra_split_pc(SplitParams p) {
   constexpr int NP = NBW * RT;   // (branch, row tile) pairs
@@ -193,13 +413,30 @@ mlra_split_pc(SplitParams p) {
   int* const qdone = consumed + NSLOT;
   int* const recorded = qdone + 1;    // [4] merge records written, per compute wave of a stream
   int* const exchanged = recorded + 4;  // [4] partial scores written, per compute wave
+  int* const stored = exchanged + 4;    // in-kernel merge: partial writers done
+  int* const go = stored + 1;           // in-kernel merge: the driving wave's decision made
+  int* const godec = go + 1;            // ... and what it is
   int* const tabl = reinterpret_cast<int*>(smem + lay.table);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
+  bool expired = false;       // a wait of this wave gave up (reported when it leaves)
   int k, s, bo = 0, rb0 = 0;  // bo, rb0: first branch and first query row of this workgroup
-  if (p.nrt == 1) {
+  int rr = 0;                 // in-kernel merge: index of this workgroup within its sequence
+  const int per = p.spl * p.nrt;
+  if constexpr (FUSED) {
+    // Sequence s's workgroups are the ids congruent to s mod kXcdSlots (one
+    // XCD), split-major within the sequence.
+    const int id = blockIdx.x, jx = id / kXcdSlots;
+    s = id % kXcdSlots + kXcdSlots * (jx / per);
+    rr = jx % per;
+    k = rr / p.nrt;
+    const int grp = rr % p.nrt;
+    const int nbg = p.NB / NBW;
+    bo = (grp % nbg) * NBW;
+    rb0 = (grp / nbg) * RT * kSub;
+  } else if (p.nrt == 1) {
     k = blockIdx.x;
     s = blockIdx.y;
   } else {
@@ -261,6 +498,7 @@ mlra_split_pc(SplitParams p) {
   };
   f32x16 acc[NDT];
   float m_run = -INFINITY, l_run = 0.f;
+  uint64_t n_own = 0;  // in-kernel merge: this workgroup's counter at its start
   const int cw = wave & 3;                // compute waves: index
   const int wd = cw % WD;                 // latent slice
   const int pi = (cw / WD) % NP;          // (branch, row tile) pair
@@ -284,8 +522,8 @@ mlra_split_pc(SplitParams p) {
       const int slot = j % NSLOT;
       // first pass: slots from qslot on hold the staged query rows until
       // every compute wave has read its own into registers
-      if (j >= lay.qslot && j < NSLOT) lds_wait_geq(qdone, 4);
-      lds_wait_geq(consumed + slot, (j / NSLOT) * NCW);  // previous occupant done
+      if (j >= lay.qslot && j < NSLOT) lds_wait_geq(qdone, 4, p.wait_polls, expired);
+      lds_wait_geq(consumed + slot, (j / NSLOT) * NCW, p.wait_polls, expired);  // previous occupant done
       unsigned char* sb = smem + slot * lay.slot_bytes;
       const int tok0 = (t0 + (j >> 1)) * kBlock + (j & 1) * kSub;
 #pragma unroll
@@ -323,6 +561,10 @@ mlra_split_pc(SplitParams p) {
 #pragma unroll
     for (int kt = 0; kt < TK; ++kt)
       tv[kt] = p.table[tab_base + min(t0 + kt * 256 + (int)threadIdx.x, p.max_blocks - 1)];
+    // in-kernel merge: the driving wave reads its own counter now, so the
+    // load is long done when the merge starts
+    if constexpr (FUSED)
+      if (wave == 0) n_own = own_count(p.sync, s, rr);
     // query rows of the workgroup: latent [NBW][RT*32 rows][LP chunks], then
     // RoPE [RT*32][RP]
     constexpr int QR = RT * kSub;
@@ -352,13 +594,23 @@ mlra_split_pc(SplitParams p) {
                         : (is_rope ? lay.qoff + NBW * QR * LP * 16 + (rr * RP + cr) * 16 : -1);
     }
     sizes();
-    if (nsub == 0) return;  // uniform over the workgroup
+    if (nsub == 0) {  // uniform over the workgroup
+      if constexpr (FUSED) {
+        if (wave == 0) {
+          const int nsplit = min((L + kBlock * p.tps - 1) / (kBlock * p.tps), p.spl);
+          fused_merge<NCW>(p, s, rr, per, nsplit, own_count(p.sync, s, rr), 0, lane, true, nullptr,
+                           nullptr, nullptr, expired);
+          report_expired(p.status, expired);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int kt = 0; kt < TK; ++kt) tabl[kt * 256 + threadIdx.x] = clamp_block(tv[kt], p.num_blocks);
 #pragma unroll
     for (int kq = 0; kq < QK; ++kq)
       if (qdst[kq] >= 0) *reinterpret_cast<u32x4*>(smem + qdst[kq]) = qv[kq];
-    if (threadIdx.x < 2 * NSLOT + 9) ready[threadIdx.x] = 0;  // every counter
+    if (threadIdx.x < 2 * NSLOT + 12) ready[threadIdx.x] = 0;  // every counter
     lds_barrier();
     // ---------------- compute ----------------
     // this wave's slice of the query row (the k order of the score MFMAs:
@@ -388,7 +640,7 @@ mlra_split_pc(SplitParams p) {
                     (wd * DCW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     for (int j = strm; j < nsub; j += WT) {
       const int slot = j % NSLOT;
-      lds_wait_geq(ready + slot, (j / NSLOT + 1) * 4);
+      lds_wait_geq(ready + slot, (j / NSLOT + 1) * 4, p.wait_polls, expired);
       const unsigned char* sb = smem + slot * lay.slot_bytes;
       const int tb = (t0 + (j >> 1)) * kBlock + (j & 1) * kSub;
       // LDS reads are batched ahead of the MFMAs that use them: the score
@@ -444,7 +696,7 @@ mlra_split_pc(SplitParams p) {
         lds_signal(exchanged + cw);
 #pragma unroll
         for (int w = 0; w < WD; ++w)
-          if (w != wd) lds_wait_geq(exchanged + cw - wd + w, u + 1);
+          if (w != wd) lds_wait_geq(exchanged + cw - wd + w, u + 1, p.wait_polls, expired);
         f32x16 tot = f32x16{};
 #pragma unroll
         for (int w = 0; w < WD; ++w) {
@@ -509,24 +761,31 @@ mlra_split_pc(SplitParams p) {
   }
 
   const int64_t slotp = (int64_t)s * p.spl + k;
+  if (wave >= 4) {  // loaders
+    report_expired(p.status, expired);
+    return;
+  }
   if constexpr (WT == 1) {
-    if (wave >= 4) return;
     const int row = rb0 + row0 + n;
-    if (row >= p.rows) return;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int64_t ri = (slotp * NBT + bo + b) * p.rows + row;
-    float* o = p.part_o + ri * DC + wd * DCW;
+    if (row < p.rows) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      const int64_t ri = (slotp * NBT + bo + b) * p.rows + row;
+      float* o = p.part_o + ri * DC + wd * DCW;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
-            f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} * inv;
-    if (g == 0 && wd == 0) p.part_lse[ri] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) =
+              f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} * inv;
+      if (g == 0 && wd == 0) p.part_lse[ri] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    }
+    if constexpr (FUSED) {  // partial acknowledged by the L2 before the merge uses it
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_signal(stored);
+    }
   } else {
     // Merge the WT token streams of each compute wave's triple (see above).
     constexpr int REC = NDT * 4 + 1;  // 64-lane f32x4 rows per record
-    if (wave >= 4) return;
     const int tri = cw % NCW;  // (branch, row tile, slice) within a stream
     f32x4* const M = reinterpret_cast<f32x4*>(smem + lay.merge) + tri * (WT - 1) * REC * 64;
     // The stream holding the split's last sub-tile (it finishes last) merges;
@@ -543,14 +802,17 @@ mlra_split_pc(SplitParams p) {
               f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]};
       my[(REC - 1) * 64 + lane] = f32x4{m_run, l_run, 0.f, 0.f};
       lds_signal(recorded + tri);
-      return;
-    }
+      if constexpr (!FUSED) {
+        report_expired(p.status, expired);
+        return;
+      }
+    } else {
     // Stream mst merges the others' records with its own registers in the
     // order mst, mst + 1, ... (fixed by the split's sub-tile count, so the
     // result does not depend on which stream finished first). The others
     // took the sub-tiles before its last one, so this wait is short, and it
     // always ends.
-    lds_wait_geq(recorded + tri, WT - 1);
+    lds_wait_geq(recorded + tri, WT - 1, p.wait_polls, expired);
     float ms[WT], ls[WT];
     ms[0] = m_run;
     ls[0] = l_run;
@@ -572,22 +834,33 @@ mlra_split_pc(SplitParams p) {
       l += ls[w] * wsc[w];
     }
     const int row = rb0 + row0 + n;
-    if (row >= p.rows) return;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t ri = (slotp * NBT + bo + b) * p.rows + row;
-    float* o = p.part_o + ri * DC + wd * DCW;
+    if (row < p.rows) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int64_t ri = (slotp * NBT + bo + b) * p.rows + row;
+      float* o = p.part_o + ri * DC + wd * DCW;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 v = f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} *
-                  wsc[0];
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v = f32x4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]} *
+                    wsc[0];
 #pragma unroll
-        for (int w = 1; w < WT; ++w) v += M[((w - 1) * REC + dt * 4 + q) * 64 + lane] * wsc[w];
-        *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
-      }
-    if (g == 0 && wd == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
+          for (int w = 1; w < WT; ++w) v += M[((w - 1) * REC + dt * 4 + q) * 64 + lane] * wsc[w];
+          *reinterpret_cast<f32x4*>(o + dt * 32 + 8 * q + 4 * g) = v * inv;
+        }
+      if (g == 0 && wd == 0) p.part_lse[ri] = l > 0.f ? (mm + __log2f(l)) * kLn2 : -INFINITY;
+    }
+    if constexpr (FUSED) {  // partial acknowledged by the L2 before the merge uses it
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_signal(stored);
+    }
+    }
   }
+  if constexpr (FUSED) {
+    const int nsplit = min((L + kBlock * p.tps - 1) / (kBlock * p.tps), p.spl);
+    fused_merge<NCW>(p, s, rr, per, nsplit, n_own, cw, lane, false, stored, go, godec, expired);
+  }
+  report_expired(p.status, expired);
 }
 
 // ---------------------------------------------------------------------------
@@ -927,72 +1200,80 @@ __global__ void __launch_bounds__(256) mlra_combine_cols(CombineParams c) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int NBW, int RT, int DC, int DR>
-static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
-                            hipStream_t stream) {
+template <int NBW, int RT, int DC, int DR, bool FUSED>
+static hipError_t launch_pc_as(const SplitParams& sp, const mlra_decode_plan& plan,
+                               hipStream_t stream) {
   constexpr int WD = pc_wd(DC);
   constexpr PcLds lay = pc_lds(NBW, RT, WD, DC, DR);
   constexpr int PL = pc_pl(NBW, DC, DR);
-  auto kern = mlra_split_pc<NBW, RT, WD, DC, DR, lay.nslot, PL>;
+  auto kern = mlra_split_pc<NBW, RT, WD, DC, DR, lay.nslot, PL, FUSED>;
   static std::atomic<unsigned long long> lds_allowed{0};  // per instance, per device
   const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lay.total, lds_allowed);
   if (e != hipSuccess) return e;
-  const dim3 grid = sp.nrt == 1
-                       ? dim3(plan.splits_per_seq, sp.S)
-                       : dim3((uint32_t)(((int64_t)sp.S * plan.splits_per_seq + 7) / 8 * 8 * sp.nrt));
+  const dim3 grid =
+      FUSED ? dim3((uint32_t)((int64_t)sp.S * plan.splits_per_seq * sp.nrt))
+            : (sp.nrt == 1 ? dim3(plan.splits_per_seq, sp.S)
+                           : dim3((uint32_t)(((int64_t)sp.S * plan.splits_per_seq + 7) / 8 * 8 * sp.nrt)));
   hipLaunchKernelGGL(kern, grid, dim3(512), lay.total, stream, sp);
   return hipGetLastError();
 }
 
+template <int NBW, int RT, int DC, int DR>
+static hipError_t launch_pc(const SplitParams& sp, const mlra_decode_plan& plan,
+                            hipStream_t stream, bool fused) {
+  return fused ? launch_pc_as<NBW, RT, DC, DR, true>(sp, plan, stream)
+               : launch_pc_as<NBW, RT, DC, DR, false>(sp, plan, stream);
+}
+
 template <int NBW, int RT, int DC>
-static hipError_t pc_dr(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
-  if (sp.DR == 64) return launch_pc<NBW, RT, DC, 64>(sp, plan, st);
-  if constexpr (DC <= 128) return launch_pc<NBW, RT, DC, 32>(sp, plan, st);
+static hipError_t pc_dr(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st, bool f) {
+  if (sp.DR == 64) return launch_pc<NBW, RT, DC, 64>(sp, plan, st, f);
+  if constexpr (DC <= 128) return launch_pc<NBW, RT, DC, 32>(sp, plan, st, f);
   return hipErrorInvalidValue;  // wide latents take the 64-wide RoPE key only
 }
 
 template <int NBW, int RT>
-static hipError_t pc_dc(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
-  if (sp.DC == 128) return pc_dr<NBW, RT, 128>(sp, plan, st);
-  if (sp.DC == 64) return pc_dr<NBW, RT, 64>(sp, plan, st);
+static hipError_t pc_dc(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st, bool f) {
+  if (sp.DC == 128) return pc_dr<NBW, RT, 128>(sp, plan, st, f);
+  if (sp.DC == 64) return pc_dr<NBW, RT, 64>(sp, plan, st, f);
   return hipErrorInvalidValue;
 }
 
 // (branches per workgroup, row tiles, latent width) as the planner chose them
-static hipError_t pc_nb(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st) {
+static hipError_t pc_nb(const SplitParams& sp, const mlra_decode_plan& plan, hipStream_t st, bool f) {
   const int nbw = pc_nbw(sp.NB, sp.rows, sp.DC), rt = pc_rt(sp.rows, sp.DC);
   if (sp.nrt != pc_groups(sp.NB, sp.rows, sp.DC)) return hipErrorInvalidValue;
   if (sp.DC == 512) {  // one branch, four slices
-    if (nbw == 1 && rt == 1 && sp.DR == 64) return launch_pc<1, 1, 512, 64>(sp, plan, st);
+    if (nbw == 1 && rt == 1 && sp.DR == 64) return launch_pc<1, 1, 512, 64>(sp, plan, st, f);
     return hipErrorInvalidValue;
   }
   if (sp.DC == 256) {  // two slices
     if (sp.DR != 64) return hipErrorInvalidValue;
-    if (rt == 1 && nbw == 1) return launch_pc<1, 1, 256, 64>(sp, plan, st);
-    if (rt == 1 && nbw == 2) return launch_pc<2, 1, 256, 64>(sp, plan, st);
-    if (rt == 2 && nbw == 1) return launch_pc<1, 2, 256, 64>(sp, plan, st);
+    if (rt == 1 && nbw == 1) return launch_pc<1, 1, 256, 64>(sp, plan, st, f);
+    if (rt == 1 && nbw == 2) return launch_pc<2, 1, 256, 64>(sp, plan, st, f);
+    if (rt == 2 && nbw == 1) return launch_pc<1, 2, 256, 64>(sp, plan, st, f);
     return hipErrorInvalidValue;
   }
   if (rt == 1) {
     switch (nbw) {
-      case 1: return pc_dc<1, 1>(sp, plan, st);
-      case 2: return pc_dc<2, 1>(sp, plan, st);
-      case 4: return pc_dc<4, 1>(sp, plan, st);
+      case 1: return pc_dc<1, 1>(sp, plan, st, f);
+      case 2: return pc_dc<2, 1>(sp, plan, st, f);
+      case 4: return pc_dc<4, 1>(sp, plan, st, f);
     }
   } else if (rt == 2) {
     switch (nbw) {
-      case 1: return pc_dc<1, 2>(sp, plan, st);
-      case 2: return pc_dc<2, 2>(sp, plan, st);
+      case 1: return pc_dc<1, 2>(sp, plan, st, f);
+      case 2: return pc_dc<2, 2>(sp, plan, st, f);
     }
   } else if (rt == 4 && nbw == 1) {
-    return pc_dc<1, 4>(sp, plan, st);
+    return pc_dc<1, 4>(sp, plan, st, f);
   }
   return hipErrorInvalidValue;
 }
 
 static hipError_t launch_split(const SplitParams& sp, const KernelShape& ks,
-                               const mlra_decode_plan& plan, hipStream_t st) {
-  if (ks.variant == kVariantPcBf16) return pc_nb(sp, plan, st);
+                               const mlra_decode_plan& plan, hipStream_t st, bool fused) {
+  if (ks.variant == kVariantPcBf16) return pc_nb(sp, plan, st, fused);
   dim3 grid(plan.splits_per_seq, sp.S, (sp.rows * sp.NB + 3) / 4);
   switch (sp.DC / 64) {
     case 1: hipLaunchKernelGGL(mlra_split_valu<1>, grid, dim3(256), 0, st, sp); break;
@@ -1027,6 +1308,16 @@ static void launch_combine(bool bf16, dim3 grid, const CombineParams& cp, hipStr
 }
 
 static int device_cus(int* out) { return device_cu_count(out); }
+
+// Process-wide bound of the split kernel's waits set by
+// mlra_testing_set_wait_limit (< 0: the defaults).
+static std::atomic<int> g_wait_limit{-1};
+
+// Zero the first `words` 16-byte words at p (grid-stride).
+__global__ void __launch_bounds__(256) zero_words(u32x4* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
 
 
 // Which kernels one call enqueues: the split kernel (partial results of
@@ -1066,9 +1357,12 @@ static mlra_status decode(int phases, const void* q_latent, const void* q_rope,
   if (!workspace || workspace_bytes < plan.workspace_bytes) return MLRA_ERR_WORKSPACE;
 
   const int64_t slots = (int64_t)r.S * plan.splits_per_seq * r.NB * r.rows;
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             ((slots * r.DC * 4 + 255) / 256) * 256);
+  char* const ws = static_cast<char*>(workspace);
+  float* part_o = reinterpret_cast<float*>(ws + kWsHeaderBytes);
+  float* part_lse = reinterpret_cast<float*>(ws + kWsHeaderBytes + ((slots * r.DC * 4 + 255) / 256) * 256);
+  // the split kernel merges the splits itself when the plan allows it and
+  // the call runs both halves
+  const bool fused = plan.fused_merge && phases == kBoth;
   SplitParams sp;
   sp.q_lat = q_latent;
   sp.q_rope = q_rope;
@@ -1098,9 +1392,26 @@ static mlra_status decode(int phases, const void* q_latent, const void* q_rope,
   sp.causal = r.causal;
   sp.nrt = ks.NRT;
   sp.score_scale = scale * kLog2e;
+  sp.status = reinterpret_cast<unsigned*>(ws);
+  sp.sync = reinterpret_cast<uint64_t*>(ws + kWsStatusBytes);
+  sp.out = out;
+  sp.lse = lse;
+  sp.concat = r.reduce == MLRA_BRANCH_CONCAT;
+  sp.out_rescale = out_rescale;
+  {
+    // Bounds of the in-kernel merge's waits, in 10 ns ticks. Short: 100 us
+    // plus twice the time a split's tiles take at 8 GB/s per CU (far more than
+    // any spread between workgroups of one sequence); long: 100 ms more.
+    const int64_t tile_bytes = (int64_t)kBlock * (r.NB * r.DC + r.DR) * 2;
+    sp.short_ticks = 10000 + 2 * (int64_t)plan.tiles_per_split * tile_bytes / 80;
+    sp.long_ticks = 10000000 + 10 * sp.short_ticks;
+    const int lim = g_wait_limit.load(std::memory_order_relaxed);
+    sp.wait_polls = lim >= 0 ? lim : kDefaultWaitPolls;
+    if (lim >= 0) sp.short_ticks = sp.long_ticks = lim;
+  }
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (do_split && launch_split(sp, ks, plan, hs) != hipSuccess) return MLRA_ERR_HIP;
-  if (!do_combine) return MLRA_OK;
+  if (do_split && launch_split(sp, ks, plan, hs, fused) != hipSuccess) return MLRA_ERR_HIP;
+  if (!do_combine || fused) return MLRA_OK;
 
   CombineParams cp;
   cp.part_o = part_o;
@@ -1203,6 +1514,39 @@ extern "C" mlra_status mlra_decode_partials(const void* q_latent, const void* q_
   return mlra::decode(mlra::kPartials, q_latent, q_rope, latent_cache, rope_cache, block_table,
                       seq_lens, n_branch, scale, 1.0f, nullptr, nullptr, dims, workspace,
                       workspace_bytes, stream);
+}
+
+extern "C" mlra_status mlra_decode_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace) return MLRA_ERR_NULL_PTR;
+  if (bytes < (size_t)mlra::kWsHeaderBytes) return MLRA_ERR_WORKSPACE;
+  if (!mlra::aligned16(workspace)) return MLRA_ERR_ALIGNMENT;
+  const int64_t words = mlra::kWsHeaderBytes / 16;
+  hipLaunchKernelGGL(mlra::zero_words, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<mlra::u32x4*>(workspace), words);
+  return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
+}
+
+extern "C" mlra_status mlra_decode_read_status(void* workspace, uint32_t* bits, int32_t clear,
+                                               void* stream) {
+  if (!workspace || !bits) return MLRA_ERR_NULL_PTR;
+  if (!mlra::aligned16(workspace)) return MLRA_ERR_ALIGNMENT;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, hs) != hipSuccess ||
+      hipStreamSynchronize(hs) != hipSuccess)
+    return MLRA_ERR_HIP;
+  if (clear) {  // the status word's 16-byte word only
+    hipLaunchKernelGGL(mlra::zero_words, dim3(1), dim3(256), 0, hs,
+                       static_cast<mlra::u32x4*>(workspace), (int64_t)1);
+    if (hipGetLastError() != hipSuccess) return MLRA_ERR_HIP;
+  }
+  *bits = v;
+  return MLRA_OK;
+}
+
+extern "C" mlra_status mlra_testing_set_wait_limit(int32_t polls) {
+  mlra::g_wait_limit.store(polls < 0 ? -1 : polls, std::memory_order_relaxed);
+  return MLRA_OK;
 }
 
 extern "C" mlra_status mlra_decode_combine(const int32_t* seq_lens, int32_t n_branch,

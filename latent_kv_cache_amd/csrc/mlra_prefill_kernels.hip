@@ -617,7 +617,10 @@ mlra_status prefill_plan(const Resolved& r, int32_t num_cus, int32_t num_splits,
   p.row_groups = (int32_t)RT;
   if (!dir) {
     const int64_t slots = (int64_t)r.S * spl * r.NB * r.rows;
-    p.workspace_bytes = (size_t)(pf_cdiv(slots * r.DC * 4, 256) * 256 + pf_cdiv(slots * 4, 256) * 256);
+    // after the header every workspace of the library starts with (it belongs
+    // to decode calls, so one buffer can serve both)
+    p.workspace_bytes = (size_t)(kWsHeaderBytes + pf_cdiv(slots * r.DC * 4, 256) * 256 +
+                                 pf_cdiv(slots * 4, 256) * 256);
   }
   *plan = p;
   *direct = dir;
@@ -699,10 +702,9 @@ extern "C" mlra_status mlra_prefill_attention(const void* q_latent, const void* 
   pp.seq_lens = seq_lens;
   pp.out = static_cast<__bf16*>(out);
   pp.lse = lse;
-  pp.part_o = direct ? nullptr : static_cast<float*>(workspace);
-  pp.part_lse = direct ? nullptr
-                       : reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                  pf_cdiv(slots * r.DC * 4, 256) * 256);
+  char* const wsp = direct ? nullptr : static_cast<char*>(workspace) + kWsHeaderBytes;  // past the header
+  pp.part_o = direct ? nullptr : reinterpret_cast<float*>(wsp);
+  pp.part_lse = direct ? nullptr : reinterpret_cast<float*>(wsp + pf_cdiv(slots * r.DC * 4, 256) * 256);
   pp.lsb = r.lsb;
   pp.lst = r.lst;
   pp.lsbr = r.lsbr;

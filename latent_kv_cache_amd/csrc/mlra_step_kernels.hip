@@ -346,7 +346,9 @@ extern "C" mlra_status mlra_out_projection_workspace_size(int32_t m, int32_t k, 
   if (m < 1 || k < 1 || d < 1) return MLRA_ERR_BAD_DIMS;
   if (m > mlra::kOpMaxM || k % 512 || d % 128) return MLRA_ERR_UNSUPPORTED;
   const int kc = mlra::outproj_kc(k, d);
-  *bytes = kc > 1 ? (size_t)kc * m * d * 4 : 0;
+  // K-chunk partials after the header every workspace of the library starts
+  // with (it belongs to decode calls, so one buffer can serve both)
+  *bytes = kc > 1 ? (size_t)mlra::kWsHeaderBytes + (size_t)kc * m * d * 4 : 0;
   return MLRA_OK;
 }
 
@@ -365,7 +367,8 @@ extern "C" mlra_status mlra_out_projection(const void* x, const void* w_packed, 
   p.x = static_cast<const __bf16*>(x);
   p.wp = static_cast<const __bf16*>(w_packed);
   p.y = static_cast<__bf16*>(y);
-  p.part = static_cast<float*>(workspace);
+  p.part = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + mlra::kWsHeaderBytes)
+                    : nullptr;
   p.M = m;
   p.K = k;
   p.D = d;

@@ -52,7 +52,7 @@ def test_struct_layouts_match_header():
     # int32 x 14 then int64 x 6; the plan ends with a size_t.
     assert ctypes.sizeof(_lib.DecodeDims) == 14 * 4 + 6 * 8
     assert _lib.DecodeDims.latent_stride_block.offset == 56
-    assert ctypes.sizeof(_lib.DecodePlan) == 8 * 4 + 8
+    assert ctypes.sizeof(_lib.DecodePlan) == 10 * 4 + 8
 
 
 def test_status_strings_and_version(lib):
@@ -127,7 +127,7 @@ def test_ragged_hint_balances_splits(lib):
     ("num_seqs", 0, 2), ("q_len", 5, 3), ("num_heads", 65, 3), ("d_latent", 96, 3),
     ("d_rope", 48, 3), ("block_size", 32, 3), ("block_size", 0, 2), ("max_blocks_per_seq", 0, 2),
     ("max_seq_len", 10 ** 6, 2), ("max_seq_len", -1, 2), ("num_splits", -2, 2), ("dtype", 7, 2),
-    ("reduce", 2, 2), ("reserved", 1, 2), ("latent_stride_block", 1000, 2),
+    ("reduce", 2, 2), ("flags", 2, 2), ("flags", -1, 2), ("latent_stride_block", 1000, 2),
     ("latent_stride_token", 516, 5), ("rope_stride_block", 60, 2), ("sum_seq_lens", -1, 2),
     ("num_seqs", 70000, 3),
 ])
@@ -232,7 +232,8 @@ def test_cache_append_validates_before_touching_memory(lib):
 def test_out_projection_validation(lib):
     n = ctypes.c_size_t(123)
     assert lib.mlra_out_projection_workspace_size(16, 4096, 4096, ctypes.byref(n)) == 0
-    assert n.value == 8 * 16 * 4096 * 4          # eight K-chunks of float32 partials
+    # the header every workspace starts with, then eight K-chunks of float32 partials
+    assert n.value == _lib.MLRA_DECODE_WS_HEADER_BYTES + 8 * 16 * 4096 * 4
     assert lib.mlra_out_projection_workspace_size(0, 512, 128, ctypes.byref(n)) == 2
     for m, k, d in ((129, 512, 128), (16, 768, 128), (16, 512, 96)):  # M, K or D off the grid
         assert lib.mlra_out_projection_workspace_size(m, k, d, ctypes.byref(n)) == 3
@@ -301,7 +302,7 @@ def test_prefill_plan_splits_only_when_rows_leave_cus_idle(lib):
 @pytest.mark.parametrize("field,value,status", [
     ("q_len", 0, 2), ("num_heads", 0, 2), ("dtype", _lib.MLRA_FP32, 3), ("d_latent", 256, 3),
     ("d_latent", 96, 3), ("d_rope", 48, 3), ("block_size", 32, 3), ("num_seqs", 0, 2),
-    ("max_seq_len", -1, 2), ("reserved", 1, 2),
+    ("max_seq_len", -1, 2), ("flags", 2, 2),
 ])
 def test_prefill_rejects_bad_dims(lib, field, value, status):
     d = _dims(configs.MLRA4_TP_PREFILL, **{field: value})
@@ -335,3 +336,36 @@ def test_prefill_rejects_too_many_rows_and_bad_pointers(lib):
     st = lib.mlra_prefill_attention(16, 16, 16, 16, 16, 16, 1, 0.1, 0.5, 24, 16,
                                     ctypes.byref(d), None, 0, None)
     assert st == 5
+
+
+@pytest.mark.parametrize("cfg,nb,kw,fused", [
+    (configs.MLRA4_TP_SHARE, 1, {"flags": 1}, 1),             # B=16, T=8192: 16 splits x 16
+    (configs.MLRA4_FUSED, 4, {"flags": 1}, 1),                # B=32, four branches
+    (configs.MLA_COMPARE, 1, {"flags": 1}, 1),
+    (configs.MLRA4_TP_SHARE, 1, {}, 0),                       # not asked for
+    (configs.MLRA4_TP_SHARE.with_(num_seqs=12), 1, {"flags": 1}, 0),    # not a multiple of 8
+    (configs.LONG_CONTEXT, 4, {"flags": 1}, 0),                         # 4 sequences
+    (configs.RAGGED_Q2, 4, {"flags": 1, "sum_seq_lens": 64 * 16896}, 0),  # ragged hint
+    (configs.MLRA4_TP_SHARE.with_(num_seqs=128, context=512), 1, {"flags": 1}, 0),  # > 64 seqs
+])
+def test_plan_chooses_the_in_kernel_merge(lib, cfg, nb, kw, fused):
+    d = _dims(cfg, **kw)
+    st, p = _plan(lib, d, nb)
+    assert st == 0
+    assert p.fused_merge == fused
+    if fused:  # one round of one workgroup per CU, a sequence's workgroups on one XCD
+        per = p.splits_per_seq * p.row_groups
+        assert cfg.num_seqs % 8 == 0 and cfg.num_seqs * per <= 256 and per <= 32
+    rows = cfg.num_heads * cfg.q_len
+    slots = cfg.num_seqs * p.splits_per_seq * nb * rows
+    assert p.workspace_bytes >= _lib.MLRA_DECODE_WS_HEADER_BYTES + slots * (cfg.d_latent + 1) * 4
+
+
+def test_status_and_workspace_init_validate_without_a_gpu(lib):
+    bits = ctypes.c_uint32(0)
+    assert lib.mlra_decode_read_status(None, ctypes.byref(bits), 0, None) == 1
+    assert lib.mlra_decode_read_status(24, ctypes.byref(bits), 0, None) == 5
+    assert lib.mlra_decode_workspace_init(None, 1 << 20, None) == 1
+    assert lib.mlra_decode_workspace_init(16, 100, None) == 4
+    assert lib.mlra_decode_workspace_init(24, 1 << 20, None) == 5
+    assert lib.mlra_testing_set_wait_limit(-1) == 0

@@ -1,10 +1,14 @@
 """Compile-time resource checks of the HIP kernels (CPU only: hipcc cross-compiles gfx950).
 
 The split kernels keep several 32-token sub-tiles of loads in flight per wave
-and wait for each with a partial vector-memory count; a register spill would
-add scratch loads to that count and serialise the pipeline. Every kernel must
-therefore compile without spills, and the loader/compute kernel must fit two
-waves per SIMD (at most 256 VGPRs).
+and wait for each with a partial vector-memory count; a register spill to
+scratch memory would add scratch loads to that count and serialise the
+pipeline. Every kernel must therefore compile without vector-register spills
+and without scratch memory, and the loader/compute kernel must fit two waves
+per SIMD (at most 256 VGPRs). Scalar registers may spill only in the split
+kernel's in-kernel-merge instances, and only into lanes of vector registers
+(no scratch): their merge epilogue runs once per workgroup after the
+streaming loops, and the spill code sits at kernel entry and in that epilogue.
 """
 import os
 import re
@@ -38,7 +42,8 @@ def remarks():
             name = m.group(1)
             kernels[name] = {}
             continue
-        m = re.search(r"remark:\s+(VGPRs|AGPRs|VGPRs Spill|SGPRs Spill|Occupancy \[waves/SIMD\]): (\d+)", line)
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|VGPRs Spill|SGPRs Spill|ScratchSize \[bytes/lane\]|"
+                      r"Occupancy \[waves/SIMD\]): (\d+)", line)
         if m and name:
             kernels[name][m.group(1)] = int(m.group(2))
     return kernels
@@ -52,9 +57,18 @@ def test_every_kernel_is_reported(remarks):
         assert kern in names
 
 
+def _in_kernel_merge(name):
+    # mlra_split_pc<..., bool FUSED = true>: the mangled name ends its
+    # template arguments with Lb1E
+    return "mlra_split_pc" in name and "Lb1EE" in name
+
+
 def test_no_kernel_spills(remarks):
-    spilled = {k: v for k, v in remarks.items() if v.get("VGPRs Spill", 0) or v.get("SGPRs Spill", 0)}
+    spilled = {k: v for k, v in remarks.items()
+               if v.get("VGPRs Spill", 0) or v.get("ScratchSize [bytes/lane]", 0)
+               or (v.get("SGPRs Spill", 0) and not _in_kernel_merge(k))}
     assert not spilled, spilled
+    assert any(_in_kernel_merge(k) for k in remarks)
 
 
 def test_loader_compute_kernel_runs_two_waves_per_simd(remarks):

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from latent_kv_cache_amd import api, configs
+from latent_kv_cache_amd import _lib, api, configs
 from latent_kv_cache_amd.inputs import make_inputs, to_device
 from oracle import mlra_decode
 
@@ -95,7 +95,7 @@ def test_small_shapes_every_instance(nb, dc, dr, h, q):
         assert_parity(out, lse, ro, rl)
 
 
-@pytest.mark.parametrize("cfg", configs.ALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", configs.ALL + [configs.MLRA4_TP_SHARE_Q4], ids=lambda c: c.name)
 def test_full_size_workloads(cfg):
     _say(f"full {cfg.name}")
     inp = make_inputs(cfg)
@@ -159,7 +159,8 @@ def test_single_sequence_million_token_context_sampled_heads(cfg):
 
 
 def test_fp32_path_small_shapes():
-    for nb, dc, dr, q in ((1, 256, 64, 2), (2, 512, 32, 1), (4, 64, 32, 2)):
+    for nb, dc, dr, q in ((1, 256, 64, 2), (2, 512, 32, 1), (4, 64, 32, 2), (2, 128, 64, 3),
+                          (1, 64, 32, 4)):
         cfg = _cfg(dtype="fp32", n_branch=nb, d_latent=dc, d_rope=dr, q_len=q, num_heads=5,
                    context_range=(1, 300), seed=dc + nb)
         inp = make_inputs(cfg)
@@ -289,7 +290,10 @@ def test_workspace_contents_are_never_read_before_written(num_splits):
     ro, rl = oracle(inp)
     results = []
     for fill in (float("nan"), float("inf"), -float("inf")):
+        # the header (status word, merge counters) starts at zero; everything
+        # after it is poisoned
         ws = torch.full((nbytes // 4,), fill, dtype=torch.float32, device="cuda")
+        ws[: _lib.MLRA_DECODE_WS_HEADER_BYTES // 4] = 0
         _say(f"poisoned workspace {fill} num_splits={num_splits}")
         o, l = api.mlra_decode_attention(*args, cfg.scale, cfg.out_rescale, workspace=ws, **kw)
         torch.cuda.synchronize()
