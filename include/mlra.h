@@ -224,6 +224,30 @@ mlra_status mlra_decode_attention(const void* q_latent, const void* q_rope,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mlra_decode_attention with the library's own device scratch in place of a
+ * workspace. Same arguments, results and errors as mlra_decode_attention,
+ * minus workspace and workspace_bytes. The scratch is a fixed array of
+ * MLRA_STATIC_SCRATCH_BYTES in the library's code object: every GPU that
+ * loads the library holds one, zero-filled, until the process ends; the
+ * call allocates nothing and frees nothing. A call whose plan needs more
+ * (mlra_decode_make_plan's workspace_bytes) returns MLRA_ERR_WORKSPACE
+ * before enqueuing anything. All calls on one GPU share its scratch, which
+ * keeps the last call's contents (the header is left ready for the next
+ * call): calls that overlap on one GPU (other streams, other host threads)
+ * race and must not be issued.
+ */
+#define MLRA_STATIC_SCRATCH_BYTES (64u << 20)
+
+mlra_status mlra_decode_attention_static(const void* q_latent, const void* q_rope,
+                                         const void* latent_cache, const void* rope_cache,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         int32_t n_branch, float scale, float out_rescale,
+                                         void* out, float* lse, const mlra_decode_dims* dims,
+                                         void* stream);
+
+/*
  * MLA-shaped comparison call: a single latent head (n_branch = 1, typically
  * DC = 512 plus DR = 64, the 4.5*dh per-token load the blog attributes to MLA),
  * one softmax, out_rescale = 1. Same argument rules as mlra_decode_attention;

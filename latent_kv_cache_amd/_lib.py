@@ -17,6 +17,7 @@ MLRA_BRANCH_SUM, MLRA_BRANCH_CONCAT = 0, 1
 MLRA_DECODE_WS_HEADER_BYTES = 65792          # zero before a decode workspace's first use
 MLRA_DECODE_FLAG_FUSED_MERGE = 1
 MLRA_DEVSTATUS_WAIT_EXPIRED, MLRA_DEVSTATUS_MERGE_FAILED = 1, 2
+MLRA_STATIC_SCRATCH_BYTES = 64 << 20   # scratch of mlra_decode_attention_static
 
 STATUS_NAMES = {0: "MLRA_OK", 1: "MLRA_ERR_NULL_PTR", 2: "MLRA_ERR_BAD_DIMS",
                 3: "MLRA_ERR_UNSUPPORTED", 4: "MLRA_ERR_WORKSPACE", 5: "MLRA_ERR_ALIGNMENT",
@@ -24,6 +25,7 @@ STATUS_NAMES = {0: "MLRA_OK", 1: "MLRA_ERR_NULL_PTR", 2: "MLRA_ERR_BAD_DIMS",
 
 # Functions include/mlra.h declares (checked against the header by the tests).
 EXPORTS = ("mlra_decode_make_plan", "mlra_decode_workspace_size", "mlra_decode_attention",
+           "mlra_decode_attention_static",
            "mla_decode_attention", "mlra_decode_partials", "mlra_decode_combine",
            "mlra_cache_append", "mlra_out_projection_pack", "mlra_out_projection_workspace_size",
            "mlra_out_projection", "mlra_prefill_make_plan", "mlra_prefill_workspace_size",
@@ -90,6 +92,9 @@ def load() -> ctypes.CDLL:
         lib.mlra_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, f32, f32, vp, vp,
                                               dims_p, vp, sz, vp]
         lib.mlra_decode_attention.restype = i32
+        lib.mlra_decode_attention_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, f32, f32, vp,
+                                                     vp, dims_p, vp]
+        lib.mlra_decode_attention_static.restype = i32
         lib.mla_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, vp, dims_p, vp,
                                              sz, vp]
         lib.mla_decode_attention.restype = i32

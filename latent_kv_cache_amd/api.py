@@ -319,6 +319,34 @@ def mlra_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
                  sum_seq_lens, out, lse, workspace, stream, fused_merge)
 
 
+def mlra_decode_attention_static(q_latent: torch.Tensor, q_rope: torch.Tensor,
+                                 latent_cache: torch.Tensor, rope_cache: torch.Tensor,
+                                 block_table: torch.Tensor, seq_lens: torch.Tensor, n_branch: int,
+                                 scale: float, out_rescale: float, *, out: torch.Tensor,
+                                 lse: torch.Tensor, max_seq_len: int, reduce: str = "sum",
+                                 causal: bool = True, num_splits: int = 0, sum_seq_lens: int = 0,
+                                 stream: Optional[int] = None,
+                                 fused_merge: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mlra_decode_attention on the library's own device scratch: no
+    workspace, and nothing allocated (out and lse are the caller's), e.g. for
+    code under graph capture; calls on one GPU must not overlap
+    (include/mlra.h)."""
+    lib = _lib.load()
+    if q_latent.dim() != 5 or q_latent.shape[3] != n_branch:
+        raise ValueError("q_latent must be [S][Q][H][n_branch][DC]")
+    dims = make_dims(q_latent, q_rope, latent_cache, rope_cache, block_table,
+                     max_seq_len=max_seq_len, reduce=reduce, causal=causal,
+                     num_splits=num_splits, sum_seq_lens=sum_seq_lens, fused_merge=fused_merge)
+    if stream is None:
+        stream = torch.cuda.current_stream(q_latent.device).cuda_stream
+    _lib.check(lib.mlra_decode_attention_static(
+        q_latent.data_ptr(), q_rope.data_ptr(), latent_cache.data_ptr(), rope_cache.data_ptr(),
+        block_table.data_ptr(), seq_lens.data_ptr(), int(n_branch), float(scale),
+        float(out_rescale), out.data_ptr(), lse.data_ptr(), dims, stream),
+        "mlra_decode_attention_static")
+    return out, lse
+
+
 def mlra_prefill_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
                            latent_cache: torch.Tensor, rope_cache: torch.Tensor,
                            block_table: torch.Tensor, seq_lens: torch.Tensor, n_branch: int,

@@ -1516,6 +1516,60 @@ extern "C" mlra_status mlra_decode_partials(const void* q_latent, const void* q_
                       workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free entry point: the library's own device scratch
+// ---------------------------------------------------------------------------
+namespace mlra {
+// Device scratch of mlra_decode_attention_static, zero when the code object
+// is loaded (its header must start at zero), one copy per device that loads
+// the library. Host code never uses this name as an address: each device's
+// address comes from hipGetSymbolAddress (below).
+constexpr size_t kStaticScratchBytes = (size_t)MLRA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; devices past 63 look it up on
+// every call. Concurrent first calls store the same address.
+static mlra_status static_scratch(void** ptr) {
+  static std::atomic<void*> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLRA_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    void* p = cache[dev].load(std::memory_order_acquire);
+    if (p) {
+      *ptr = p;
+      return MLRA_OK;
+    }
+  }
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLRA_ERR_HIP;
+  if (dev >= 0 && dev < 64) cache[dev].store(p, std::memory_order_release);
+  *ptr = p;
+  return MLRA_OK;
+}
+}  // namespace mlra
+
+extern "C" mlra_status mlra_decode_attention_static(const void* q_latent, const void* q_rope,
+                                                    const void* latent_cache,
+                                                    const void* rope_cache,
+                                                    const int32_t* block_table,
+                                                    const int32_t* seq_lens, int32_t n_branch,
+                                                    float scale, float out_rescale, void* out,
+                                                    float* lse, const mlra_decode_dims* dims,
+                                                    void* stream) {
+  // the plan's workspace must fit the scratch (host-side, before any device work)
+  mlra_decode_plan plan;
+  mlra_status st = mlra_decode_make_plan(dims, n_branch, 0, &plan);
+  if (st != MLRA_OK) return st;
+  if (plan.workspace_bytes > mlra::kStaticScratchBytes) return MLRA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = mlra::static_scratch(&ws);
+  if (st != MLRA_OK) return st;
+  return mlra::decode(mlra::kBoth, q_latent, q_rope, latent_cache, rope_cache, block_table,
+                      seq_lens, n_branch, scale, out_rescale, out, lse, dims, ws,
+                      mlra::kStaticScratchBytes, stream);
+}
+
 extern "C" mlra_status mlra_decode_workspace_init(void* workspace, size_t bytes, void* stream) {
   if (!workspace) return MLRA_ERR_NULL_PTR;
   if (bytes < (size_t)mlra::kWsHeaderBytes) return MLRA_ERR_WORKSPACE;
