@@ -492,6 +492,43 @@ def copy_calibration(torch, mib: int, steps: int, warmup: int) -> int:
 
 DEFAULT_WORKLOAD = "mlra4_tp_share_b16_t8192"
 
+CEILING_BUFFER = 2 << 30  # bytes streamed by the 2 GB read, and rotated through by the small one
+
+
+def read_ceiling(torch, lib, nbytes: int, workgroups: int, steps: int, timed) -> dict:
+    """Streaming-read ceiling in the same run (mlra_stream_read, a plain HIP
+    read kernel): nbytes per launch with `workgroups` workgroups of 512
+    threads, launches rotating through a 2 GB buffer so that none finds its
+    bytes in the 256 MB Infinity Cache; then one 2 GB read per launch."""
+    dev = torch.device("cuda:0")
+    buf = torch.empty(CEILING_BUFFER, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(max(workgroups, 2048), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    unit = 16 * workgroups
+    n = max(unit, nbytes // unit * unit)
+    slots = CEILING_BUFFER // n
+
+    def small(i):
+        _check_status(lib.mlra_stream_read(buf.data_ptr() + (i % slots) * n, n, workgroups,
+                                           sink.data_ptr(), stream))
+
+    def big(i):
+        _check_status(lib.mlra_stream_read(buf.data_ptr(), CEILING_BUFFER, 2048, sink.data_ptr(),
+                                           stream))
+
+    ms_small = timed(small)
+    ms_big = timed(big, min(steps, 20))
+    del buf
+    return {"at_split_shape_gbs": round(n / (ms_small * 1e-3) / 1e9, 1), "workgroups": workgroups,
+            "bytes": n, "us": round(ms_small * 1e3, 3),
+            "gbs_2gb": round(CEILING_BUFFER / (ms_big * 1e-3) / 1e9, 1)}
+
+
+def _check_status(st: int) -> None:
+    if st != 0:
+        raise RuntimeError(f"mlra_stream_read failed with status {st}")
+
 
 def main() -> int:
     ap = argparse.ArgumentParser()
@@ -616,21 +653,25 @@ def main() -> int:
     # (K split-kernel launches, then K combine launches over the last
     # partials), each run bracketed by two events on the launch stream; an
     # event between every two kernels would itself add about 1.5 us per event.
-    def timed(fn):
+    def timed(fn, n=None):
+        n = n or args.steps
         torch.cuda.synchronize()
         head_start()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for i in range(args.steps):
+        for i in range(n):
             fn(i)
         b.record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
+        return a.elapsed_time(b) / n
 
     split_avg = timed(lambda i: prep.partials(tables[i % copies]))
     comb_avg = timed(lambda i: prep.combine())
     split_bytes = ab["total"] - ab["out"] - ab["lse"]
     split_gbs = split_bytes / (split_avg * 1e-3) / 1e9
+    # the same-run ceiling: a plain read of the split kernel's bytes with one
+    # 512-thread workgroup per CU (its launch shape), and a 2 GB read
+    ceiling = read_ceiling(torch, api._lib.load(), split_bytes, plan.num_cus, args.steps, timed)
 
     # per-step events (a separate pass) for the median step time
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -674,6 +715,9 @@ def main() -> int:
         "kernels": {"split_avg_us": round(split_avg * 1e3, 3),
                     "combine_avg_us": round(comb_avg * 1e3, 3),
                     "split_algorithmic_bytes": split_bytes},
+        "read_ceiling": ceiling,
+        "pct_of_read_ceiling": round(100 * gbs / ceiling["at_split_shape_gbs"], 2),
+        "split_pct_of_read_ceiling": round(100 * split_gbs / ceiling["at_split_shape_gbs"], 2),
         "roofline": {"bound": "hbm", "kernel": split_kernel, "achieved": round(split_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},

@@ -413,6 +413,19 @@ mlra_status mlra_prefill_attention(const void* q_latent, const void* q_rope,
                                    void* out, float* lse, const mlra_decode_dims* dims,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement helper, not part of the attention path: read `bytes` bytes
+ * from src with `workgroups` workgroups of 512 threads (each a contiguous
+ * chunk of bytes / workgroups, 16 bytes per lane per load, 8 loads per lane
+ * in flight), folding them so that no load is dropped; sink[workgroups]
+ * (uint32) is written only for one data pattern in 2^32. bench.py times it
+ * in the same run as the decode kernels, at their launch shape, as the
+ * streaming-read ceiling they are compared with. bytes must be a multiple
+ * of 16 * workgroups; src 16-byte aligned. Asynchronous on stream.
+ */
+mlra_status mlra_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
+                             void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* mlra_status_string(mlra_status status);
 

@@ -30,7 +30,7 @@ EXPORTS = ("mlra_decode_make_plan", "mlra_decode_workspace_size", "mlra_decode_a
            "mlra_cache_append", "mlra_out_projection_pack", "mlra_out_projection_workspace_size",
            "mlra_out_projection", "mlra_prefill_make_plan", "mlra_prefill_workspace_size",
            "mlra_prefill_attention", "mlra_decode_workspace_init", "mlra_decode_read_status",
-           "mlra_testing_set_wait_limit", "mlra_status_string", "mlra_version")
+           "mlra_testing_set_wait_limit", "mlra_stream_read", "mlra_status_string", "mlra_version")
 
 
 class DecodeDims(ctypes.Structure):
@@ -121,6 +121,8 @@ def load() -> ctypes.CDLL:
         lib.mlra_decode_workspace_init.restype = i32
         lib.mlra_decode_read_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), i32, vp]
         lib.mlra_decode_read_status.restype = i32
+        lib.mlra_stream_read.argtypes = [vp, sz, i32, vp, vp]
+        lib.mlra_stream_read.restype = i32
         lib.mlra_testing_set_wait_limit.argtypes = [i32]
         lib.mlra_testing_set_wait_limit.restype = i32
         lib.mlra_status_string.argtypes = [i32]
