@@ -638,83 +638,60 @@ mlra_split_pc(SplitParams p) {
     const int a_r = (n * RP + wd * RCHW + g * (RCHW / 2)) * 16 + NBW * LAT_B;
     const int a_t = b * LAT_B + (4 * (lane >> 5) + ((lane & 15) >> 2)) * LP * 16 +
                     (wd * DCW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-    for (int j = strm; j < nsub; j += WT) {
-      const int slot = j % NSLOT;
-      lds_wait_geq(ready + slot, (j / NSLOT + 1) * 4, p.wait_polls, expired);
-      const unsigned char* sb = smem + slot * lay.slot_bytes;
-      const int tb = (t0 + (j >> 1)) * kBlock + (j & 1) * kSub;
-      // LDS reads are batched ahead of the MFMAs that use them: the score
-      // operands (A = slot rows) first, then the C^T operands of P.C
-      // (transpose reads) in two halves slotted between the score MFMAs. LDS
-      // returns in order, so each MFMA waits only for its own operand, and at
-      // most 15 reads are outstanding past any wait (the counter's limit;
-      // beyond it the wait would be for every read).
-      bf16x8 aR[NR], aL[NL], aT[2][NDT];
-      auto read_t = [&](int h2) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const i16x4 lo = lds_read_tr(sb + a_t + (16 * h2) * LP * 16 + dt * 64);
-          const i16x4 hi = lds_read_tr(sb + a_t + (16 * h2 + 8) * LP * 16 + dt * 64);
-          aT[h2][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-      };
+    // Pieces of a sub-tile's work, shared by both loop forms below.
+    bf16x8 aR[NR], aL[NL], aT[2][NDT];
+    auto slot_at = [&](int j) { return smem + (j % NSLOT) * lay.slot_bytes; };
+    auto wait_ready = [&](int j) {
+      lds_wait_geq(ready + j % NSLOT, (j / NSLOT + 1) * 4, p.wait_polls, expired);
+    };
+    auto read_a = [&](const unsigned char* sb) {  // score operands (A = slot rows)
 #pragma unroll
       for (int st = 0; st < NR; ++st) aR[st] = rd16(sb + a_r + st * 16);
 #pragma unroll
       for (int st = 0; st < NL; ++st) aL[st] = rd16(sb + a_l + st * 16);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 sc = f32x16{}, sd = f32x16{};
+    };
+    auto read_t = [&](const unsigned char* sb, int h2) {  // C^T operands of P . C
 #pragma unroll
-      for (int st = 0; st < NR; ++st) sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qR[st], sd, 0, 0, 0);
-      read_t(0);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < NL; ++st) {
-        if (st % 2 == 0)
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[st], sc, 0, 0, 0);
-        else
-          sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[st], sd, 0, 0, 0);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const i16x4 lo = lds_read_tr(sb + a_t + (16 * h2) * LP * 16 + dt * 64);
+        const i16x4 hi = lds_read_tr(sb + a_t + (16 * h2 + 8) * LP * 16 + dt * 64);
+        aT[h2][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-      read_t(1);
-      __builtin_amdgcn_sched_barrier(0);
-      // every read of the slot is issued: hand it back once they complete
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      lds_signal(consumed + slot);
-      sc += sd;
-      if constexpr (WD > 1) {
-        // The WD waves of a (branch, row tile) pair hold partial scores over
-        // their slices: each leaves its part in the exchange area (double
-        // buffered by the stream's sub-tile parity), and all of them add the
-        // WD parts in slice order, so they hold bit-identical scores and take
-        // the same softmax decisions. A part is overwritten two sub-tiles
-        // later, after its readers have signalled the sub-tile in between.
-        const int u = j / WT;  // this stream's sub-tile count
-        f32x4* const X = reinterpret_cast<f32x4*>(smem + lay.xchg) + (u & 1) * 4 * 4 * 64;
+    };
+    // The WD waves of a (branch, row tile) pair hold partial scores over
+    // their slices: each leaves its part in the exchange area (double
+    // buffered by the stream's sub-tile parity), and all of them add the WD
+    // parts in slice order, so they hold bit-identical scores and take the
+    // same softmax decisions. A part is overwritten two sub-tiles later,
+    // after its readers have signalled the sub-tile in between.
+    auto exchange = [&](int u, f32x16 sc) {
+      f32x4* const X = reinterpret_cast<f32x4*>(smem + lay.xchg) + (u & 1) * 4 * 4 * 64;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          X[(cw * 4 + q) * 64 + lane] = f32x4{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
-        lds_signal(exchanged + cw);
+      for (int q = 0; q < 4; ++q)
+        X[(cw * 4 + q) * 64 + lane] = f32x4{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
+      lds_signal(exchanged + cw);
 #pragma unroll
-        for (int w = 0; w < WD; ++w)
-          if (w != wd) lds_wait_geq(exchanged + cw - wd + w, u + 1, p.wait_polls, expired);
-        f32x16 tot = f32x16{};
+      for (int w = 0; w < WD; ++w)
+        if (w != wd) lds_wait_geq(exchanged + cw - wd + w, u + 1, p.wait_polls, expired);
+      f32x16 tot = f32x16{};
 #pragma unroll
-        for (int w = 0; w < WD; ++w) {
-          f32x16 part = sc;
-          if (w != wd) {
+      for (int w = 0; w < WD; ++w) {
+        f32x16 part = sc;
+        if (w != wd) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 v = X[((cw - wd + w) * 4 + q) * 64 + lane];
-              part[4 * q] = v[0];
-              part[4 * q + 1] = v[1];
-              part[4 * q + 2] = v[2];
-              part[4 * q + 3] = v[3];
-            }
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = X[((cw - wd + w) * 4 + q) * 64 + lane];
+            part[4 * q] = v[0];
+            part[4 * q + 1] = v[1];
+            part[4 * q + 2] = v[2];
+            part[4 * q + 3] = v[3];
           }
-          tot = w == 0 ? part : tot + part;
         }
-        sc = tot;
+        tot = w == 0 ? part : tot + part;
       }
+      return tot;
+    };
+    auto mask = [&](f32x16& sc, int tb) {
       if (tb + kSub > min_vis) {  // uniform
         // element r holds token tb + 4g + 8(r/4) + r%4: compare the constant
         // part against a per-lane limit
@@ -722,25 +699,22 @@ mlra_split_pc(SplitParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[r] = 8 * (r >> 2) + (r & 3) < lim ? sc[r] : -INFINITY;
       }
-      // online softmax against a lazily moved reference maximum: rescale only
-      // when a row maximum exceeds it by more than kLazyLog2 (log2 units)
+    };
+    // Online softmax against a lazily moved reference maximum: the reference
+    // moves only when a row maximum exceeds it by more than kLazyLog2 (log2
+    // units). Returns whether any lane moved it with a running sum behind it
+    // (then O must be scaled by alpha before this sub-tile's P . C).
+    auto softmax = [&](const f32x16& sc, bf16x8 (&pB)[2], float& alpha) {
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
       mx = wave_max_halves(mx) * p.score_scale;
       const bool first = m_run == -INFINITY;
       const bool grow = first ? mx > -INFINITY : mx > m_run + kLazyLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
-        m_run = grow ? mx : m_run;
-        l_run *= alpha;
-        if (__builtin_amdgcn_ballot_w64(grow && !first)) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-        }
-      }
+      alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+      m_run = grow ? mx : m_run;
+      l_run *= alpha;
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      bf16x8 pB[2];
       float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
@@ -751,11 +725,105 @@ mlra_split_pc(SplitParams p) {
           pB[h2][e] = (__bf16)pe;
         }
       l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      return grow && !first;
+    };
+    auto rescale = [&](bool moved, float alpha) {
+      if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+      }
+    };
+    auto pv = [&](const bf16x8 (&pB)[2]) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aT[h2][dt], pB[h2], acc[dt], 0, 0, 0);
+    };
+    if constexpr (WT == 1) {
+      // One token stream per wave: a software pipeline across sub-tiles.
+      // Iteration j holds the scores of sub-tile j (from the previous
+      // iteration) and keeps slot j until its C^T reads are done; it issues
+      // the score MFMAs of sub-tile j + 1 first and runs the softmax of
+      // sub-tile j on the vector ALU while they execute, then P . C of
+      // sub-tile j. A wave thus holds two slots at a time.
+      auto score1 = [&]() {  // S^T = C . Q^T, one accumulator chain
+        f32x16 sc = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NR; ++st) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qR[st], sc, 0, 0, 0);
+#pragma unroll
+        for (int st = 0; st < NL; ++st) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[st], sc, 0, 0, 0);
+        return sc;
+      };
+      wait_ready(0);
+      read_a(slot_at(0));
+      f32x16 S = score1();
+      for (int j = 0; j < nsub; ++j) {
+        const unsigned char* sb = slot_at(j);
+        const bool more = j + 1 < nsub;  // uniform
+        if constexpr (WD > 1) S = exchange(j, S);
+        mask(S, (t0 + (j >> 1)) * kBlock + (j & 1) * kSub);
+        read_t(sb, 0);
+        read_t(sb, 1);
+        if (more) wait_ready(j + 1);
+        // past the last sub-tile the next scores are computed from this
+        // (still held) slot and dropped
+        read_a(more ? slot_at(j + 1) : sb);
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x16 Sn = score1();
+        bf16x8 pB[2];
+        float alpha;
+        const bool moved = softmax(S, pB, alpha);
+        // interleave: each score MFMA followed by a share of the softmax
+#pragma unroll
+        for (int i = 0; i < NR + NL; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        rescale(moved, alpha);
+        pv(pB);
+        lds_signal(consumed + j % NSLOT);  // its C^T reads are done (P . C used them)
+        S = Sn;
+      }
+    } else {
+      for (int j = strm; j < nsub; j += WT) {
+        const unsigned char* sb = slot_at(j);
+        wait_ready(j);
+        // LDS reads are batched ahead of the MFMAs that use them: the score
+        // operands (A = slot rows) first, then the C^T operands of P.C
+        // (transpose reads) in two halves slotted between the score MFMAs.
+        // LDS returns in order, so each MFMA waits only for its own operand,
+        // and at most 15 reads are outstanding past any wait (the counter's
+        // limit; beyond it the wait would be for every read).
+        read_a(sb);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 sc = f32x16{}, sd = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NR; ++st) sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aR[st], qR[st], sd, 0, 0, 0);
+        read_t(sb, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < NL; ++st) {
+          if (st % 2 == 0)
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[st], sc, 0, 0, 0);
+          else
+            sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL[st], qL[st], sd, 0, 0, 0);
+        }
+        read_t(sb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // every read of the slot is issued: hand it back once they complete
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        lds_signal(consumed + j % NSLOT);
+        sc += sd;
+        if constexpr (WD > 1) sc = exchange(j / WT, sc);
+        mask(sc, (t0 + (j >> 1)) * kBlock + (j & 1) * kSub);
+        bf16x8 pB[2];
+        float alpha;
+        const bool moved = softmax(sc, pB, alpha);
+        rescale(moved, alpha);
+        pv(pB);
+      }
     }
     l_run = wave_sum_halves(l_run);
   }
