@@ -499,15 +499,17 @@ def read_ceiling(torch, lib, nbytes: int, workgroups: int, steps: int, timed) ->
     """Streaming-read ceiling in the same run (mlra_stream_read, a plain HIP
     read kernel): nbytes per launch with `workgroups` workgroups of 512
     threads, launches rotating through a 2 GB buffer so that none finds its
-    bytes in the 256 MB Infinity Cache; then one 2 GB read per launch."""
+    bytes in the 256 MB Infinity Cache (a read larger than the buffer gets a
+    buffer of its own size); then one 2 GB read per launch."""
     dev = torch.device("cuda:0")
-    buf = torch.empty(CEILING_BUFFER, dtype=torch.uint8, device=dev)
+    unit = 16 * workgroups
+    n = max(unit, nbytes // unit * unit)
+    size = max(CEILING_BUFFER, n)
+    buf = torch.empty(size, dtype=torch.uint8, device=dev)
     buf.fill_(1)
     sink = torch.zeros(max(workgroups, 2048), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    unit = 16 * workgroups
-    n = max(unit, nbytes // unit * unit)
-    slots = CEILING_BUFFER // n
+    slots = size // n
 
     def small(i):
         _check_status(lib.mlra_stream_read(buf.data_ptr() + (i % slots) * n, n, workgroups,
