@@ -348,7 +348,8 @@ def bench_prefill(torch, args) -> int:
         api.mlra_prefill_attention(d["q_latent"], d["q_rope"], d["latent_cache"],
                                    d["rope_cache"], d["block_table"], d["seq_lens"], NB,
                                    cfg.scale, cfg.out_rescale, max_seq_len=inp.max_seq_len,
-                                   causal=cfg.causal, out=out, lse=lse, workspace=ws)
+                                   causal=cfg.causal, sum_seq_lens=int(inp.seq_lens.sum()),
+                                   out=out, lse=lse, workspace=ws)
 
     def timed(fn):
         for i in range(args.warmup):

@@ -352,17 +352,20 @@ def mlra_prefill_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,
                            block_table: torch.Tensor, seq_lens: torch.Tensor, n_branch: int,
                            scale: float, out_rescale: float, *, max_seq_len: int,
                            reduce: str = "sum", causal: bool = True, num_splits: int = 0,
+                           sum_seq_lens: int = 0,
                            out: Optional[torch.Tensor] = None,
                            lse: Optional[torch.Tensor] = None,
                            workspace: Optional[torch.Tensor] = None,
                            stream: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunked-prefill MLRA attention (many query tokens per sequence, bf16);
-    see include/mlra.h. Same tensors and results as mlra_decode_attention."""
+    see include/mlra.h. Same tensors and results as mlra_decode_attention.
+    sum_seq_lens (optional) is the host-side sum of seq_lens: when it shows
+    every sequence at max_seq_len the kernel skips ranking its work items."""
     if q_latent.dim() != 5 or q_latent.shape[3] != n_branch:
         raise ValueError("q_latent must be [S][Q][H][n_branch][DC]")
     return _call("prefill", q_latent, q_rope, latent_cache, rope_cache, block_table, seq_lens,
-                 n_branch, scale, out_rescale, max_seq_len, reduce, causal, num_splits, 0,
-                 out, lse, workspace, stream)
+                 n_branch, scale, out_rescale, max_seq_len, reduce, causal, num_splits,
+                 sum_seq_lens, out, lse, workspace, stream)
 
 
 def mla_decode_attention(q_latent: torch.Tensor, q_rope: torch.Tensor,

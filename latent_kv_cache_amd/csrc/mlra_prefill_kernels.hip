@@ -56,6 +56,10 @@ constexpr int kPfMaxTiles = 1024;           // 64-token tiles per split (block i
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
+// Items (sequence, row tile, split) that a workgroup ranks to dispatch them
+// longest first: each compares every pair it owns, keys in 4 KB of LDS.
+constexpr int kPfOrderMaxItems = 1024;
+
 struct PrefillParams {
   const __bf16* q_lat;
   const __bf16* q_rope;
@@ -70,6 +74,7 @@ struct PrefillParams {
   int64_t lsb, lst, lsbr, rsb, rst;
   int32_t S, Q, H, rows, NB, RT, spl, tps, max_blocks, num_blocks, lcap, causal;
   int32_t direct;     // write out/lse here (one split, no branch sum)
+  int32_t order;      // 1: dispatch (sequence, row tile, split) items longest first
   int32_t concat;     // out holds every branch
   float score_scale;  // scale * log2(e): scores kept in base-2 units
   float out_rescale;
@@ -190,17 +195,53 @@ mlra_prefill(PrefillParams p) {
   static_assert(W * 32 * NT == kPfRows, "256 rows per workgroup");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  // workgroup -> (split, branch, sequence, row tile); the last row tiles,
-  // which see the most tokens, are dispatched first
-  int id = blockIdx.x;
-  const int k = id % p.spl;
-  id /= p.spl;
-  const int b = id % p.NB;
-  id /= p.NB;
-  const int s = id % p.S;
-  const int rt = p.RT - 1 - id / p.S;
-
+  // workgroup -> (split, branch, sequence, row tile). Items (sequence, row
+  // tile, split) are numbered last row tile first (those see the most
+  // tokens), then sequence, then split; the branches of an item take
+  // consecutive workgroups.
   const int tid = threadIdx.x, lane = tid & 63;
+  int item = blockIdx.x / p.NB;
+  const int b = blockIdx.x % p.NB;
+  if (p.order) {
+    // With lengths that differ (ragged contexts), take items longest first:
+    // every workgroup ranks all items by their visible tokens (ties in item
+    // order, a strict total order the same in every workgroup) and takes
+    // the one whose rank is its own item number. Keys live in the tile ring,
+    // which no load has touched yet.
+    const int G = p.S * p.RT * p.spl, G4 = (G + 3) / 4;
+    int* const keys = reinterpret_cast<int*>(smem);
+    int* const pick = keys + 4 * G4;
+    for (int t = tid; t < 4 * G4; t += THREADS) {
+      int key = -1;  // padding: below every real key
+      if (t < G) {
+        const int kt = t % p.spl, st = (t / p.spl) % p.S, rtt = p.RT - 1 - t / (p.spl * p.S);
+        int Lt = p.seq_lens[st];
+        Lt = Lt < 0 ? 0 : (Lt > p.lcap ? p.lcap : Lt);
+        const int vm = max(0, pf_visible(Lt, p.Q, p.H, min(rtt * kPfRows + kPfRows, p.rows) - 1, p.causal));
+        const int lo = kt * p.tps * kPfTile;
+        key = max(0, min(lo + p.tps * kPfTile, vm) - lo);
+      }
+      keys[t] = key;
+    }
+    pf_lds_barrier();
+    for (int t = tid; t < G; t += THREADS) {
+      const int key = keys[t];
+      int rank = 0;
+      for (int u = 0; u < G4; ++u) {
+        const int4 kk = reinterpret_cast<const int4*>(keys)[u];
+        rank += (kk.x > key || (kk.x == key && 4 * u < t)) + (kk.y > key || (kk.y == key && 4 * u + 1 < t)) +
+                (kk.z > key || (kk.z == key && 4 * u + 2 < t)) + (kk.w > key || (kk.w == key && 4 * u + 3 < t));
+      }
+      if (rank == item) *pick = t;
+    }
+    pf_lds_barrier();
+    item = *pick;
+    pf_lds_barrier();  // the ring is free again before any tile load
+  }
+  const int k = item % p.spl;
+  const int s = (item / p.spl) % p.S;
+  const int rt = p.RT - 1 - item / (p.spl * p.S);
+
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, g = lane >> 5;
   int L = p.seq_lens[s];
@@ -723,6 +764,12 @@ extern "C" mlra_status mlra_prefill_attention(const void* q_latent, const void* 
   pp.lcap = r.lcap;
   pp.causal = r.causal;
   pp.direct = direct ? 1 : 0;
+  // Longest-first dispatch unless the length hint says every sequence has the
+  // same length (then the fixed order is already longest first), and only
+  // while ranking the items stays cheap for every workgroup.
+  const int64_t items = (int64_t)r.S * plan.row_groups * plan.splits_per_seq;
+  const bool uniform = dims->sum_seq_lens > 0 && dims->sum_seq_lens == (int64_t)r.S * r.lcap;
+  pp.order = items <= kPfOrderMaxItems && !uniform ? 1 : 0;
   pp.concat = r.reduce == MLRA_BRANCH_CONCAT ? 1 : 0;
   pp.score_scale = scale * kPfLog2e;
   pp.out_rescale = out_rescale;

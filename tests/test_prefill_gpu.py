@@ -28,14 +28,14 @@ def _say(msg):
     print(f"[gpu-case] {msg}", flush=True)
 
 
-def run_prefill(inp, reduce="sum", num_splits=0, dev=None, seq_lens=None):
+def run_prefill(inp, reduce="sum", num_splits=0, dev=None, seq_lens=None, sum_seq_lens=0):
     cfg = inp.cfg
     d = dev if dev is not None else to_device(inp)
     sl = d["seq_lens"] if seq_lens is None else torch.from_numpy(seq_lens).cuda()
     out, lse = api.mlra_prefill_attention(
         d["q_latent"], d["q_rope"], d["latent_cache"], d["rope_cache"], d["block_table"], sl,
         cfg.n_branch, cfg.scale, cfg.out_rescale, max_seq_len=inp.max_seq_len, reduce=reduce,
-        causal=cfg.causal, num_splits=num_splits)
+        causal=cfg.causal, num_splits=num_splits, sum_seq_lens=sum_seq_lens)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -170,6 +170,28 @@ def test_repeat_calls_are_bitwise_identical():
     a = run_prefill(inp, "sum", dev=dev, num_splits=3)
     b = run_prefill(inp, "sum", dev=dev, num_splits=3)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_dispatch_order_does_not_change_results():
+    # Workgroups take their (sequence, row tile, split) item longest first
+    # unless the length hint shows a uniform batch; each item's arithmetic is
+    # the same either way, so both orders give bit-identical results, and
+    # ragged lengths (ranked) match the oracle.
+    cfg = _cfg(num_seqs=3, q_len=40, num_heads=16, n_branch=2, context=600, context_range=None,
+               seed=52)
+    inp = make_inputs(cfg)
+    dev = to_device(inp)
+    for splits in (0, 3):
+        _say(f"prefill uniform batch, ranked and fixed order, splits={splits}")
+        ranked = run_prefill(inp, "sum", dev=dev, num_splits=splits)
+        fixed = run_prefill(inp, "sum", dev=dev, num_splits=splits,
+                            sum_seq_lens=int(inp.seq_lens.sum()))
+        assert np.array_equal(ranked[0], fixed[0]) and np.array_equal(ranked[1], fixed[1])
+        assert_parity(*ranked, *oracle(inp, "sum"))
+    rag = make_inputs(cfg.with_(name="pf_rag_order", context=None, context_range=(40, 900), seed=53))
+    _say(f"prefill ragged batch ranked, lens={rag.seq_lens.tolist()}")
+    assert_parity(*run_prefill(rag, "concat", sum_seq_lens=int(rag.seq_lens.sum())),
+                  *oracle(rag, "concat"))
 
 
 def test_branch_major_latent_and_padded_rope_strides():
