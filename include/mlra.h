@@ -351,8 +351,8 @@ mlra_status mlra_cache_append(const float* latent_new, const float* rope_new,
  *  y  [M][D] bf16, dense (nearest, ties to even)
  * W is a fixed weight: mlra_out_projection_pack rewrites it once, on the
  * stream, into the order the kernel loads (D*K*2 bytes, caller-owned):
- *     packed[t][kb][q][l][e] = W[16t + l%16][64kb + 32q + 8(l/16) + e]
- * for t < D/16, kb < K/64, q < 2, l < 64, e < 8; mlra_out_projection takes
+ *     packed[g][kb][w][q][l][e] = W[128g + 16w + l%16][64kb + 32q + 8(l/16) + e]
+ * for g < D/128, kb < K/64, w < 8, q < 2, l < 64, e < 8; mlra_out_projection takes
  * the packed weight. Sizes: 1 <= M <= 128 (decode rows; larger M is an
  * ordinary GEMM), K a multiple of 512, D a multiple of 128; otherwise
  * MLRA_ERR_UNSUPPORTED. workspace: at least

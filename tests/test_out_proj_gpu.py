@@ -49,16 +49,16 @@ def test_out_projection_shapes(m, k, d):
 
 
 def test_packed_layout_and_determinism():
-    k, d = 1024, 128
+    k, d = 1024, 256
     x, w = make_out_proj_inputs(20, k, d, seed=8)
     wd = torch.from_numpy(w).cuda().to(torch.bfloat16)
     _say("out-proj packed layout")
     packed = api.pack_out_projection_weight(wd).view(torch.int16).cpu().numpy()
     wi = wd.view(torch.int16).cpu().numpy()
-    # packed[t][kb][q][l][e] = W[16t + l%16][64kb + 32q + 8(l/16) + e]
-    t, kb, q, l, e = np.meshgrid(np.arange(d // 16), np.arange(k // 64), np.arange(2),
-                                 np.arange(64), np.arange(8), indexing="ij")
-    expect = wi[16 * t + l % 16, 64 * kb + 32 * q + 8 * (l // 16) + e]
+    # packed[g][kb][w][q][l][e] = W[128g + 16w + l%16][64kb + 32q + 8(l/16) + e]
+    g, kb, tw, q, l, e = np.meshgrid(np.arange(d // 128), np.arange(k // 64), np.arange(8),
+                                     np.arange(2), np.arange(64), np.arange(8), indexing="ij")
+    expect = wi[128 * g + 16 * tw + l % 16, 64 * kb + 32 * q + 8 * (l // 16) + e]
     assert np.array_equal(packed.reshape(expect.shape), expect)
     assert np.array_equal(_run(x, w), _run(x, w))
 
