@@ -124,7 +124,8 @@ typedef struct mlra_decode_dims {
   int64_t rope_stride_block, rope_stride_token;
   /* Optional host-side sum of seq_lens (0 = unknown: plan as if every
    * sequence had max_seq_len). Only steers how tokens are split across
-   * workgroups; results do not depend on it. */
+   * workgroups (decode) and whether workgroups are ordered by their work
+   * (prefill); results do not depend on it. */
   int64_t sum_seq_lens;
 } mlra_decode_dims;
 
@@ -396,8 +397,11 @@ mlra_status mlra_out_projection(const void* x, const void* w_packed, void* y, in
  *    returns 0 otherwise, and workspace may then be NULL;
  *  - shapes whose grid would pass 2^31 - 1 workgroups (attention, or the
  *    merge of splits and branches) give MLRA_ERR_UNSUPPORTED.
- * Results are deterministic: repeated calls give bit-identical out and lse.
- * mlra_prefill_make_plan fills the decode plan struct: row_groups counts
+ * When the lengths may differ (sum_seq_lens 0, or below num_seqs *
+ * max_seq_len) and the call has at most 1024 (sequence, row group, split)
+ * items, workgroups take them longest first, ranked on the device from
+ * seq_lens. Results are deterministic: repeated calls give bit-identical out
+ * and lse, whatever the order. mlra_prefill_make_plan fills the decode plan struct: row_groups counts
  * 256-row workgroups per sequence and branch, kernel_variant is 8.
  */
 mlra_status mlra_prefill_make_plan(const mlra_decode_dims* dims, int32_t n_branch,
