@@ -40,7 +40,8 @@ def _run(x, w):
 
 @pytest.mark.parametrize("m,k,d", [(1, 512, 128), (16, 4096, 4096), (33, 512, 384), (64, 1024, 256),
                                    (100, 1536, 128), (128, 2048, 128), (7, 512, 4096),
-                                   (20, 1024, 640), (32, 16384, 4096), (128, 16384, 256)])
+                                   (20, 1024, 640), (32, 16384, 4096), (128, 16384, 256),
+                                   (96, 16384, 4096)])  # x staged in sub-chunks inside the loop
 def test_out_projection_shapes(m, k, d):
     x, w = make_out_proj_inputs(m, k, d, seed=m + k + d)
     _say(f"out-proj m={m} k={k} d={d}")
