@@ -292,7 +292,7 @@ __global__ void __launch_bounds__(512) mlra_outproj(OutProjParams p) {
 // y[m][n] = bf16(sum over K-chunks of the partials, in chunk order), four
 // outputs per thread, every chunk's load in flight together (KC <= KMAX).
 template <int KMAX>
-__global__ void __launch_bounds__(256) mlra_outproj_reduce(OutProjParams p) {
+__global__ void __launch_bounds__(64) mlra_outproj_reduce(OutProjParams p) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   const int64_t total = (int64_t)p.M * p.D;
   if (i >= total) return;
@@ -320,8 +320,14 @@ static int outproj_kc(int K, int D) {
   return 1;
 }
 // 64-column blocks of x staged at a time: the whole chunk when it fits.
+// 16-row tiles of the kernel instance that serves M rows (1, 2, 4 or 8)
+static int outproj_mt(int M) {
+  const int mt = (M + 15) / 16;
+  return mt <= 1 ? 1 : mt <= 2 ? 2 : mt <= 4 ? 4 : 8;
+}
+// The instance stages all of its MT*16 rows (rows past M as zeros).
 static int outproj_sb(int M, int K, int KC) {
-  const int rows = (M + 15) / 16 * 16, nblk = K / 64 / KC;
+  const int rows = outproj_mt(M) * 16, nblk = K / 64 / KC;
   int sb = nblk;
   while (sb > 1 && rows * (sb * 128 + 16) > kOpXBytes) --sb;
   return sb;
@@ -443,19 +449,21 @@ extern "C" mlra_status mlra_out_projection(const void* x, const void* w_packed, 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const dim3 grid((uint32_t)(d / 128), (uint32_t)p.KC);
   p.SB = mlra::outproj_sb(m, k, p.KC);
-  const int mt = (m + 15) / 16;
+  const int mt = mlra::outproj_mt(m);
   hipError_t e;
-  if (mt <= 1) e = mlra::outproj_launch<1>(grid, p, hs);
-  else if (mt <= 2) e = mlra::outproj_launch<2>(grid, p, hs);
-  else if (mt <= 4) e = mlra::outproj_launch<4>(grid, p, hs);
+  if (mt == 1) e = mlra::outproj_launch<1>(grid, p, hs);
+  else if (mt == 2) e = mlra::outproj_launch<2>(grid, p, hs);
+  else if (mt == 4) e = mlra::outproj_launch<4>(grid, p, hs);
   else e = mlra::outproj_launch<8>(grid, p, hs);
   if (e != hipSuccess) return MLRA_ERR_HIP;
   if (p.KC > 1) {
+    // one wave per workgroup, so that the few thousand threads of a decode-sized
+    // sum spread over every CU (each CU draws only some 20 GB/s on its own)
     const int64_t threads = ((int64_t)m * d + 3) / 4;
-    const dim3 rg((uint32_t)((threads + 255) / 256));
-    if (p.KC <= 8) hipLaunchKernelGGL(mlra::mlra_outproj_reduce<8>, rg, dim3(256), 0, hs, p);
-    else if (p.KC <= 16) hipLaunchKernelGGL(mlra::mlra_outproj_reduce<16>, rg, dim3(256), 0, hs, p);
-    else hipLaunchKernelGGL(mlra::mlra_outproj_reduce<32>, rg, dim3(256), 0, hs, p);
+    const dim3 rg((uint32_t)((threads + 63) / 64));
+    if (p.KC <= 8) hipLaunchKernelGGL(mlra::mlra_outproj_reduce<8>, rg, dim3(64), 0, hs, p);
+    else if (p.KC <= 16) hipLaunchKernelGGL(mlra::mlra_outproj_reduce<16>, rg, dim3(64), 0, hs, p);
+    else hipLaunchKernelGGL(mlra::mlra_outproj_reduce<32>, rg, dim3(64), 0, hs, p);
   }
   return hipGetLastError() == hipSuccess ? MLRA_OK : MLRA_ERR_HIP;
 }
